@@ -1,0 +1,229 @@
+"""Seeded synthetic workloads for quantized attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no quantization, no softmax, no attention).  Both the CPU
+oracle and the HIP path read the arrays it returns, so the two sides always see
+the same inputs.
+
+Every tensor is drawn with ``numpy.random.default_rng([config_id, tensor_id])``
+(tensor ids: Q=0, K=1, V=2, K channel offset=3, outlier channels=4, pages=5),
+sampled in float32 and cast round-to-nearest-even to the workload's dtype by
+torch.
+
+Workloads (the shapes the pages discuss; the pages give no data sets):
+
+* ``tiny``        B=1, H=2, L=256, D=64, fp16, Q/K/V ~ N(0,1), K += per-channel
+                  offset ~ N(0, 2^2), non-causal.
+* ``llm_prefill`` B=2, H=32, L=4096, D=128, bf16, K offset ~ N(0, 3^2), causal.
+* ``video_dit``   B=1, H=40, L=32760, D=128, bf16, Q/K Student-t(3) with 4
+                  outlier channels per head scaled x20 (same channels for Q and
+                  K), V ~ N(0,1); Q/K/V are strided [B,L,H,D] views into one
+                  stacked [B,L,3,H,D] buffer (the layout a fused QKV projection
+                  produces, which FastVideo's sage_attn3 backend copies with a
+                  permute+contiguous before its kernel).
+* ``video_dit_mxfp4`` same tensors as ``video_dit`` (MXFP4 QK with Hadamard).
+* ``paged_decode`` batch 16, 4 query tokens per sequence, 16 query heads on 1
+                  KV head, D=128, bf16 queries; FP8 e4m3 KV cache with a
+                  per-token fp32 scale, page 128, context 8192, sliding window
+                  4096, page table = seeded permutation of the 1024-page pool.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+T_Q, T_K, T_V, T_OFFSET, T_OUTLIER, T_PAGES = 0, 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    config_id: int          # seed root
+    B: int
+    H: int
+    Lq: int
+    Lk: int
+    D: int
+    dtype: torch.dtype
+    causal: bool
+    qk_mode: str            # "int8" or "mxfp4"
+    dist: str               # "normal_offset" or "student_t_outliers"
+    k_offset_sigma: float = 0.0
+    stacked: bool = False   # Q/K/V are views of a stacked [B,L,3,H,D] buffer
+    outlier_channels: int = 4
+    outlier_scale: float = 20.0
+    q_block: int = 128
+    k_block: int = 64
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    config_id: int
+    batch: int
+    mtp: int
+    hq: int
+    hkv: int
+    D: int
+    page_size: int
+    ctx: int
+    window: int
+    q_dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def pages_per_seq(self) -> int:
+        return (self.ctx + self.page_size - 1) // self.page_size
+
+    @property
+    def num_pages(self) -> int:
+        return self.batch * self.pages_per_seq
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+WORKLOADS = {
+    "tiny": PrefillWorkload("tiny", 0, 1, 2, 256, 256, 64, torch.float16, False, "int8",
+                            "normal_offset", k_offset_sigma=2.0),
+    "llm_prefill": PrefillWorkload("llm_prefill", 1, 2, 32, 4096, 4096, 128, torch.bfloat16,
+                                   True, "int8", "normal_offset", k_offset_sigma=3.0),
+    "video_dit": PrefillWorkload("video_dit", 2, 1, 40, 32760, 32760, 128, torch.bfloat16,
+                                 False, "int8", "student_t_outliers", stacked=True),
+    "video_dit_mxfp4": PrefillWorkload("video_dit_mxfp4", 2, 1, 40, 32760, 32760, 128,
+                                       torch.bfloat16, False, "mxfp4", "student_t_outliers",
+                                       stacked=True),
+    "paged_decode": DecodeWorkload("paged_decode", 4, 16, 4, 16, 1, 128, 128, 8192, 4096),
+}
+
+
+def _rng(config_id: int, tensor_id: int) -> np.random.Generator:
+    return np.random.default_rng([config_id, tensor_id])
+
+
+def _normal(config_id, tensor_id, shape) -> np.ndarray:
+    return _rng(config_id, tensor_id).standard_normal(shape, dtype=np.float32)
+
+
+def _student_t(config_id, tensor_id, shape, nu=3.0, chunk=1 << 24) -> np.ndarray:
+    rng = _rng(config_id, tensor_id)
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        out[s:e] = rng.standard_t(nu, e - s).astype(np.float32)
+    return out.reshape(shape)
+
+
+def outlier_channels(w: PrefillWorkload) -> np.ndarray:
+    """[H, n] distinct channel indices per head (same for Q and K)."""
+    rng = _rng(w.config_id, T_OUTLIER)
+    return np.stack([rng.choice(w.D, size=w.outlier_channels, replace=False)
+                     for _ in range(w.H)]).astype(np.int64)
+
+
+def _to_dtype(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    return torch.from_numpy(a).to(dtype)
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor                  # logical [B, Lq, H, D] (possibly strided view)
+    k: torch.Tensor                  # logical [B, Lk, H, D]
+    v: torch.Tensor                  # logical [B, Lk, H, D]
+    base: Optional[torch.Tensor] = None  # stacked buffer when the views share one
+
+
+def make_prefill(w: PrefillWorkload, Lq: Optional[int] = None, Lk: Optional[int] = None,
+                 device: str = "cpu") -> PrefillInputs:
+    """Draws Q, K, V for a prefill workload.
+
+    ``Lq``/``Lk`` override the sequence lengths (same distributions and seeds,
+    the first rows of a longer draw are NOT reused: a shorter draw is its own
+    sample), which the parity tests use for sizes the oracle finishes quickly.
+    """
+    B, H, D = w.B, w.H, w.D
+    Lq = w.Lq if Lq is None else Lq
+    Lk = w.Lk if Lk is None else Lk
+    cid = w.config_id
+    if w.dist == "normal_offset":
+        q = _normal(cid, T_Q, (B, Lq, H, D))
+        k = _normal(cid, T_K, (B, Lk, H, D))
+        v = _normal(cid, T_V, (B, Lk, H, D))
+        off = _rng(cid, T_OFFSET).normal(0.0, w.k_offset_sigma, (H, D)).astype(np.float32)
+        k += off[None, None, :, :]
+    elif w.dist == "student_t_outliers":
+        q = _student_t(cid, T_Q, (B, Lq, H, D))
+        k = _student_t(cid, T_K, (B, Lk, H, D))
+        v = _normal(cid, T_V, (B, Lk, H, D))
+        ch = outlier_channels(w)
+        for h in range(H):
+            q[:, :, h, ch[h]] *= np.float32(w.outlier_scale)
+            k[:, :, h, ch[h]] *= np.float32(w.outlier_scale)
+    else:
+        raise ValueError(w.dist)
+
+    if w.stacked and Lq == Lk:
+        base = torch.empty((B, Lq, 3, H, D), dtype=w.dtype)
+        base[:, :, 0] = _to_dtype(q, w.dtype)
+        del q
+        base[:, :, 1] = _to_dtype(k, w.dtype)
+        del k
+        base[:, :, 2] = _to_dtype(v, w.dtype)
+        del v
+        if device != "cpu":
+            base = base.to(device)
+        return PrefillInputs(base[:, :, 0], base[:, :, 1], base[:, :, 2], base)
+    qt, kt, vt = (_to_dtype(x, w.dtype) for x in (q, k, v))
+    if device != "cpu":
+        qt, kt, vt = qt.to(device), kt.to(device), vt.to(device)
+    return PrefillInputs(qt, kt, vt)
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [batch, mtp, hq, D] bf16
+    k_cache: torch.Tensor      # [num_pages, hkv, page, D] uint8 (e4m3 codes)
+    v_cache: torch.Tensor      # [num_pages, hkv, page, D] uint8 (e4m3 codes)
+    k_scale: torch.Tensor      # [num_pages, hkv, page] fp32
+    v_scale: torch.Tensor      # [num_pages, hkv, page] fp32
+    page_table: torch.Tensor   # [batch, pages_per_seq] int32
+    ctx_lens: torch.Tensor     # [batch] int32
+
+
+def _per_token_e4m3(x: np.ndarray):
+    """Synthesises an e4m3 cache with a per-token fp32 scale (amax/448) from
+    float draws, using torch's float8_e4m3fn cast.  This builds an input; the
+    decode path consumes the cache as given."""
+    t = torch.from_numpy(x)
+    amax = t.abs().amax(dim=-1, keepdim=True)
+    scale = (amax / 448.0).to(torch.float32)
+    scale = torch.where(scale > 0, scale, torch.ones_like(scale))
+    codes = (t / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.squeeze(-1).contiguous()
+
+
+def make_decode(w: DecodeWorkload, batch: Optional[int] = None, ctx: Optional[int] = None,
+                pool_seed: int = 0) -> DecodeInputs:
+    """Draws a paged decode problem.  ``pool_seed`` > 0 draws an independent KV
+    pool and page table of the same shape (used to rotate pools when timing)."""
+    batch = w.batch if batch is None else batch
+    ctx = w.ctx if ctx is None else ctx
+    pps = (ctx + w.page_size - 1) // w.page_size
+    npages = batch * pps
+    cid = w.config_id if pool_seed == 0 else 1000 + pool_seed
+    q = _normal(w.config_id, T_Q, (batch, w.mtp, w.hq, w.D))
+    kf = _normal(cid, T_K, (npages, w.hkv, w.page_size, w.D))
+    vf = _normal(cid, T_V, (npages, w.hkv, w.page_size, w.D))
+    kc, ks = _per_token_e4m3(kf)
+    vc, vs = _per_token_e4m3(vf)
+    perm = _rng(cid, T_PAGES).permutation(npages).astype(np.int32)
+    table = torch.from_numpy(perm.reshape(batch, pps).copy())
+    ctx_lens = torch.full((batch,), ctx, dtype=torch.int32)
+    return DecodeInputs(_to_dtype(q, w.q_dtype), kc, vc, ks, vs, table, ctx_lens)

@@ -1,0 +1,113 @@
+"""Pins of the oracle's paged decode: the page's window-tile counts, reduction
+to exact attention of the last MTP rows (float mode), invariance to page
+placement and to the split length, and the quantized mode against exact."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_window_tiles_match_page(orc):
+    with open(os.path.join(GOLD, "aiter7388_window_tiles.json")) as f:
+        g = json.load(f)
+    for window, tiles in g["cases"]:
+        assert orc.decode_num_splits(window, g["mtp"], g["tile"]) == tiles
+        # and it is the largest number of tile-aligned windows a span of
+        # window + mtp - 1 consecutive keys touches, over every alignment
+        span = window + g["mtp"] - 1
+        brute = max((s + span - 1) // g["tile"] - s // g["tile"] + 1 for s in range(g["tile"]))
+        assert brute == tiles
+
+
+def _contiguous_cache(k, v, page):
+    """[B, ctx, Hkv, D] float -> identity-paged caches [P, Hkv, page, D]."""
+    B, ctx, Hkv, D = k.shape
+    pps = ctx // page
+    kc = k.reshape(B, pps, page, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(B * pps, Hkv, page, D)
+    vc = v.reshape(B, pps, page, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(B * pps, Hkv, page, D)
+    table = np.arange(B * pps, dtype=np.int32).reshape(B, pps)
+    return np.ascontiguousarray(kc), np.ascontiguousarray(vc), table
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("window", [0, 40, 100])
+@pytest.mark.parametrize("tile", [16, 32, 256])
+def test_float_mode_is_exact_attention(orc, window, tile):
+    B, ctx, Hq, Hkv, D, MTP, page = 2, 96, 4, 2, 16, 3, 16
+    k, v = _rand((B, ctx, Hkv, D), 1), _rand((B, ctx, Hkv, D), 2)
+    q = _rand((B, MTP, Hq, D), 3, 2.0)
+    kc, vc, table = _contiguous_cache(k, v, page)
+    ones = np.ones(kc.shape[:3], np.float32)
+    out = orc.paged_decode(q, kc, vc, ones, ones, table, np.full(B, ctx, np.int32),
+                           window=window, sm_scale=0.3, tile=tile, quant=False)
+    for b in range(B):
+        for m in range(MTP):
+            pos = ctx - MTP + m
+            lo = max(0, pos - window + 1) if window else 0
+            for h in range(Hq):
+                hk = h // (Hq // Hkv)
+                ref = orc.attn_exact(q[b, m, h][None, None, None], k[b, lo:pos + 1, hk][None, None],
+                                     v[b, lo:pos + 1, hk][None, None], False, 0.3)
+                assert np.abs(out[b, m, h] - ref[0, 0, 0]).max() < 2e-6
+
+
+def test_float_mode_applies_per_token_scales(orc):
+    B, ctx, Hkv, D, page = 1, 64, 1, 8, 16
+    k, v = _rand((B, ctx, Hkv, D), 4), _rand((B, ctx, Hkv, D), 5)
+    ks = np.abs(_rand((ctx,), 6)) + 0.5
+    vs = np.abs(_rand((ctx,), 7)) + 0.5
+    q = _rand((B, 1, 2, D), 8)
+    kc, vc, table = _contiguous_cache(k, v, page)
+    kss = ks.reshape(-1, 1, page)
+    vss = vs.reshape(-1, 1, page)
+    out = orc.paged_decode(q, kc, vc, kss, vss, table, np.full(B, ctx, np.int32), window=0,
+                           sm_scale=0.5, tile=32, quant=False)
+    kk = k[0, :, 0] * ks[:, None]
+    vv = v[0, :, 0] * vs[:, None]
+    for h in range(2):
+        ref = orc.attn_exact(q[0, 0, h][None, None, None], kk[None, None], vv[None, None], False, 0.5)
+        assert np.abs(out[0, 0, h] - ref[0, 0, 0]).max() < 2e-6
+
+
+def test_page_permutation_invariance(orc):
+    from quantized_attention_block_amd import workloads as wl
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=2, ctx=600)
+    q = inp.q.float().numpy()
+    kc, vc = inp.k_cache.numpy(), inp.v_cache.numpy()
+    ks, vs = inp.k_scale.numpy(), inp.v_scale.numpy()
+    table, ctx = inp.page_table.numpy(), inp.ctx_lens.numpy()
+    common = dict(window=256, sm_scale=w.sm_scale, tile=256)
+    a = orc.paged_decode(q, kc, vc, ks, vs, table, ctx, **common)
+    perm = np.random.default_rng(9).permutation(kc.shape[0])
+    inv = np.argsort(perm)
+    b = orc.paged_decode(q, kc[perm], vc[perm], ks[perm], vs[perm], inv[table].astype(np.int32),
+                         ctx, **common)
+    assert np.array_equal(a, b)
+
+
+def test_quant_mode_close_to_exact(orc):
+    from quantized_attention_block_amd import workloads as wl
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=2, ctx=1100)
+    q = inp.q.float().numpy()
+    kc, vc = inp.k_cache.numpy(), inp.v_cache.numpy()
+    ks, vs = inp.k_scale.numpy(), inp.v_scale.numpy()
+    table, ctx = inp.page_table.numpy(), inp.ctx_lens.numpy()
+    out = orc.paged_decode(q, kc, vc, ks, vs, table, ctx, window=512, sm_scale=w.sm_scale)
+    kf = orc.e4m3_decode_array(kc) * ks[..., None]
+    vf = orc.e4m3_decode_array(vc) * vs[..., None]
+    ref = orc.paged_decode(q, kf, vf, np.ones_like(ks), np.ones_like(vs), table, ctx,
+                           window=512, sm_scale=w.sm_scale, quant=False)
+    cos = (out.ravel() @ ref.ravel()) / np.linalg.norm(out) / np.linalg.norm(ref)
+    assert cos >= 0.999
+    # the split length changes nothing in float mode
+    ref2 = orc.paged_decode(q, kf, vf, np.ones_like(ks), np.ones_like(vs), table, ctx,
+                            window=512, sm_scale=w.sm_scale, quant=False, tile=64)
+    assert np.abs(ref - ref2).max() < 2e-6
