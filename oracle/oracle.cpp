@@ -43,6 +43,7 @@
 namespace {
 
 const double kLog2e = 1.4426950408889634073599246810019;  // log2(e)
+const float kLog2Fp8Max = (float)8.8073549220576041074;   // fp32(log2(448))
 
 // ---------------------------------------------------------------------------
 // Rounding to a small binary floating-point format, from its definition.
@@ -386,28 +387,35 @@ int64_t orc_qk_int8_exact(const int8_t* q8, const int8_t* k8, int D) {
 // Per query row, KV tiles of BN keys are visited in ascending order; tiles whose
 // every key is causally masked are skipped.  Per tile, in the order of
 // [Sage2 README] (QK -> update_mdo -> accumulate_d -> RS_32_to_8 -> PV):
-//   (a) S = exact integer q8 . k8 (INT8) or the exact MXFP4 block sum;
-//   (b) INT8: c = fp32(fp32(q_scale * k_scale) * alpha), x = fp32(float(S) * c);
-//       MXFP4: x = fp32(fp32(S) * alpha); alpha = fp32(sm_scale * log2 e);
+//   (a) S = exact integer q8 . k8 (INT8) or the MXFP4 block sum rounded once
+//       to fp32;
+//   (b) c = fp32(fp32(q_scale * k_scale) * alpha) (INT8) or c = alpha (MXFP4),
+//       alpha = fp32(sm_scale * log2 e); the score x = fp32(float(S) * c);
 //       masked keys get x = -inf;
 //   (c) m_new = max(m, max_j x_j); a = exp2(m - m_new) (0 while m = -inf);
 //       l = a * l; O = a * O (update_mdo);
-//   (d) p_j = exp2(x_j - m_new); l += sum_j p_j in key order (accumulate_d,
-//       from the fp32 p, before conversion);
-//   (e) P8_j = e4m3(fp32(448 * p_j)) (RS_32_to_8; the static 448 = FP8_MAX
-//       scale of [aiter #7388], valid because p <= 1);
+//   (d) the FP8_MAX-scaled probability 448 * 2^(x_j - m_new) is evaluated as
+//       q_j = exp2(fma(float(S_j), c, -m')) with m' = fp32(m_new - fp32(log2
+//       448)): one rounding for the exponent, FP8_MAX folded into it;
+//       l += q_j in key order (accumulate_d, from the fp32 values, before
+//       conversion; l therefore carries the factor 448);
+//   (e) P8_j = e4m3(q_j) (RS_32_to_8; 448 = FP8_MAX of [aiter #7388], valid
+//       because the unscaled probability is <= 1);
 //   (f) O[d] += fp32(sum_j dec(P8_j) * dec(V8[j, d])) with the tile's sum exact.
-// Epilogue: out[d] = fp32(fp32(O[d] * v_scale[d]) / fp32(448 * l)) (1/FP8_MAX
-// and the fused V scale); l == 0 -> 0.
+// Epilogue: out[d] = fp32(fp32(O[d] * v_scale[d]) / l) (the fused V scale; l
+// holds 448 sum p, i.e. the epilogue's 1/FP8_MAX); l == 0 -> 0.
 // READINGS: exp2 with log2(e) folded into alpha; exp2 is evaluated in binary64
-// and rounded once; the tile length BN and the ascending order are part of the
-// numeric definition (the running max decides how P is rounded), so the caller
-// passes the kernel's BN.
-// Pins: with quantization off (ORC_QK_FLOAT, quant_pv = 0) it equals exact
-// attention within 1e-6 and is invariant to BN; with V = 1 the output is the
-// row sum of P, which lies within the e4m3 rounding bound of 1.  The quantized
-// result itself has no independent pin beyond those bounds (parity unpinned
-// except against the HIP path, by design of the method).
+// and rounded once; the pages fix no rounding order for 448 * 2^(x - m), and
+// since it decides the e4m3 code of P, it is evaluated in the order the fused
+// kernel uses (the fma and the folded log2 448 above); the tile length BN and
+// the ascending order are part of the numeric definition (the running max
+// decides how P is rounded), so the caller passes the kernel's BN.
+// Pins: with quantization off (ORC_QK_FLOAT, quant_pv = 0: x = fp32(S alpha),
+// p = exp2(x - m), out = O / l) it equals exact attention within 1e-6 and is
+// invariant to BN; with V = 1 the output is the row sum of P8 / l, which lies
+// within the e4m3 rounding bound of 1.  The quantized result itself has no
+// independent pin beyond those bounds (parity unpinned except against the HIP
+// path, by design of the method).
 
 namespace {
 
@@ -416,8 +424,12 @@ struct EmulRow {
     const orc_attn_inputs& in;
     float alpha;
     int nqb, nkb;
+    const float* dec;   // e4m3 code -> value, tabulated from orc_e4m3_decode
 
-    float score(int b, int h, int i, int j) const {
+    // Returns float(S) for key j of row i and sets *c to its scale (INT8:
+    // fp32(q_scale * k_scale) * alpha; MXFP4: alpha; float mode: 1 with S
+    // already scaled by sm_scale * log2 e).
+    float score(int b, int h, int i, int j, float* c) const {
         const int D = p.D;
         if (p.qk_mode == ORC_QK_INT8) {
             const int8_t* qr = in.q8 + idx4(b, h, i, 0, p.H, p.Lq, D);
@@ -425,8 +437,8 @@ struct EmulRow {
             int64_t S = orc_qk_int8_exact(qr, kr, D);
             float qs = in.q_scale[((int64_t)b * p.H + h) * nqb + i / p.q_block];
             float ks = in.k_scale[((int64_t)b * p.H + h) * nkb + j / p.k_block];
-            float c = (qs * ks) * alpha;
-            return (float)S * c;
+            *c = (qs * ks) * alpha;
+            return (float)S;
         }
         if (p.qk_mode == ORC_QK_MXFP4) {
             const uint8_t* qr = in.q4 + idx4(b, h, i, 0, p.H, p.Lq, D);
@@ -438,26 +450,28 @@ struct EmulRow {
                 int64_t isum = 0;   // sum of (2 q)(2 k): E2M1 values are multiples of 0.5
                 for (int d = bl * 32; d < bl * 32 + 32; ++d) {
                     int64_t a = (int64_t)std::lrint(2.0 * orc_e2m1_decode(qr[d]));
-                    int64_t c = (int64_t)std::lrint(2.0 * orc_e2m1_decode(kr[d]));
-                    isum += a * c;
+                    int64_t c2 = (int64_t)std::lrint(2.0 * orc_e2m1_decode(kr[d]));
+                    isum += a * c2;
                 }
                 int ex = ((int)qe[bl] - 127) + ((int)ke[bl] - 127) - 2;
                 S += std::ldexp((double)isum, ex);
             }
-            return (float)S * alpha;
+            *c = alpha;
+            return (float)S;
         }
         const float* qr = in.qf + idx4(b, h, i, 0, p.H, p.Lq, D);
         const float* kr = in.kf + idx4(b, h, j, 0, p.H, p.Lk, D);
         double S = 0.0;
         for (int d = 0; d < D; ++d) S += (double)qr[d] * (double)kr[d];
+        *c = 1.0f;
         return (float)(S * p.sm_scale * kLog2e);
     }
 
     void run(int b, int h, int i, float* out) const {
         const int D = p.D, BN = p.BN;
         float m = -INFINITY, l = 0.0f;
-        std::vector<float> O(D, 0.0f), x(BN), pr(BN);
-        std::vector<uint8_t> p8(BN);
+        std::vector<float> O(D, 0.0f), Sf(BN), cs(BN), pr(BN);
+        std::vector<uint8_t> p8(BN), vis(BN);
         std::vector<double> acc(D);
         const int kend = p.causal ? std::min(p.Lk, i + 1) : p.Lk;
         for (int n0 = 0; n0 < kend; n0 += BN) {
@@ -466,25 +480,35 @@ struct EmulRow {
             float mt = -INFINITY;
             for (int t = 0; t < nt; ++t) {
                 int j = n0 + t;
-                x[t] = (p.causal && j > i) ? -INFINITY : score(b, h, i, j);
-                mt = std::max(mt, x[t]);
+                vis[t] = !(p.causal && j > i);
+                if (!vis[t]) continue;
+                Sf[t] = score(b, h, i, j, &cs[t]);
+                mt = std::max(mt, Sf[t] * cs[t]);          // x = fp32(S c)
             }
             const float m_new = std::max(m, mt);
             const float a = (m == -INFINITY) ? 0.0f : exp2_f32(m - m_new);
             l = a * l;
             for (int d = 0; d < D; ++d) O[d] = a * O[d];
-            for (int t = 0; t < nt; ++t) {
-                pr[t] = (x[t] == -INFINITY) ? 0.0f : exp2_f32(x[t] - m_new);
-                l = l + pr[t];
+            if (p.quant_pv) {
+                const float mq = m_new - kLog2Fp8Max;
+                for (int t = 0; t < nt; ++t) {
+                    pr[t] = vis[t] ? exp2_f32(std::fma(Sf[t], cs[t], -mq)) : 0.0f;
+                    l = l + pr[t];
+                }
+            } else {
+                for (int t = 0; t < nt; ++t) {
+                    pr[t] = vis[t] ? exp2_f32(Sf[t] * cs[t] - m_new) : 0.0f;
+                    l = l + pr[t];
+                }
             }
             std::fill(acc.begin(), acc.end(), 0.0);
             if (p.quant_pv) {
-                for (int t = 0; t < nt; ++t) p8[t] = orc_e4m3_encode(448.0f * pr[t]);
+                for (int t = 0; t < nt; ++t) p8[t] = orc_e4m3_encode(pr[t]);
                 for (int t = 0; t < nt; ++t) {
-                    double pv = orc_e4m3_decode(p8[t]);
+                    double pv = dec[p8[t]];
                     if (pv == 0.0) continue;
                     const uint8_t* vr = in.v8 + idx4(b, h, n0 + t, 0, p.H, p.Lk, D);
-                    for (int d = 0; d < D; ++d) acc[d] += pv * (double)orc_e4m3_decode(vr[d]);
+                    for (int d = 0; d < D; ++d) acc[d] += pv * (double)dec[vr[d]];
                 }
             } else {
                 for (int t = 0; t < nt; ++t) {
@@ -501,7 +525,7 @@ struct EmulRow {
                 out[d] = 0.0f;
             } else if (p.quant_pv) {
                 float vs = in.v_scale[((int64_t)b * p.H + h) * D + d];
-                out[d] = (O[d] * vs) / (448.0f * l);
+                out[d] = (O[d] * vs) / l;
             } else {
                 out[d] = O[d] / l;
             }
@@ -515,9 +539,11 @@ int orc_attn_emulated(const orc_attn_params* p, const orc_attn_inputs* in,
                       const int32_t* rows, int64_t nrows, float* out) {
     if (!p || !in || p->BN <= 0 || p->D <= 0) return -1;
     if (p->qk_mode == ORC_QK_MXFP4 && p->D % 32) return -1;
+    float dec[256];
+    for (int c = 0; c < 256; ++c) dec[c] = orc_e4m3_decode((uint8_t)c);
     EmulRow er{*p, *in, (float)(p->sm_scale * kLog2e),
                (p->Lq + p->q_block - 1) / std::max(1, p->q_block),
-               (p->Lk + p->k_block - 1) / std::max(1, p->k_block)};
+               (p->Lk + p->k_block - 1) / std::max(1, p->k_block), dec};
     int64_t n = rows ? nrows : (int64_t)p->B * p->H * p->Lq;
     parallel_for(n, p->nthreads, [&](int64_t r) {
         int b, h, i;
@@ -622,6 +648,8 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
     const float alpha = (float)(p->sm_scale * kLog2e);
     const int group = p->Hq / p->Hkv;
     int64_t nrows = (int64_t)p->B * p->MTP * p->Hq;
+    float dec[256];
+    for (int c = 0; c < 256; ++c) dec[c] = orc_e4m3_decode((uint8_t)c);
     std::atomic<int> bad{0};
     parallel_for(nrows, p->nthreads, [&](int64_t r) {
         const int hq = (int)(r % p->Hq);
@@ -670,8 +698,7 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
                     if (p->quant) {
                         const uint8_t* kr = (const uint8_t*)k_cache + row * D;
                         double dot = 0.0;
-                        for (int d = 0; d < D; ++d)
-                            dot += (double)orc_e4m3_decode(q8[d]) * (double)orc_e4m3_decode(kr[d]);
+                        for (int d = 0; d < D; ++d) dot += (double)dec[q8[d]] * (double)dec[kr[d]];
                         xv = (((float)dot * q_s) * k_scale[row]) * alpha;
                     } else {
                         const float* kr = (const float*)k_cache + row * D;
@@ -701,10 +728,10 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
                         int64_t row = 0;
                         slot(t, &row);
                         float pp = pr[t - r0] * v_scale[row];
-                        double pv = orc_e4m3_decode(orc_e4m3_encode(pp * inv_v));
+                        double pv = dec[orc_e4m3_encode(pp * inv_v)];
                         if (pv == 0.0) continue;
                         const uint8_t* vr = (const uint8_t*)v_cache + row * D;
-                        for (int d = 0; d < D; ++d) acc[d] += pv * (double)orc_e4m3_decode(vr[d]);
+                        for (int d = 0; d < D; ++d) acc[d] += pv * (double)dec[vr[d]];
                     }
                     for (int d = 0; d < D; ++d) Osp[d] = (float)acc[d] * back_v;
                 } else {
