@@ -1,0 +1,259 @@
+/*
+ * sage.h - C ABI of the MI355X (gfx950) quantized-attention library.
+ *
+ * SageAttention2-style quantized scaled-dot-product attention and an FP8
+ * paged-KV decode, as discussed on these pages (cited by title and section):
+ *   [xDiT #665]    xDiT pull request 665 "Sage v2 improvements" - the Sage v2
+ *                  MXFP4 attention is fed strided tensors without contiguity
+ *                  copies, and its Hadamard matrix (BLOCK_R = 128) is built
+ *                  once and reused by every call.
+ *   [FastVideo]    FastVideo API page "sage_attn3" (SageAttention3Impl) -
+ *                  constructor arguments causal / softmax_scale /
+ *                  num_kv_heads; its pre/post-processing copies QKV into
+ *                  [B,H,L,D] and back, the copies this library avoids.
+ *   [aiter #7388]  ROCm/aiter pull request 7388 (FlyDSL pa_decode) - paged
+ *                  decode with an FP8 KV cache, per-token scales, sliding
+ *                  window, split-KV partitions merged by a reduce step; FP8
+ *                  flavour must match the architecture (OCP e4m3fn on gfx950,
+ *                  FNUZ refused); FP8_MAX = 448 scales Q and P.
+ *   [Sage2 README] "Sage2 SM89 Temporal Pair Experiment" README, section
+ *                  Candidate - INT8 QK, FP8 PV, fused V scale, per-tile order
+ *                  QK -> online-softmax update -> row sum -> FP8 P -> PV.
+ *
+ * Conventions
+ *  - Tensors are described by sage_tensor: a device pointer, a dtype, and a
+ *    LOGICAL shape with element strides.  Q/K/V/out are logical [B, L, H, D];
+ *    any B/L/H strides are accepted (so [B,L,H,D], [B,H,L,D] and views into a
+ *    stacked QKV buffer all work) but stride[D] must be 1.  The library never
+ *    copies an input to make it contiguous.
+ *  - Alignment: every pointer handed to the library must be 16-byte aligned;
+ *    for strided Q/K/V/out, every row start (each B/L/H stride in bytes) must
+ *    be a multiple of 16 bytes.
+ *  - Quantized tensors use the library layouts documented per function; they
+ *    must be contiguous with exactly the stated shape.  Padded lengths:
+ *    SAGE_PAD(L) = ceil(L / 128) * 128.
+ *  - Ownership: the caller owns every tensor and every workspace.  The only
+ *    device memory the library allocates is inside sage_hadamard_create.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  Every
+ *    call only enqueues work on that stream: no allocation, no
+ *    synchronisation, no host blocking.
+ *  - Errors: every function returns a sage_status.  All argument validation
+ *    runs before any HIP call (so it can be exercised without a GPU) and is
+ *    O(1).  On failure nothing is enqueued and sage_last_error() returns a
+ *    thread-local message.  Launch failures are reported as SAGE_ERR_HIP;
+ *    faults inside a kernel surface at the caller's next synchronisation.
+ *    No C++ exception crosses this interface.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_VERSION_MAJOR 0
+#define SAGE_VERSION_MINOR 1
+#define SAGE_PAD(L) ((((L) + 127) / 128) * 128)
+
+typedef enum {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, inconsistent sizes  */
+    SAGE_ERR_DTYPE = 2,        /* unsupported dtype or combination (incl. FNUZ FP8) */
+    SAGE_ERR_SHAPE = 3,        /* shape mismatch, unsupported head dim, R != 128  */
+    SAGE_ERR_LAYOUT = 4,       /* stride[D] != 1, non-contiguous library tensor  */
+    SAGE_ERR_ALIGNMENT = 5,    /* pointer or row stride not 16-byte aligned      */
+    SAGE_ERR_WORKSPACE = 6,    /* workspace missing or too small                 */
+    SAGE_ERR_ARCH = 7,         /* current device is not gfx950                   */
+    SAGE_ERR_HIP = 8,          /* a HIP runtime call or launch failed            */
+    SAGE_ERR_UNSUPPORTED = 9   /* valid request outside what is implemented      */
+} sage_status;
+
+typedef enum {
+    SAGE_F16 = 1,
+    SAGE_BF16 = 2,
+    SAGE_F32 = 3,
+    SAGE_I8 = 4,
+    SAGE_I32 = 5,
+    SAGE_U8 = 6,
+    SAGE_FP8_E4M3FN = 7,    /* OCP e4m3 (gfx950's MFMA format), max 448            */
+    SAGE_FP8_E4M3FNUZ = 8,  /* gfx94x flavour: always refused (SAGE_ERR_DTYPE)    */
+    SAGE_FP4X2_E2M1 = 9,    /* two E2M1 codes per byte, element 2i in low nibble  */
+    SAGE_E8M0 = 10          /* MX shared exponent, value 2^(code-127)             */
+} sage_dtype;
+
+typedef struct {
+    void* data;          /* device pointer, 16-byte aligned                     */
+    int32_t dtype;       /* sage_dtype                                          */
+    int32_t ndim;        /* 1..5                                                */
+    int64_t shape[5];
+    int64_t stride[5];   /* in elements (for FP4X2: in bytes, i.e. code pairs)  */
+} sage_tensor;
+
+typedef enum { SAGE_QK_INT8 = 0, SAGE_QK_MXFP4 = 1 } sage_qk_mode;
+
+/* Immutable Hadamard rotation (Sylvester order R, scaled by 1/sqrt(R)) kept on
+ * one device and shared by every call and thread ([xDiT #665]: built once). */
+typedef struct sage_hadamard sage_hadamard;
+
+/* ------------------------------------------------------------------------- */
+/* Q/K quantization.                                                          */
+/*
+ * Method (SageAttention2 as named on the pages; step details are the
+ * library's documented reading):
+ *  - smooth_k: mu[b,h,d] = mean of K over all Lk tokens (fp64 sum, rounded
+ *    once to fp32); K_s = fp32(K - mu).
+ *  - SAGE_QK_INT8: Q in q_block-token blocks and K_s in k_block-token blocks
+ *    per (b,h): scale = fp32(amax / 127), code = clamp(rne(fp32(x *
+ *    fp32(127 / amax))), -127, 127); amax == 0 -> scale 0, codes 0.
+ *      q_out   I8   [B, H, SAGE_PAD(Lq), D]    (rows >= Lq are 0)
+ *      q_scale F32  [B, H, SAGE_PAD(Lq) / q_block]
+ *      k_out   I8   [B, H, SAGE_PAD(Lk), D]
+ *      k_scale F32  [B, H, SAGE_PAD(Lk) / k_block]
+ *    q_block must be 128; k_block must be 64 or 128.
+ *  - SAGE_QK_MXFP4 ([xDiT #665]): rows of Q and K_s are rotated per 128-channel
+ *    block by the Hadamard handle (NULL: no rotation), then quantized per 32
+ *    channels: E8M0 exponent e = floor(log2 amax) - 2, codes
+ *    e2m1_rne_sat(x * 2^-e).
+ *      q_out   FP4X2 [B, H, SAGE_PAD(Lq), D/2]   q_scale E8M0 [B, H, SAGE_PAD(Lq), D/32]
+ *      k_out   FP4X2 [B, H, SAGE_PAD(Lk), D/2]   k_scale E8M0 [B, H, SAGE_PAD(Lk), D/32]
+ *  q, k: F16 or BF16 logical [B, L, H, D], D in {64, 128}, any B/L/H strides.
+ *  k_mean: optional F32 [B, H, D] output of mu (NULL: kept in the workspace).
+ *  workspace: sage_quantize_qk_workspace_size bytes.
+ */
+typedef struct {
+    int32_t mode;       /* sage_qk_mode                              */
+    int32_t q_block;    /* INT8: tokens per Q scale (128)            */
+    int32_t k_block;    /* INT8: tokens per K scale (64 or 128)      */
+    int32_t smooth_k;   /* 1: subtract the per-channel K mean        */
+} sage_qk_params;
+
+sage_status sage_quantize_qk_workspace_size(const sage_tensor* q, const sage_tensor* k,
+                                            const sage_qk_params* params, size_t* bytes);
+sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k,
+                             const sage_qk_params* params,
+                             const sage_tensor* q_out, const sage_tensor* q_scale,
+                             const sage_tensor* k_out, const sage_tensor* k_scale,
+                             const sage_tensor* k_mean, const sage_hadamard* hadamard,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* V quantization to FP8 e4m3 with one scale per channel ([Sage2 README]: the
+ * kernel fuses a per-channel V scale).  Per (b,h,d): amax over all Lk tokens,
+ * scale = fp32(amax / 448), code = e4m3_rne(fp32(v * fp32(448 / amax))).
+ *   v       F16/BF16 logical [B, Lk, H, D], any B/L/H strides
+ *   v_out   FP8_E4M3FN [B, H, D, SAGE_PAD(Lk)]  ("transposed V": keys contiguous;
+ *           keys >= Lk are 0)
+ *   v_scale F32 [B, H, D]
+ */
+sage_status sage_quantize_v_workspace_size(const sage_tensor* v, size_t* bytes);
+sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
+                            const sage_tensor* v_scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Quantized attention forward.  For each query row, KV tiles of 128 keys in
+ * ascending order: S = QK^T on INT8 (or scaled MXFP4) MFMA with int32 (fp32)
+ * accumulation; x = S * q_scale * k_scale * sm_scale * log2(e); online
+ * softmax with fp32 running max m and row sum l (l summed from the fp32
+ * probabilities, before conversion); P = e4m3(448 p), with 448 p evaluated as
+ * exp2(fma(S, c, -(m - log2 448))); O += P V on FP8 MFMA with fp32
+ * accumulation; out = O * v_scale[d] / (448 l), rounded to out's dtype,
+ * written with out's strides ([Sage2 README], [aiter #7388]: 448 = FP8_MAX
+ * of OCP e4m3).  Causal masks keep key j <= query i (Lq == Lk);
+ * fully masked tiles are skipped.
+ *   q_q, q_scale, k_q, k_scale: sage_quantize_qk outputs (mode = qk_mode)
+ *   v_q, v_scale: sage_quantize_v outputs
+ *   out: F16, BF16 or F32 logical [B, Lq, H, D], any B/L/H strides
+ * num_kv_heads: K/V heads (H % num_kv_heads == 0; query head h reads KV head
+ * h / (H / num_kv_heads)); 0 means H.  No workspace is needed (pass NULL, 0).
+ */
+typedef struct {
+    float sm_scale;        /* <= 0: 1/sqrt(D)                                  */
+    int32_t causal;
+    int32_t qk_mode;       /* sage_qk_mode                                     */
+    int32_t batch, heads, seqlen_q, seqlen_k, head_dim;
+    int32_t num_kv_heads;  /* 0: heads                                         */
+    int32_t q_block, k_block;  /* INT8 scale granularities used by quantize_qk */
+} sage_attn_params;
+
+sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale,
+                          const sage_tensor* k_q, const sage_tensor* k_scale,
+                          const sage_tensor* v_q, const sage_tensor* v_scale,
+                          const sage_attn_params* params, const sage_tensor* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Paged decode over an FP8 e4m3 KV cache ([aiter #7388]).
+ *   q          BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides), query token m sits
+ *              at position ctx_lens[b] - MTP + m
+ *   k_cache    FP8_E4M3FN [P, Hkv, page, D] contiguous
+ *   v_cache    FP8_E4M3FN [P, Hkv, D, page] contiguous when v_transposed = 1,
+ *              [P, Hkv, page, D] otherwise
+ *   k_scale, v_scale  F32 [P, Hkv, page] (per-token scales)
+ *   page_table I32 [B, max_pages]: page of token t is page_table[b][t / page]
+ *   ctx_lens   I32 [B]
+ *   out        BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides)
+ * With window W > 0 query position p sees keys [p - W + 1, p]; otherwise
+ * [0, p].  The work is split into 256-token tiles aligned to absolute
+ * positions, one split per tile (page: "each tile is its own task"); splits
+ * write (m, l, O) partials to the workspace and a merge step combines them.
+ * Q rows are quantized to e4m3 with a per-(token, head) scale; scores use FP8
+ * MFMA; P is requantized per tile with the tile's largest per-token V scale.
+ * D must be 128; the page size must be a multiple of 32 that divides 256 or
+ * is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
+ * below ctx_lens[b] must be valid page indices (device data is not checked),
+ * and ctx_lens[b] <= params.max_ctx.
+ */
+typedef struct {
+    float sm_scale;        /* <= 0: 1/sqrt(D)                  */
+    int32_t window;        /* 0: no sliding window             */
+    int32_t v_transposed;  /* layout flag of v_cache           */
+    int32_t max_ctx;       /* upper bound of ctx_lens (sizes the split plan) */
+} sage_decode_params;
+
+sage_status sage_paged_decode_workspace_size(const sage_tensor* q, const sage_tensor* k_cache,
+                                             const sage_tensor* page_table,
+                                             const sage_decode_params* params, size_t* bytes);
+sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache,
+                              const sage_tensor* v_cache, const sage_tensor* k_scale,
+                              const sage_tensor* v_scale, const sage_tensor* page_table,
+                              const sage_tensor* ctx_lens, const sage_decode_params* params,
+                              const sage_tensor* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Number of splits per sequence the plan uses for a window:
+ * (window + mtp - 1 - 1 + 255) / 256 + 1 when window > 0, else
+ * ceil(max_ctx / 256) ([aiter #7388] window tiles). */
+int32_t sage_decode_num_splits(int32_t window, int32_t mtp, int32_t max_ctx);
+
+/* ------------------------------------------------------------------------- */
+/* Helpers.                                                                   */
+
+/* Builds the order-R Sylvester Hadamard matrix scaled by 1/sqrt(R) on
+ * `device` (R must be 128).  The handle is immutable and may be shared by
+ * threads and calls; destroy it once no enqueued work uses it. */
+sage_status sage_hadamard_create(int32_t R, int32_t device, void* stream, sage_hadamard** out);
+sage_status sage_hadamard_destroy(sage_hadamard* h);
+
+/* Test hook: int32 S = Q8 K8^T for query rows [q0, q0 + nq) and keys
+ * [k0, k0 + nk) of every (b, h), computed by the attention kernel's own QK
+ * step (same MFMA shape, operand layout and reduction order).  q0 and nq must
+ * be multiples of 32, k0 and nk multiples of 128, inside the padded lengths
+ * of the INT8 q_q [B, H, Lqp, D] and k_q [B, H, Lkp, D].
+ *   out I32 [B, H, nq, nk] contiguous. */
+sage_status sage_debug_qk_tile(const sage_tensor* q_q, const sage_tensor* k_q,
+                               int32_t q0, int32_t nq, int32_t k0, int32_t nk,
+                               const sage_tensor* out, void* stream);
+
+/* Thread-local message of the last failure on this thread ("" if none). */
+const char* sage_last_error(void);
+/* (major << 16) | minor */
+int32_t sage_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H */

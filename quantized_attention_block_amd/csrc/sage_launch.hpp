@@ -1,0 +1,98 @@
+// Host-side launch interface between the C ABI layer (abi.cpp) and the gfx950
+// kernels.  Every launcher only enqueues on `stream` and returns the launch
+// status; all argument validation has already happened in abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+// A logical [B, L, H, D] half-precision view with element strides (stride of
+// D is 1).
+struct HalfView {
+    const void* ptr;
+    int64_t sB, sL, sH;
+    int bf16;   // 1: bfloat16, 0: float16
+};
+
+// Output view [B, L, H, D] with element strides.
+constexpr int kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2;
+struct OutView {
+    void* ptr;
+    int64_t sB, sL, sH;
+    int dtype;   // kOutF16 / kOutBF16 / kOutF32
+};
+
+constexpr int kKvTile = 128;       // KV tile of the attention kernel (and padding unit)
+constexpr int kMeanChunk = 256;    // tokens per partial sum of the K mean
+constexpr int kDecodeTile = 256;   // decode split length (tokens)
+
+__host__ __device__ inline int pad128(int L) { return (L + 127) / 128 * 128; }
+inline int mean_chunks(int L) { return (L + kMeanChunk - 1) / kMeanChunk; }
+
+// K mean: partial fp64 sums [B*H, nchunk, D] then mu fp32 [B*H, D].
+hipError_t launch_k_mean(const HalfView& k, int B, int H, int L, int D, double* partial,
+                         float* mu, hipStream_t stream);
+
+// INT8 block quantization of Q (q_block rows) and smoothed K (k_block rows).
+hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
+                                int Lk, int D, int q_block, int k_block, const float* mu,
+                                int8_t* q_out, float* q_scale, int8_t* k_out, float* k_scale,
+                                hipStream_t stream);
+
+// V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales.
+hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, uint32_t* amax_ws,
+                          uint8_t* v_out, float* v_scale, hipStream_t stream);
+
+// Hadamard rotation (optional) + MXFP4 quantization of Q and smoothed K.
+// hadamard_bf16 / hadamard_f16: 128x128 +-1 matrices (NULL: no rotation);
+// mu_rot_ws: fp32 [B*H, D] scratch for mu * H.
+hipError_t launch_quant_qk_mxfp4(const HalfView& q, const HalfView& k, int B, int H, int Lq,
+                                 int Lk, int D, const float* mu, const void* hadamard_bf16,
+                                 const void* hadamard_f16, float inv_sqrt_r, float* mu_rot_ws,
+                                 uint8_t* q_out, uint8_t* q_e8, uint8_t* k_out, uint8_t* k_e8,
+                                 hipStream_t stream);
+
+struct AttnArgs {
+    const void* q;        // int8 [B,H,Lqp,D] or fp4x2 [B,H,Lqp,D/2]
+    const void* q_scale;  // fp32 [B,H,Lqp/q_block] or e8m0 [B,H,Lqp,D/32]
+    const void* k;
+    const void* k_scale;
+    const uint8_t* v;     // e4m3 [B,Hkv,D,Lkp]
+    const float* v_scale; // [B,Hkv,D]
+    OutView out;
+    int B, H, Hkv, Lq, Lk, D;
+    int q_block, k_block;
+    int causal;
+    int mxfp4;
+    float sm_scale;
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+
+hipError_t launch_debug_qk(const int8_t* q, const int8_t* k, int B, int H, int Lqp, int Lkp,
+                           int D, int q0, int nq, int k0, int nk, int32_t* out,
+                           hipStream_t stream);
+
+struct DecodeArgs {
+    const void* q;            // bf16
+    int64_t q_sB, q_sM, q_sH;
+    const uint8_t* k_cache;   // [P,Hkv,page,D]
+    const uint8_t* v_cache;   // [P,Hkv,D,page] or [P,Hkv,page,D]
+    const float* k_scale;     // [P,Hkv,page]
+    const float* v_scale;
+    const int32_t* page_table;
+    int64_t pt_stride;
+    const int32_t* ctx_lens;
+    void* out;                // bf16
+    int64_t o_sB, o_sM, o_sH;
+    int B, MTP, Hq, Hkv, D, page, num_pages, max_pages;
+    int window, v_transposed, num_splits;
+    float sm_scale;
+    float* partials;          // [B, Hkv, num_splits, rows, D + 2]
+};
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_hadamard_build(int R, void* bf16_mat, void* f16_mat, hipStream_t stream);
+
+}  // namespace sage

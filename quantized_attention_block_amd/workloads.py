@@ -141,14 +141,17 @@ class PrefillInputs:
 
 
 def make_prefill(w: PrefillWorkload, Lq: Optional[int] = None, Lk: Optional[int] = None,
-                 device: str = "cpu") -> PrefillInputs:
+                 device: str = "cpu", B: Optional[int] = None,
+                 H: Optional[int] = None) -> PrefillInputs:
     """Draws Q, K, V for a prefill workload.
 
-    ``Lq``/``Lk`` override the sequence lengths (same distributions and seeds,
-    the first rows of a longer draw are NOT reused: a shorter draw is its own
-    sample), which the parity tests use for sizes the oracle finishes quickly.
+    ``Lq``/``Lk``/``B``/``H`` override the sizes (same distributions and seeds;
+    a smaller draw is its own sample, not a slice of the full one), which the
+    parity tests use for sizes the oracle finishes quickly.
     """
-    B, H, D = w.B, w.H, w.D
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    D = w.D
     Lq = w.Lq if Lq is None else Lq
     Lk = w.Lk if Lk is None else Lk
     cid = w.config_id
@@ -163,7 +166,7 @@ def make_prefill(w: PrefillWorkload, Lq: Optional[int] = None, Lk: Optional[int]
         k = _student_t(cid, T_K, (B, Lk, H, D))
         v = _normal(cid, T_V, (B, Lk, H, D))
         ch = outlier_channels(w)
-        for h in range(H):
+        for h in range(min(H, ch.shape[0])):
             q[:, :, h, ch[h]] *= np.float32(w.outlier_scale)
             k[:, :, h, ch[h]] *= np.float32(w.outlier_scale)
     else:

@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/sage.h declares, and refuses bad arguments before any HIP call (every
+case here fails validation, so no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def S():
+    from quantized_attention_block_amd import sage
+    if not os.path.exists(sage.LIB_PATH):
+        from quantized_attention_block_amd import build
+        build.build()
+    sage.lib()
+    return sage
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "sage.h")) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(S):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(S.lib(), n), n
+    assert S.lib().sage_version() == 1
+
+
+def test_decode_split_plan_matches_page_and_oracle(S, orc):
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "aiter7388_window_tiles.json")) as f:
+        g = json.load(f)
+    for window, tiles in g["cases"]:
+        assert S.sage_decode_num_splits(window, g["mtp"], 32768) == tiles
+        assert orc.decode_num_splits(window, g["mtp"], 256) == tiles
+    assert S.sage_decode_num_splits(0, 4, 8192) == 32
+    assert S.sage_decode_num_splits(4096, 4, 1000) == 4      # capped by the context
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced
+
+
+def T(dtype, shape, stride=None, data=FAKE):
+    d = S_mod().SageTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def S_mod():
+    from quantized_attention_block_amd import sage
+    return sage
+
+
+def _qk_call(S, q, k, prm, outs, ws_bytes=1 << 30, hadamard=None):
+    r = ctypes.byref
+    return S.lib().sage_quantize_qk(r(q), r(k), r(prm), r(outs[0]), r(outs[1]), r(outs[2]),
+                                    r(outs[3]), None, hadamard, ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def _int8_outs(S, B, H, Lq, Lk, D, kb=64):
+    p = lambda L: (L + 127) // 128 * 128
+    return (T(S.I8, (B, H, p(Lq), D)), T(S.F32, (B, H, p(Lq) // 128)),
+            T(S.I8, (B, H, p(Lk), D)), T(S.F32, (B, H, p(Lk) // kb)))
+
+
+def test_quantize_qk_refusals(S):
+    B, L, H, D = 1, 256, 2, 128
+    q = T(S.BF16, (B, L, H, D))
+    k = T(S.BF16, (B, L, H, D))
+    prm = S.QkParams(S.QK_INT8, 128, 64, 1)
+    outs = _int8_outs(S, B, H, L, L, D)
+    # head-dim stride must be 1
+    bad = T(S.BF16, (B, L, H, D), stride=(L * H * D * 2, H * D * 2, D * 2, 2))
+    assert _qk_call(S, bad, k, prm, outs) == S.ERR_LAYOUT
+    # row strides must be multiples of 16 bytes
+    bad = T(S.BF16, (B, L, H, D), stride=(L * H * 132, H * 132, 132, 1))
+    assert _qk_call(S, bad, k, prm, outs) == S.ERR_ALIGNMENT
+    # misaligned base pointer
+    assert _qk_call(S, T(S.BF16, (B, L, H, D), data=FAKE + 2), k, prm, outs) == S.ERR_ALIGNMENT
+    # unsupported dtype / head dim / block sizes
+    assert _qk_call(S, T(S.F32, (B, L, H, D)), k, prm, outs) == S.ERR_DTYPE
+    assert _qk_call(S, T(S.BF16, (B, L, H, 96)), T(S.BF16, (B, L, H, 96)), prm, outs) == S.ERR_SHAPE
+    assert _qk_call(S, q, k, S.QkParams(S.QK_INT8, 64, 64, 1), outs) == S.ERR_UNSUPPORTED
+    assert _qk_call(S, q, k, S.QkParams(7, 128, 64, 1), outs) == S.ERR_INVALID_ARG
+    # wrong output shape / dtype / layout
+    o = list(outs)
+    o[0] = T(S.I8, (B, H, 200, D))
+    assert _qk_call(S, q, k, prm, o) == S.ERR_SHAPE
+    o = list(outs)
+    o[1] = T(S.F16, (B, H, 2))
+    assert _qk_call(S, q, k, prm, o) == S.ERR_DTYPE
+    o = list(outs)
+    o[2] = T(S.I8, (B, H, 256, D), stride=(H * 256 * D, D, H * D, 1))
+    assert _qk_call(S, q, k, prm, o) == S.ERR_LAYOUT
+    # workspace too small
+    assert _qk_call(S, q, k, prm, outs, ws_bytes=16) == S.ERR_WORKSPACE
+    msg = S.lib().sage_last_error().decode()
+    assert "workspace" in msg
+    # MXFP4 needs D = 128 (BLOCK_R = 128)
+    q64, k64 = T(S.BF16, (B, L, H, 64)), T(S.BF16, (B, L, H, 64))
+    assert _qk_call(S, q64, k64, S.QkParams(S.QK_MXFP4, 128, 64, 1), outs) == S.ERR_SHAPE
+
+
+def test_hadamard_order_refused(S):
+    h = ctypes.c_void_p()
+    assert S.lib().sage_hadamard_create(64, 0, None, ctypes.byref(h)) == S.ERR_SHAPE
+    assert S.lib().sage_hadamard_create(256, 0, None, ctypes.byref(h)) == S.ERR_SHAPE
+    assert not h.value
+
+
+def test_attn_fwd_refusals(S):
+    B, L, H, D = 1, 256, 2, 128
+    r = ctypes.byref
+    qq, qs, kq, ks = _int8_outs(S, B, H, L, L, D)
+    vq = T(S.FP8_E4M3FN, (B, H, D, 256))
+    vs = T(S.F32, (B, H, D))
+    out = T(S.BF16, (B, L, H, D))
+
+    def call(prm, vq_=vq, out_=out):
+        return S.lib().sage_attn_fwd(r(qq), r(qs), r(kq), r(ks), r(vq_), r(vs), r(prm), r(out_),
+                                     None, 0, None)
+
+    good = dict(sm_scale=0.0, causal=0, qk_mode=S.QK_INT8, batch=B, heads=H, seqlen_q=L,
+                seqlen_k=L, head_dim=D, num_kv_heads=0, q_block=128, k_block=64)
+    P = lambda **kw: S.AttnParams(**{**good, **kw})
+    assert call(P(), vq_=T(S.FP8_E4M3FNUZ, (B, H, D, 256))) == S.ERR_DTYPE
+    assert "fnuz" in S.lib().sage_last_error().decode()
+    assert call(P(causal=1, seqlen_k=200)) == S.ERR_UNSUPPORTED
+    assert call(P(num_kv_heads=3)) == S.ERR_SHAPE
+    assert call(P(head_dim=96)) == S.ERR_SHAPE
+    assert call(P(), out_=T(S.BF16, (B, L, H, D), stride=(L * H * D, H * D, D, 2))) == S.ERR_LAYOUT
+    assert call(P(), out_=T(S.I32, (B, L, H, D))) == S.ERR_DTYPE
+    assert call(P(), out_=T(S.F32, (B, L, H, D), stride=(L * H * D, H * D, 2 * D + 2, 1))) == S.ERR_ALIGNMENT
+    assert call(P(seqlen_q=300)) == S.ERR_SHAPE          # q_q padded length no longer matches
+    assert call(P(sm_scale=float("nan"))) == S.ERR_INVALID_ARG
+
+
+def test_paged_decode_refusals(S):
+    B, MTP, Hq, D, P_, Hkv, page = 2, 4, 16, 128, 8, 1, 128
+    r = ctypes.byref
+    q = T(S.BF16, (B, MTP, Hq, D))
+    kc = T(S.FP8_E4M3FN, (P_, Hkv, page, D))
+    vc = T(S.FP8_E4M3FN, (P_, Hkv, D, page))
+    ksc = T(S.F32, (P_, Hkv, page))
+    vsc = T(S.F32, (P_, Hkv, page))
+    pt = T(S.I32, (B, 4))
+    cl = T(S.I32, (B,))
+    out = T(S.BF16, (B, MTP, Hq, D))
+
+    def call(prm, kc_=kc, vc_=vc, q_=q, ws=1 << 30, pt_=pt):
+        return S.lib().sage_paged_decode(r(q_), r(kc_), r(vc_), r(ksc), r(vsc), r(pt_), r(cl),
+                                         r(prm), r(out), ctypes.c_void_p(FAKE), ws, None)
+
+    prm = S.DecodeParams(0.0, 256, 1, 512)
+    # an FNUZ cache is not gfx950's MFMA format
+    assert call(prm, kc_=T(S.FP8_E4M3FNUZ, (P_, Hkv, page, D))) == S.ERR_DTYPE
+    assert call(prm, vc_=T(S.FP8_E4M3FNUZ, (P_, Hkv, D, page))) == S.ERR_DTYPE
+    assert call(prm, kc_=T(S.BF16, (P_, Hkv, page, D))) == S.ERR_DTYPE
+    assert call(prm, q_=T(S.F16, (B, MTP, Hq, D))) == S.ERR_DTYPE
+    assert call(prm, ws=64) == S.ERR_WORKSPACE
+    assert call(S.DecodeParams(0.0, 256, 1, 4096)) == S.ERR_SHAPE       # table too short
+    assert call(S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED  # plain V layout
+    assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
+    assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, 3, page, D)), vc_=T(S.FP8_E4M3FN, (P_, 3, D, page))) == S.ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from quantized_attention_block_amd import sage
+    monkeypatch.setattr(sage, "_lib", None)
+    monkeypatch.setattr(sage, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        sage.lib()

@@ -1,0 +1,92 @@
+"""Paged FP8 decode parity on the GPU: the full batch-16 / MTP4 / GQA16 /
+window-4096 workload against the oracle (every row), plus edge cases (no
+window, ragged and unequal contexts, MTP1, GQA8 on two KV heads, page 64),
+page-placement invariance and determinism."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_attention_block_amd import sage
+from quantized_attention_block_amd import workloads as wl
+from tests._util import cosine, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _run(inp, dev, window, max_ctx, sm_scale):
+    q = inp.q.to(dev)
+    kc = inp.k_cache.to(dev).view(torch.float8_e4m3fn)
+    vt = inp.v_cache.transpose(2, 3).contiguous().to(dev).view(torch.float8_e4m3fn)
+    out = sage.sage_paged_decode(q, kc, vt, inp.k_scale.to(dev), inp.v_scale.to(dev),
+                                 inp.page_table.to(dev), inp.ctx_lens.to(dev), max_ctx=max_ctx,
+                                 window=window, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _oracle(orc, inp, window, sm_scale, quant=True):
+    args = (inp.q.float().numpy(), inp.k_cache.numpy(), inp.v_cache.numpy(),
+            inp.k_scale.numpy(), inp.v_scale.numpy(), inp.page_table.numpy(),
+            inp.ctx_lens.numpy())
+    if quant:
+        return orc.paged_decode(*args, window=window, sm_scale=sm_scale)
+    kf = orc.e4m3_decode_array(args[1]) * args[3][..., None]
+    vf = orc.e4m3_decode_array(args[2]) * args[4][..., None]
+    return orc.paged_decode(args[0], kf, vf, np.ones_like(args[3]), np.ones_like(args[4]),
+                            args[5], args[6], window=window, sm_scale=sm_scale, quant=False)
+
+
+def _check(g, o, e):
+    assert cosine(g, o) >= 0.999
+    assert np.abs(g - o).max() <= 1e-2
+    assert cosine(g, e) >= 0.99
+
+
+def test_paged_decode_full_workload(dev, orc):
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w)
+    say("paged decode full workload")
+    g = _run(inp, dev, w.window, w.ctx, w.sm_scale)
+    _check(g, _oracle(orc, inp, w.window, w.sm_scale), _oracle(orc, inp, w.window, w.sm_scale, False))
+    # determinism
+    assert np.array_equal(g, _run(inp, dev, w.window, w.ctx, w.sm_scale))
+
+
+@pytest.mark.parametrize("window,ctx", [(0, 1000), (4096, 700), (300, 1537), (1, 512)])
+def test_paged_decode_windows_and_contexts(dev, orc, window, ctx):
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=3, ctx=ctx)
+    inp.ctx_lens[1] = max(4, ctx - 257)          # unequal contexts in one batch
+    inp.ctx_lens[2] = max(4, ctx // 3)
+    say("paged decode", window, ctx)
+    g = _run(inp, dev, window, ctx, w.sm_scale)
+    _check(g, _oracle(orc, inp, window, w.sm_scale), _oracle(orc, inp, window, w.sm_scale, False))
+
+
+@pytest.mark.parametrize("mtp,hq,hkv,page", [(1, 16, 1, 128), (4, 16, 2, 128), (2, 8, 1, 64),
+                                             (4, 16, 1, 256)])
+def test_paged_decode_shapes(dev, orc, mtp, hq, hkv, page):
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("v", 9, 4, mtp, hq, hkv, 128, page, 1200, 512)
+    inp = wl.make_decode(w)
+    say("paged decode shape", mtp, hq, hkv, page)
+    g = _run(inp, dev, w.window, w.ctx, base.sm_scale)
+    _check(g, _oracle(orc, inp, w.window, base.sm_scale), _oracle(orc, inp, w.window, base.sm_scale, False))
+
+
+def test_page_placement_invariance(dev):
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=4, ctx=2000)
+    say("page placement")
+    a = _run(inp, dev, 1024, 2000, w.sm_scale)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(inp.k_cache.shape[0]))
+    inv = torch.argsort(perm)
+    moved = wl.DecodeInputs(inp.q, inp.k_cache[perm], inp.v_cache[perm], inp.k_scale[perm],
+                            inp.v_scale[perm], inv[inp.page_table.long()].int(), inp.ctx_lens)
+    b = _run(moved, dev, 1024, 2000, w.sm_scale)
+    assert np.array_equal(a, b)

@@ -1,0 +1,113 @@
+"""Quantizer parity on the GPU: INT8 Q/K codes and scales, the K mean, e4m3 V
+codes and scales, and MXFP4 codes/E8M0 scales, bit-exact against the oracle
+(INT8 K is compared given the GPU's mean, which must itself equal the
+oracle's)."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_attention_block_amd import sage
+from quantized_attention_block_amd import workloads as wl
+from tests._util import canon, require_gpu, say, u8
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny", dict()),                                   # fp16, D=64, 2 Q / 4 K blocks
+    ("llm_prefill", dict(Lq=520, Lk=520, B=1, H=3)),    # ragged tail, bf16, D=128
+    ("video_dit", dict(Lq=1000, Lk=1000, H=3)),         # stacked strided views, outliers
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("name,kw", CASES)
+@pytest.mark.parametrize("k_block", [64, 128])
+def test_int8_qk_bit_exact(dev, orc, name, kw, k_block):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    say("int8 quantize", name, kw, k_block)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_INT8, k_block=k_block)
+    torch.cuda.synchronize()
+    qc, kc = canon(inp.q), canon(inp.k)
+    Lq, Lk = qc.shape[2], kc.shape[2]
+    mu_o = orc.k_mean(kc)
+    mu_g = qk.k_mean.cpu().numpy()
+    assert np.array_equal(mu_g, mu_o)
+    q8, qs = orc.quant_int8(qc, 128)
+    k8, ks = orc.quant_int8(orc.smooth_k(kc, mu_g), k_block)
+    gq, gk = qk.q.cpu().numpy(), qk.k.cpu().numpy()
+    assert np.array_equal(gq[:, :, :Lq], q8) and not gq[:, :, Lq:].any()
+    assert np.array_equal(gk[:, :, :Lk], k8) and not gk[:, :, Lk:].any()
+    gqs, gks = qk.q_scale.cpu().numpy(), qk.k_scale.cpu().numpy()
+    assert np.array_equal(gqs, qs)
+    assert np.array_equal(gks[..., :ks.shape[-1]], ks) and not gks[..., ks.shape[-1]:].any()
+
+
+@pytest.mark.parametrize("name,kw", CASES)
+def test_v_fp8_bit_exact(dev, orc, name, kw):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    say("v quantize", name, kw)
+    v_q, v_s = sage.sage_quantize_v(inp.v)
+    torch.cuda.synchronize()
+    vc = canon(inp.v)
+    L = vc.shape[2]
+    v8, vs = orc.quant_v_fp8(vc)
+    g = u8(v_q).transpose(0, 1, 3, 2)          # [B,H,Lkp,D]
+    assert np.array_equal(g[:, :, :L], v8) and not g[:, :, L:].any()
+    assert np.array_equal(v_s.cpu().numpy(), vs)
+
+
+@pytest.mark.parametrize("name,kw", CASES[1:])
+def test_mxfp4_without_rotation_bit_exact(dev, orc, name, kw):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    say("mxfp4 quantize (no rotation)", name, kw)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4)
+    torch.cuda.synchronize()
+    qc, kc = canon(inp.q), canon(inp.k)
+    Lq, Lk = qc.shape[2], kc.shape[2]
+    mu_g = qk.k_mean.cpu().numpy()
+    assert np.array_equal(mu_g, orc.k_mean(kc))
+    q4, qe = orc.quant_mxfp4(qc)
+    k4, ke = orc.quant_mxfp4(orc.smooth_k(kc, mu_g))
+    gq = orc.unpack_fp4(qk.q.cpu().numpy())
+    gk = orc.unpack_fp4(qk.k.cpu().numpy())
+    assert np.array_equal(gq[:, :, :Lq], q4) and not gq[:, :, Lq:].any()
+    assert np.array_equal(gk[:, :, :Lk], k4) and not gk[:, :, Lk:].any()
+    assert np.array_equal(qk.q_scale.cpu().numpy()[:, :, :Lq], qe)
+    assert np.array_equal(qk.k_scale.cpu().numpy()[:, :, :Lk], ke)
+
+
+@pytest.mark.parametrize("name,kw", CASES[1:])
+def test_mxfp4_with_hadamard(dev, orc, name, kw):
+    """The rotation sums 128 products in fp32 on MFMA, so a value that sits on
+    an E2M1 rounding boundary can round the other way than the oracle's
+    correctly rounded sum: codes agree except on such boundary cases, and the
+    dequantized values agree to within one code step."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    had = sage.Hadamard(0)
+    say("mxfp4 quantize (hadamard)", name, kw)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4, hadamard=had)
+    torch.cuda.synchronize()
+    qc, kc = canon(inp.q), canon(inp.k)
+    mu = qk.k_mean.cpu().numpy()
+    vals = np.array([orc.e2m1_decode(c) for c in range(16)], np.float32)
+    for x, codes, e8 in ((orc.rotate(qc), qk.q, qk.q_scale),
+                         (orc.rotate(orc.smooth_k(kc, mu)), qk.k, qk.k_scale)):
+        L = x.shape[2]
+        o4, oe = orc.quant_mxfp4(x)
+        g4 = orc.unpack_fp4(codes.cpu().numpy())[:, :, :L]
+        ge = e8.cpu().numpy()[:, :, :L]
+        assert (ge == oe).mean() > 0.999
+        assert (g4 == o4).mean() > 0.995
+        deq = lambda c, e: vals[c] * np.repeat(2.0 ** (e.astype(np.float32) - 127), 32, axis=-1)
+        same_e = np.repeat(ge == oe, 32, axis=-1)
+        step = np.repeat(2.0 ** (oe.astype(np.float32) - 127), 32, axis=-1) * 2.0
+        diff = np.abs(deq(g4, ge) - deq(o4, oe))
+        assert (diff[same_e] <= step[same_e] + 1e-30).all()
