@@ -148,13 +148,23 @@ def decode_bench(steps, warmup, dev, pools=32):
     for _ in range(warmup * 10):
         call()
     torch.cuda.synchronize()
+    # one decode (decode + merge kernels) per pool, captured once and replayed:
+    # the device time per call without Python launch overhead
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(pools):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    t = min(_events_time(call, max(200, steps * 20), stream) for _ in range(5))
+    t = min(_events_time(graph.replay, max(10, steps), stream) for _ in range(5)) / pools
+    t_eager = _events_time(call, 200, stream)
     keys = min(w.ctx, w.window + w.mtp - 1)
     alg_bytes = w.batch * w.hkv * keys * (2 * w.D + 8) + 2 * (w.batch * w.mtp * w.hq * w.D * 2)
     gbs = alg_bytes / t / 1e9
     return {"metric": "paged FP8 decode HBM GB/s (decode + merge)", "value": round(gbs, 1),
-            "unit": "GB/s", "us_per_call": round(t * 1e6, 3), "algorithmic_bytes": alg_bytes,
+            "unit": "GB/s", "us_per_call": round(t * 1e6, 3),
+            "us_per_call_eager_python": round(t_eager * 1e6, 2), "algorithmic_bytes": alg_bytes,
             "workload": "batch16 MTP4 GQA16 D128 page128 ctx8192 window4096 fp8-e4m3 per-token",
             "kv_pools_rotated": pools,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -188,9 +198,11 @@ def cpu_baseline(wname, target_s=15.0):
                                      rows=rows, nthreads=cores)
         return time.perf_counter() - t0
 
-    probe_rows = 64
-    tp = run(probe_rows)
-    nrows = int(max(probe_rows, min(200000, probe_rows * target_s / max(tp, 1e-3))))
+    # the per-run cost is one head's quantization plus a per-row emulation
+    # cost: two probes give both, then the sample is sized to ~target_s
+    t1, t2 = run(64), run(512)
+    per_row = max((t2 - t1) / 448.0, 1e-7)
+    nrows = int(max(512, min(2_000_000, (target_s - t1) / per_row)))
     t = run(nrows)
     literal = 4.0 * nrows * w.Lk * w.D      # same formula per query row as the GPU value
     return {"value": round(literal / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",

@@ -62,13 +62,20 @@ __device__ __forceinline__ int kappa(int r) {
     return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
+// XOR swizzles of the 16-byte chunks of an LDS row.  gfx950's LDS serves a
+// 16-byte-per-lane read 16 lanes at a time over 64 four-byte banks, so the 16
+// rows one such lane group reads (rows kappa(0..15) or kappa(16..31) of a
+// sub-tile for K, 16 consecutive channels for V) must land in 16 distinct
+// 16-byte bank groups.
 template <int D, bool MX>
 __device__ __forceinline__ int k_swz(int r) {
-    constexpr int n = Geo<D, MX>::kRowChunks;
-    return ((r & 3) | ((r >> 2) & 4)) & (n - 1);
+    if constexpr (Geo<D, MX>::kRowChunks == 8)          // 128-byte rows: 2 rows per bank sweep
+        return ((r >> 1) & 3) | ((r >> 2) & 4);
+    else                                               // 64-byte rows: 4 rows per bank sweep
+        return ((r >> 2) & 1) | ((r >> 3) & 2);
 }
 
-__device__ __forceinline__ int v_swz(int d) { return d & 7; }
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
 template <int D, bool MX>
 __device__ __forceinline__ uint8_t* k_lds_addr(uint8_t* base, int r, int c) {
@@ -79,77 +86,71 @@ __device__ __forceinline__ uint8_t* v_lds_addr(uint8_t* vbase, int d, int c) {
     return vbase + d * kBN + 16 * (c ^ v_swz(d));
 }
 
-// Cooperative load of one KV tile (K codes, K E8M0 scales for MXFP4, V^T
-// codes) into registers, then into one LDS stage.  nthr threads take part.
-template <int D, bool MX, int NTHR>
-struct TileLoader {
+// One KV tile (K codes, K E8M0 scales for MXFP4, V^T codes) is copied from
+// global memory straight into an LDS stage with gfx950's 16-byte global->LDS
+// loads: each wave instruction fills 64 consecutive 16-byte LDS chunks (lane
+// i -> chunk i), so the XOR swizzle is applied on the global side by letting
+// lane i fetch the chunk that belongs at its LDS position.  Completion is
+// awaited with s_waitcnt vmcnt(0) followed by a block barrier.
+template <int D, bool MX, int NWAVES>
+struct TileDma {
     using G = Geo<D, MX>;
     static constexpr int kKChunks = G::kKBytes / 16;
     static constexpr int kVChunks = G::kVBytes / 16;
-    static constexpr int kKLoads = (kKChunks + NTHR - 1) / NTHR;
-    static constexpr int kVLoads = (kVChunks + NTHR - 1) / NTHR;
-    static constexpr int kSLoads = (G::kKScaleBytes / 16 + NTHR - 1) / NTHR;
-    uint4 kr[kKLoads];
-    uint4 vr[kVLoads];
-    uint4 sr[kSLoads > 0 ? kSLoads : 1];
+    static constexpr int kKSChunks = G::kKScaleBytes / 16;
+    static constexpr int kKRegions = kKChunks / 64;   // 1 KB regions
+    static constexpr int kVRegions = kVChunks / 64;
+    static_assert(kKChunks % 64 == 0 && kVChunks % 64 == 0, "tile must be whole 1 KB regions");
+    static_assert(kKRegions % NWAVES == 0 && kVRegions % NWAVES == 0, "regions split evenly");
+    static_assert(kKSChunks <= 64, "K scales fit one wave instruction");
 
-    // kbase: K codes of this (b, kv head) [Lkp][row bytes]; kscale: [Lkp][D/32]
-    // vbase: V^T of this (b, kv head) [D][Lkp]
-    __device__ __forceinline__ void load(const uint8_t* kbase, const uint8_t* kscale,
-                                         const uint8_t* vbase, int Lkp, int kt, int tid,
-                                         bool with_v = true) {
+    // kr: K codes of this (b, kv head) [Lkp][row bytes]; ksr: its E8M0 scales
+    // [Lkp][D/32] (MXFP4); vr: V^T of this (b, kv head) [D][Lkp].  Buffer
+    // resources bound to exactly those extents (reads outside return 0); the
+    // tile offset goes in the scalar offset, the swizzled chunk offset in the
+    // per-lane offset.
+    __device__ __forceinline__ static void issue(uint8_t* stage, __amdgpu_buffer_rsrc_t kr,
+                                                 __amdgpu_buffer_rsrc_t ksr,
+                                                 __amdgpu_buffer_rsrc_t vr, int Lkp, int kt,
+                                                 int wave, int lane, bool with_v = true) {
 #pragma unroll
-        for (int i = 0; i < kKLoads; ++i) {
-            const int g = tid + NTHR * i;
-            if (g < kKChunks)
-                kr[i] = *(const uint4*)(kbase + (int64_t)kt * G::kKBytes + 16 * g);
+        for (int j = 0; j < kKRegions / NWAVES; ++j) {
+            const int region = j * NWAVES + wave;
+            const int p = region * 64 + lane;                  // LDS chunk position
+            const int r = p / G::kRowChunks;
+            const int c = (p % G::kRowChunks) ^ k_swz<D, MX>(r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, stage + region * 1024, 16,
+                                                     r * G::kRowBytes + 16 * c, kt * G::kKBytes, 0, 0);
         }
         if constexpr (MX) {
-#pragma unroll
-            for (int i = 0; i < kSLoads; ++i) {
-                const int g = tid + NTHR * i;
-                if (g < G::kKScaleBytes / 16)
-                    sr[i] = *(const uint4*)(kscale + (int64_t)kt * G::kKScaleBytes + 16 * g);
-            }
+            if (wave == 0 && lane < kKSChunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksr, stage + G::kKBytes, 16, 16 * lane,
+                                                         kt * G::kKScaleBytes, 0, 0);
         }
         if (!with_v) return;
+        uint8_t* vstage = stage + G::kKBytes + G::kKScaleBytes;
 #pragma unroll
-        for (int i = 0; i < kVLoads; ++i) {
-            const int g = tid + NTHR * i;
-            if (g < kVChunks) {
-                const int d = g / G::kVChunksPerRow, c = g % G::kVChunksPerRow;
-                vr[i] = *(const uint4*)(vbase + (int64_t)d * Lkp + (int64_t)kt * kBN + 16 * c);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t* stage, int tid, bool with_v = true) {
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i) {
-            const int g = tid + NTHR * i;
-            if (g < kKChunks) {
-                const int r = g / G::kRowChunks, c = g % G::kRowChunks;
-                *(uint4*)k_lds_addr<D, MX>(stage, r, c) = kr[i];
-            }
-        }
-        if constexpr (MX) {
-#pragma unroll
-            for (int i = 0; i < kSLoads; ++i) {
-                const int g = tid + NTHR * i;
-                if (g < G::kKScaleBytes / 16) *(uint4*)(stage + G::kKBytes + 16 * g) = sr[i];
-            }
-        }
-        if (!with_v) return;
-        uint8_t* vb = stage + G::kKBytes + G::kKScaleBytes;
-#pragma unroll
-        for (int i = 0; i < kVLoads; ++i) {
-            const int g = tid + NTHR * i;
-            if (g < kVChunks) {
-                const int d = g / G::kVChunksPerRow, c = g % G::kVChunksPerRow;
-                *(uint4*)v_lds_addr(vb, d, c) = vr[i];
-            }
+        for (int j = 0; j < kVRegions / NWAVES; ++j) {
+            const int region = j * NWAVES + wave;
+            const int p = region * 64 + lane;
+            const int d = p / G::kVChunksPerRow;
+            const int c = (p % G::kVChunksPerRow) ^ v_swz(d);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vstage + region * 1024, 16, d * Lkp + 16 * c,
+                                                     kt * kBN, 0, 0);
         }
     }
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    // raw buffer, stride 0, bounds = bytes; dword 3 = gfx9 raw-buffer config
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void wait_dma() {
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's LDS DMA has landed
+}
 
 // Q fragment of one wave: query row (l % 32) of the wave's 32 rows.
 // INT8: 16-byte chunk (2 c + half) for c < D/32.  MXFP4: chunk (2 c + half)
@@ -188,12 +189,43 @@ __device__ __forceinline__ v16f qk_subtile_mx(uint8_t* stage, const QFrag<D, tru
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
         const v4i a4 = *(const v4i*)k_lds_addr<D, true>(stage, r, 2 * c + half);
-        const v8i a = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
-        const v8i b = {q.f[c][0], q.f[c][1], q.f[c][2], q.f[c][3], 0, 0, 0, 0};
+        // fp4 operands occupy the low four dwords; the upper four are not read
+        const v8i a = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+        const v8i b = __builtin_shufflevector(q.f[c], q.f[c], 0, 1, 2, 3, -1, -1, -1, -1);
         const int sa = ks[r * (D / 32) + 2 * c + half];
         acc = mfma_f4_32x32x64(a, b, acc, sa, q.s[c]);
     }
     return acc;
+}
+
+// QK of the four 32-key sub-tiles of a staged tile, with the K fragments of
+// sub-tile t+1 read from LDS before the MFMAs of sub-tile t.
+template <int D, bool MX, class SAcc>
+__device__ __forceinline__ void qk_tile(uint8_t* stage, const QFrag<D, MX>& q, int lane, SAcc* S) {
+    if constexpr (MX) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t] = qk_subtile_mx<D>(stage, q, t, lane);
+    } else {
+        constexpr int NC = D / 32;
+        const int half = lane >> 5, col = lane & 31;
+        v4i kf[2][NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            kf[0][c] = *(const v4i*)k_lds_addr<D, false>(stage, kappa(col), 2 * c + half);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t + 1 < 4) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    kf[(t + 1) & 1][c] = *(const v4i*)k_lds_addr<D, false>(
+                        stage, 32 * (t + 1) + kappa(col), 2 * c + half);
+            }
+            v16i acc = {0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc = mfma_i8_32x32x32(kf[t & 1][c], q.f[c], acc);
+            S[t] = acc;
+        }
+    }
 }
 
 template <int D, bool MX>
@@ -233,7 +265,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int b = bh / a.H, h = bh % a.H;
     const int hk = h / (a.H / a.Hkv);
     const int bhk = b * a.Hkv + hk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int half = lane >> 5, col = lane & 31;
     const int q0w = qb * kBM + wave * 32;
     const int qrow = q0w + col;
@@ -254,8 +287,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (!MX) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
     const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
 
-    TileLoader<D, MX, kThreads> ld;
-    ld.load(kbase, ksc, vbase, Lkp, 0, tid);
+    using Dma = TileDma<D, MX, 4>;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)Lkp * G::kRowBytes);
+    const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(MX ? ksc : kbase, MX ? (int64_t)Lkp * (D / 32) : 16);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (int64_t)D * Lkp);
+    Dma::issue(smem, krs, ksrs, vrs, Lkp, 0, wave, lane);
+    // INT8: the two 64-key block scales of the next tile, folded with q_scale
+    // and alpha (c = fp32(fp32(q_s k_s) alpha)); prefetched one tile ahead.
+    const int kb_per_tile = MX ? 0 : kBN / a.k_block;
+    float ksn[2] = {0.0f, 0.0f};
+    if constexpr (!MX) {
+        ksn[0] = kscale_f[0];
+        ksn[1] = kscale_f[kb_per_tile - 1];
+    }
 
     v16f O[kDB];
 #pragma unroll
@@ -264,105 +308,142 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     for (int kt = 0; kt < ntiles; ++kt) {
         uint8_t* stage = smem + (kt & 1) * G::kStageBytes;
-        ld.store(stage, tid);
+        wait_dma();
         __syncthreads();
-        if (kt + 1 < ntiles) ld.load(kbase, ksc, vbase, Lkp, kt + 1, tid);
+        float ksc_t[2] = {ksn[0], ksn[1]};
+        if (kt + 1 < ntiles) {
+            Dma::issue(smem + ((kt + 1) & 1) * G::kStageBytes, krs, ksrs, vrs, Lkp, kt + 1, wave, lane);
+            if constexpr (!MX) {
+                ksn[0] = kscale_f[(kt + 1) * kb_per_tile];
+                ksn[1] = kscale_f[(kt + 1) * kb_per_tile + kb_per_tile - 1];
+            }
+        }
 
         const int key0 = kt * kBN;
         // waves whose every key of this tile is causally masked skip it
         if (a.causal && key0 > q0w + 31) continue;
         const bool full = (key0 + kBN <= a.Lk) && (!a.causal || key0 + kBN - 1 <= q0w);
 
-        // ---- QK^T and the tile's row max --------------------------------
-        // S holds int32 scores (INT8) or fp32 scores (MXFP4) of 4 sub-tiles;
+        // S holds int32 (INT8) or fp32 (MXFP4) scores of the 4 sub-tiles;
         // element (t, e) is key key0 + 32 t + 16 half + e of query qrow.
         using SAcc = typename std::conditional<MX, v16f, v16i>::type;
-        SAcc S[kNT];
         float c[kNT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            if constexpr (MX) {
-                S[t] = qk_subtile_mx<D>(stage, qf, t, lane);
-                c[t] = alpha;
-            } else {
-                S[t] = qk_subtile_i8<D>(stage, qf, t, lane);
-                c[t] = (q_s * kscale_f[(key0 + 32 * t) / a.k_block]) * alpha;
-            }
-        }
-        auto visible = [&](int t, int e) {
-            const int key = key0 + 32 * t + 16 * half + e;
-            return key < a.Lk && (!a.causal || key <= qrow);
-        };
-        float tmax = -INFINITY;
-        if (full) {
+        for (int t = 0; t < kNT; ++t) c[t] = MX ? alpha : (q_s * ksc_t[t < 2 ? 0 : 1]) * alpha;
+
+        // The tile body, instantiated once for full tiles and once for tiles
+        // that cross the causal diagonal or the ragged end.  In the latter,
+        // each 32-key sub-tile is (wave-uniformly) empty, crossing or full for
+        // this wave's 32 rows: empty sub-tiles skip their MFMAs and exps and
+        // only crossing ones test keys one by one.
+        auto tile_body = [&](auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            int st[kNT];   // 0 empty, 1 crossing, 2 full
 #pragma unroll
             for (int t = 0; t < kNT; ++t) {
-                auto mx = S[t][0];
-#pragma unroll
-                for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
-                tmax = fmaxf(tmax, (float)mx * c[t]);   // rounding is monotone
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (visible(t, e)) tmax = fmaxf(tmax, (float)S[t][e] * c[t]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-
-        // ---- online softmax update -----------------------------------------
-        const float m_new = fmaxf(m, tmax);
-        if (__any(m_new > m)) {
-            const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-            l *= sc;
-#pragma unroll
-            for (int i = 0; i < kDB; ++i) O[i] *= sc;
-        }
-        m = m_new;
-        const float mb = (m_new == -INFINITY ? 0.0f : m_new) - kLog2Fp8Max;
-
-        // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
-        // accumulates q (so l = 448 * sum p).  Packed into the PV B operand:
-        // byte 16 t' + e of group u is key 64 u + 32 t' + 16 half + e.
-        v8i pf[2];
-        float ls0 = 0.0f, ls1 = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int t = 2 * u + w / 4, e0 = 4 * (w % 4);
-                float p[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float xv = __builtin_fmaf((float)S[t][e0 + j], c[t], -mb);
-                    if (!full && !visible(t, e0 + j)) xv = -INFINITY;
-                    p[j] = __builtin_amdgcn_exp2f(xv);
+                if constexpr (FULL) {
+                    st[t] = 2;
+                } else {
+                    const int lo = key0 + 32 * t, hi = lo + 31;
+                    const bool empty = lo >= a.Lk || (a.causal && lo > q0w + 31);
+                    const bool whole = hi < a.Lk && (!a.causal || hi <= q0w);
+                    st[t] = empty ? 0 : (whole ? 2 : 1);
                 }
-                ls0 += p[0] + p[1];
-                ls1 += p[2] + p[3];
-                uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], 0);
-                pk = cvt_pk_fp8<true>(p[2], p[3], pk);
-                pf[u][w] = (int)pk;
             }
-        l += ls0 + ls1;
+            auto visible = [&](int t, int e) {
+                const int key = key0 + 32 * t + 16 * half + e;
+                return key < a.Lk && (!a.causal || key <= qrow);
+            };
+            SAcc S[kNT];
+            if constexpr (FULL) {
+                qk_tile<D, MX>(stage, qf, lane, S);
+            } else {
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    if (st[t] == 0) continue;
+                    if constexpr (MX)
+                        S[t] = qk_subtile_mx<D>(stage, qf, t, lane);
+                    else
+                        S[t] = qk_subtile_i8<D>(stage, qf, t, lane);
+                }
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) {
+                if (st[t] == 2) {
+                    auto mx = S[t][0];
+#pragma unroll
+                    for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
+                    tmax = fmaxf(tmax, (float)mx * c[t]);   // rounding is monotone
+                } else if (st[t] == 1) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        tmax = fmaxf(tmax, visible(t, e) ? (float)S[t][e] * c[t] : -INFINITY);
+                }
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
 
-        // ---- O^T += V^T P^T ---------------------------------------------------
-        uint8_t* vb = stage + G::kKBytes + G::kKScaleBytes;
+            // ---- online softmax update -------------------------------------
+            const float m_new = fmaxf(m, tmax);
+            if (__any(m_new > m)) {
+                const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+                l *= sc;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int db = 0; db < kDB; ++db) {
-                const int d = 32 * db + col;
-                const v4i lo = *(const v4i*)v_lds_addr(vb, d, 4 * u + half);
-                const v4i hi = *(const v4i*)v_lds_addr(vb, d, 4 * u + 2 + half);
-                const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                O[db] = mfma_f8_32x32x64(av, pf[u], O[db]);
+                for (int i = 0; i < kDB; ++i) O[i] *= sc;
             }
+            m = m_new;
+            const float mb = (m_new == -INFINITY ? 0.0f : m_new) - kLog2Fp8Max;
+
+            // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
+            // accumulates q (so l = 448 * sum p).  Packed into the PV B operand:
+            // byte 16 t' + e of group u is key 64 u + 32 t' + 16 half + e; the PV
+            // MFMAs of group u follow its conversion so they overlap group u+1's.
+            uint8_t* vb = stage + G::kKBytes + G::kKScaleBytes;
+            float ls = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (st[2 * u] == 0 && st[2 * u + 1] == 0) continue;
+                v8i pf;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const int t = 2 * u + w / 4, e0 = 4 * (w % 4);
+                    if (st[t] == 0) {
+                        pf[w] = 0;
+                        continue;
+                    }
+                    float p[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float xv = __builtin_fmaf((float)S[t][e0 + j], c[t], -mb);
+                        if (st[t] == 1 && !visible(t, e0 + j)) xv = -INFINITY;
+                        p[j] = __builtin_amdgcn_exp2f(xv);
+                    }
+                    ls += (p[0] + p[1]) + (p[2] + p[3]);
+                    uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], 0);
+                    pk = cvt_pk_fp8<true>(p[2], p[3], pk);
+                    pf[w] = (int)pk;
+                }
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) {
+                    const int d = 32 * db + col;
+                    const v4i lo = *(const v4i*)v_lds_addr(vb, d, 4 * u + half);
+                    const v4i hi = *(const v4i*)v_lds_addr(vb, d, 4 * u + 2 + half);
+                    const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    O[db] = mfma_f8_32x32x64(av, pf, O[db]);
+                }
+            }
+            l += ls;
+        };
+        if (full)
+            tile_body(std::true_type{});
+        else
+            tile_body(std::false_type{});
     }
 
-    // ---- epilogue: out = (O * v_scale) / l, written with the caller's strides
+    // ---- epilogue: out = (O * v_scale) / l (times the reciprocal of l), written
+    // with the caller's strides
     const float lt = l + __shfl_xor(l, 32);
+    const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;   // one division per row
     if (qrow < a.Lq) {
         const float* vs = a.v_scale + (int64_t)bhk * D;
         const int64_t ooff = (int64_t)b * a.out.sB + (int64_t)qrow * a.out.sL + (int64_t)h * a.out.sH;
@@ -374,7 +455,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    o[j] = lt > 0.0f ? (O[db][4 * i + j] * vs[d0 + j]) / lt : 0.0f;
+                    o[j] = (O[db][4 * i + j] * vs[d0 + j]) * inv_l;
                 if (a.out.dtype == kOutF32) {
                     *(float4*)((float*)a.out.ptr + ooff + d0) = make_float4(o[0], o[1], o[2], o[3]);
                 } else {
@@ -409,9 +490,9 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* 
     const uint8_t* qbase = (const uint8_t*)q + (int64_t)bh * Lqp * D;
     const uint8_t* kbase = (const uint8_t*)k + (int64_t)bh * Lkp * D + (int64_t)k0 * D;
     // stage K rows [k0 + 128 kg, +128); the V part of the stage is not used
-    TileLoader<D, false, 64> ld;
-    ld.load(kbase, nullptr, nullptr, 0, kg, lane, false);
-    ld.store(stage, lane, false);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)nk * D);
+    TileDma<D, false, 1>::issue(stage, krs, krs, krs, 0, kg, 0, lane, false);
+    wait_dma();
     __syncthreads();
     QFrag<D, false> qf;
     load_qfrag<D, false>(qf, qbase, nullptr, q0 + 32 * qg + col, lane);

@@ -271,40 +271,52 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     }
 }
 
-// Merge of the split partials of one (sequence, KV head): m* = max m_s,
-// out = sum 2^(m_s - m*) O_s / sum 2^(m_s - m*) l_s (split order), bf16.
-__global__ __launch_bounds__(kThreads) void k_decode_merge(DecodeArgs a) {
-    const int bk = blockIdx.x, b = bk / a.Hkv, hk = bk % a.Hkv;
+// Merge of the split partials of one (sequence, KV head, row): m* = max m_s,
+// out = sum 2^(m_s - m*) O_s / sum 2^(m_s - m*) l_s (fp32, split order), bf16.
+// One wave per row: lane s holds split s's (m, l) (splits beyond 64 are
+// folded in lane order); the weights are broadcast and every lane then merges
+// two output channels over all splits with coalesced loads.
+constexpr int kMergeRowsPerBlock = 4;
+
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int rowg = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    const int R = a.MTP * (a.Hq / a.Hkv);
+    const int bk = rowg / kRows, r = rowg % kRows;
+    if (bk >= a.B * a.Hkv || r >= R) return;
+    const int b = bk / a.Hkv, hk = bk % a.Hkv;
     const int ctx = a.ctx_lens[b];
-    const int G = a.Hq / a.Hkv, R = a.MTP * G;
+    const int G = a.Hq / a.Hkv;
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
-    for (int item = threadIdx.x; item < R * (kD / 4); item += kThreads) {
-        const int r = item / (kD / 4), d0 = 4 * (item % (kD / 4));
-        const float* base = a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartStride;
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, base[(int64_t)sp * kRows * kPartStride + kD]);
-        float L = 0.0f, o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-        for (int sp = 0; sp < nsp; ++sp) {
-            const float* p = base + (int64_t)sp * kRows * kPartStride;
-            const float ms = p[kD];
-            if (ms == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(ms - M);
-            L = L + w * p[kD + 1];
-            const float4 o = *(const float4*)(p + d0);
-            o0 = o0 + w * o.x;
-            o1 = o1 + w * o.y;
-            o2 = o2 + w * o.z;
-            o3 = o3 + w * o.w;
+    const float* base = a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartStride;
+    const int64_t sstride = (int64_t)kRows * kPartStride;
+    float M = -INFINITY;
+    for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, base[sp * sstride + kD]);
+    M = wave_max(M);
+    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = 0; s0 < nsp; s0 += 64) {
+        const int sp = s0 + lane;
+        float w = 0.0f, lw = 0.0f;
+        if (sp < nsp) {
+            const float ms = base[sp * sstride + kD];
+            w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+            lw = w * base[sp * sstride + kD + 1];
         }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        const int mt = r / G, g = r % G;
-        uint16_t* op = (uint16_t*)a.out + (int64_t)b * a.o_sB + (int64_t)mt * a.o_sM +
-                       (int64_t)(hk * G + g) * a.o_sH + d0;
-        const uint32_t w0 = f32_to_bf16_bits(o0 * inv) | ((uint32_t)f32_to_bf16_bits(o1 * inv) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(o2 * inv) | ((uint32_t)f32_to_bf16_bits(o3 * inv) << 16);
-        *(uint2*)op = make_uint2(w0, w1);
+        const int n = min(64, nsp - s0);
+        for (int j = 0; j < n; ++j) {
+            const float wj = __shfl(w, j);
+            L = L + __shfl(lw, j);
+            const float2 o = *(const float2*)(base + (s0 + j) * sstride + 2 * lane);
+            o0 = o0 + wj * o.x;
+            o1 = o1 + wj * o.y;
+        }
     }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int mt = r / G, g = r % G;
+    uint16_t* op = (uint16_t*)a.out + (int64_t)b * a.o_sB + (int64_t)mt * a.o_sM +
+                   (int64_t)(hk * G + g) * a.o_sH + 2 * lane;
+    *(uint32_t*)op = f32_to_bf16_bits(o0 * inv) | ((uint32_t)f32_to_bf16_bits(o1 * inv) << 16);
 }
 
 }  // namespace
@@ -313,7 +325,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid(a.num_splits, a.B * a.Hkv);
     k_paged_decode<<<grid, kThreads, 0, stream>>>(a, alpha);
-    k_decode_merge<<<a.B * a.Hkv, kThreads, 0, stream>>>(a);
+    const int rows = a.B * a.Hkv * kRows;
+    k_decode_merge<<<(rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock, 64 * kMergeRowsPerBlock, 0,
+                     stream>>>(a);
     return hipGetLastError();
 }
 
