@@ -194,7 +194,7 @@ def cpu_baseline(wname, target_s=15.0):
         ri = np.sort(rng.integers(0, w.Lq, nrows))
         rows = np.stack([np.zeros_like(ri), np.zeros_like(ri), ri], 1)
         t0 = time.perf_counter()
-        oracle.prefill_int8_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale, BN=128,
+        oracle.prefill_int8_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale, BN=64,
                                      rows=rows, nthreads=cores)
         return time.perf_counter() - t0
 

@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define SAGE_VERSION_MAJOR 0
-#define SAGE_VERSION_MINOR 1
+#define SAGE_VERSION_MINOR 2
 #define SAGE_PAD(L) ((((L) + 127) / 128) * 128)
 
 typedef enum {
@@ -154,8 +154,9 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
-/* Quantized attention forward.  For each query row, KV tiles of 128 keys in
- * ascending order: S = QK^T on INT8 (or scaled MXFP4) MFMA with int32 (fp32)
+/* Quantized attention forward.  For each query row, KV tiles of
+ * sage_attn_kv_tile() keys in ascending order (the online-softmax block size,
+ * so part of the numeric result): S = QK^T on INT8 (or scaled MXFP4) MFMA with int32 (fp32)
  * accumulation; x = S * q_scale * k_scale * sm_scale * log2(e); online
  * softmax with fp32 running max m and row sum l (l summed from the fp32
  * probabilities, before conversion); P = e4m3(448 p), with 448 p evaluated as
@@ -184,6 +185,9 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale,
                           const sage_tensor* v_q, const sage_tensor* v_scale,
                           const sage_attn_params* params, const sage_tensor* out,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keys per KV tile of sage_attn_fwd's online softmax (64). */
+int32_t sage_attn_kv_tile(void);
 
 /* ------------------------------------------------------------------------- */
 /* Paged decode over an FP8 e4m3 KV cache ([aiter #7388]).

@@ -212,6 +212,8 @@ const char* sage_last_error(void) { return g_err; }
 
 int32_t sage_version(void) { return (SAGE_VERSION_MAJOR << 16) | SAGE_VERSION_MINOR; }
 
+int32_t sage_attn_kv_tile(void) { return sage::kKvTile; }
+
 int32_t sage_decode_num_splits(int32_t window, int32_t mtp, int32_t max_ctx) {
     const int tile = sage::kDecodeTile;
     if (max_ctx <= 0) return 0;

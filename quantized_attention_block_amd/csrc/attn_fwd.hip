@@ -17,10 +17,18 @@
 // gfx950 design:
 //  - Block = 4 waves = 128 query rows (one Q scale block); each wave owns 32
 //    query rows for the whole KV loop (Q fragments stay in VGPRs).
-//  - KV tiles of 128 keys are staged through LDS with a two-stage double
-//    buffer (global -> VGPR prefetch of tile j+1 overlaps the math of tile j;
-//    one barrier per tile).  16-byte chunks are XOR-swizzled per row so the
-//    MFMA operand reads do not collide on LDS banks.
+//  - KV tiles of 64 keys are copied global -> LDS with 16-byte
+//    buffer_load ... lds instructions (no staging registers) into a ring of
+//    five LDS stages, two steps ahead of use; one barrier per tile.  16-byte
+//    chunks are XOR-swizzled per row so the MFMA operand reads do not
+//    collide on LDS banks.
+//  - Software pipeline per wave: step j issues the PV MFMAs of tile j-1 and
+//    the QK MFMAs of tile j+1 in the same basic block as the softmax VALU
+//    work (row max, convert, exp2, FP8 pack) of tile j, so the matrix cores
+//    run while the vector ALUs work.  O's rescale for tile j's new row max is
+//    applied at the top of step j+1, before PV(j) joins O.  Stage use in
+//    step j: K of j+1 and V of j-1 are read, V of j waits for the next step,
+//    j+2 and j+3 are landing.
 //  - The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_i32_32x32x32_i8: each lane then holds one query and, per 32-key
 //    sub-tile, 16 consecutive keys (K rows are fed to the A operand in a
@@ -28,7 +36,9 @@
 //    B operand of the PV product O^T = V^T P^T (v_mfma_f32_32x32x64 e4m3), so
 //    P never leaves registers, and V^T (stored transposed, keys contiguous)
 //    is read in natural key order, two 16-byte LDS reads per operand.
-//  - Row max is taken on the int32 scores (rounding is monotone, so
+//  - INT8 scores leave the MFMA biased by 1.5 * 2^23 (the accumulator starts
+//    at that float's bit pattern), so fp32(S) is one exact subtraction.  Row
+//    max is taken on the integer scores (rounding is monotone, so
 //    max fp32(S c) = fp32(max S c)); the O/l rescale is skipped when no row of
 //    the wave changed its max; 448 is folded into the exp2 offset.
 #include "sage_device.hpp"
@@ -39,21 +49,26 @@
 namespace sage {
 namespace {
 
-constexpr int kBM = 128;     // query rows per block
-constexpr int kBN = kKvTile; // keys per KV tile
+constexpr int kBM = 128;            // query rows per block
+constexpr int kBN = kKvTile;        // keys per KV tile
+constexpr int kNT = kBN / 32;       // 32-key sub-tiles per tile
+constexpr int kStages = 5;          // LDS ring depth: tiles j-1 .. j+3 in step j
 constexpr int kThreads = 256;
 constexpr float kLog2Fp8Max = 8.807354922057604f;   // log2(448)
+static_assert(kBN == 64, "the PV operand packing assumes 64-key tiles");
 
-// Element size of one K row in bytes: INT8 codes D, packed E2M1 codes D/2.
+// Byte geometry of one LDS stage: K codes (INT8: D bytes per key, E2M1: D/2),
+// the E8M0 scales of K (MXFP4 only), then V^T codes (D rows of kBN keys).
 template <int D, bool MX>
 struct Geo {
     static constexpr int kRowBytes = MX ? D / 2 : D;       // K / Q row bytes
     static constexpr int kRowChunks = kRowBytes / 16;      // 16-byte chunks per row
     static constexpr int kKBytes = kBN * kRowBytes;
     static constexpr int kKScaleBytes = MX ? kBN * (D / 32) : 0;
+    static constexpr int kVOff = kKBytes + kKScaleBytes;
     static constexpr int kVBytes = D * kBN;
-    static constexpr int kStageBytes = kKBytes + kKScaleBytes + kVBytes;
-    static constexpr int kVChunksPerRow = kBN / 16;        // 8
+    static constexpr int kStageBytes = kVOff + kVBytes;
+    static constexpr int kVRowChunks = kBN / 16;           // 4
 };
 
 // A-operand row r of a 32-key sub-tile holds key kappa(r); with this order
@@ -75,15 +90,17 @@ __device__ __forceinline__ int k_swz(int r) {
         return ((r >> 2) & 1) | ((r >> 3) & 2);
 }
 
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+// V^T rows are 64 bytes (4 chunks): 4 channels share one bank sweep.
+__device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
 
 template <int D, bool MX>
 __device__ __forceinline__ uint8_t* k_lds_addr(uint8_t* base, int r, int c) {
     using G = Geo<D, MX>;
     return base + r * G::kRowBytes + 16 * (c ^ k_swz<D, MX>(r));
 }
-__device__ __forceinline__ uint8_t* v_lds_addr(uint8_t* vbase, int d, int c) {
-    return vbase + d * kBN + 16 * (c ^ v_swz(d));
+template <int D, bool MX>
+__device__ __forceinline__ uint8_t* v_lds_addr(uint8_t* stage, int d, int c) {
+    return stage + Geo<D, MX>::kVOff + d * kBN + 16 * (c ^ v_swz(d));
 }
 
 // One KV tile (K codes, K E8M0 scales for MXFP4, V^T codes) is copied from
@@ -128,13 +145,13 @@ struct TileDma {
                                                          kt * G::kKScaleBytes, 0, 0);
         }
         if (!with_v) return;
-        uint8_t* vstage = stage + G::kKBytes + G::kKScaleBytes;
+        uint8_t* vstage = stage + G::kVOff;
 #pragma unroll
         for (int j = 0; j < kVRegions / NWAVES; ++j) {
             const int region = j * NWAVES + wave;
             const int p = region * 64 + lane;
-            const int d = p / G::kVChunksPerRow;
-            const int c = (p % G::kVChunksPerRow) ^ v_swz(d);
+            const int d = p / G::kVRowChunks;
+            const int c = (p % G::kVRowChunks) ^ v_swz(d);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vstage + region * 1024, 16, d * Lkp + 16 * c,
                                                      kt * kBN, 0, 0);
         }
@@ -152,6 +169,20 @@ __device__ __forceinline__ void wait_dma() {
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's LDS DMA has landed
 }
 
+// Workgroup barrier after this wave's LDS DMA of all but its last N loads has
+// landed (loads complete in issue order) and its LDS reads and writes are
+// done.  __syncthreads() would also wait for every load in flight, including
+// the DMA of tiles that are not needed yet.  The empty asm statements keep
+// the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void dma_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | N);   // vmcnt(N) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Q fragment of one wave: query row (l % 32) of the wave's 32 rows.
 // INT8: 16-byte chunk (2 c + half) for c < D/32.  MXFP4: chunk (2 c + half)
 // for c < D/64 plus the E8M0 byte of MX block (2 c + half).
@@ -162,19 +193,42 @@ struct QFrag {
     int s[MX ? kN : 1];
 };
 
-// The QK step of one 32-key sub-tile t of the staged tile.  Shared by the
-// attention kernel and the debug tile kernel.
+// INT8 scores are accumulated on top of the bit pattern of 1.5 * 2^23: the
+// int32 result, read as a float, is then exactly 1.5 * 2^23 + S (floats in
+// [2^23, 2^24) are the integers, and |S| <= D * 127^2 < 2^22 for D <= 256),
+// so one subtraction yields fp32(S) exactly, cheaper than v_cvt_f32_i32.
+// Integer comparison of biased scores orders them like S.
+constexpr int kSBias = 0x4B400000;
+constexpr float kSBiasF = 12582912.0f;   // 1.5 * 2^23
+__device__ __forceinline__ float score_f(int biased) { return __int_as_float(biased) - kSBiasF; }
+__device__ __forceinline__ float score_f(float s) { return s; }
+
+// Sixteen copies of the bias, kept in registers across the KV loop as the
+// first MFMA's accumulator input (an opaque value, so the compiler does not
+// re-materialize the literal into every accumulator).
+__device__ __forceinline__ v16i score_bias() {
+    v16i b;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) b[e] = kSBias;
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
+// The QK step of one 32-key sub-tile t of a staged tile (biased int32
+// scores; bias = score_bias()).  Shared by the attention kernel and the debug
+// tile kernel.
 template <int D>
 __device__ __forceinline__ v16i qk_subtile_i8(uint8_t* stage, const QFrag<D, false>& q, int t,
-                                              int lane) {
+                                              int lane, const v16i& bias) {
+    static_assert(D <= 256, "biased INT8 scores need |S| < 2^22");
     const int half = lane >> 5;
     const int r = 32 * t + kappa(lane & 31);
-    v16i acc = {0};
+    v4i kf[D / 32];
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-        const v4i a = *(const v4i*)k_lds_addr<D, false>(stage, r, 2 * c + half);
-        acc = mfma_i8_32x32x32(a, q.f[c], acc);
-    }
+    for (int c = 0; c < D / 32; ++c) kf[c] = *(const v4i*)k_lds_addr<D, false>(stage, r, 2 * c + half);
+    v16i acc = mfma_i8_32x32x32(kf[0], q.f[0], bias);
+#pragma unroll
+    for (int c = 1; c < D / 32; ++c) acc = mfma_i8_32x32x32(kf[c], q.f[c], acc);
     return acc;
 }
 
@@ -185,47 +239,52 @@ __device__ __forceinline__ v16f qk_subtile_mx(uint8_t* stage, const QFrag<D, tru
     const int half = lane >> 5;
     const int r = 32 * t + kappa(lane & 31);
     const uint8_t* ks = stage + G::kKBytes;
+    v4i kf[D / 64];
+    int sa[D / 64];
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        kf[c] = *(const v4i*)k_lds_addr<D, true>(stage, r, 2 * c + half);
+        sa[c] = ks[r * (D / 32) + 2 * c + half];
+    }
     v16f acc = {0};
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
-        const v4i a4 = *(const v4i*)k_lds_addr<D, true>(stage, r, 2 * c + half);
         // fp4 operands occupy the low four dwords; the upper four are not read
-        const v8i a = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+        const v8i a = __builtin_shufflevector(kf[c], kf[c], 0, 1, 2, 3, -1, -1, -1, -1);
         const v8i b = __builtin_shufflevector(q.f[c], q.f[c], 0, 1, 2, 3, -1, -1, -1, -1);
-        const int sa = ks[r * (D / 32) + 2 * c + half];
-        acc = mfma_f4_32x32x64(a, b, acc, sa, q.s[c]);
+        acc = mfma_f4_32x32x64(a, b, acc, sa[c], q.s[c]);
     }
     return acc;
 }
 
-// QK of the four 32-key sub-tiles of a staged tile, with the K fragments of
-// sub-tile t+1 read from LDS before the MFMAs of sub-tile t.
-template <int D, bool MX, class SAcc>
-__device__ __forceinline__ void qk_tile(uint8_t* stage, const QFrag<D, MX>& q, int lane, SAcc* S) {
-    if constexpr (MX) {
+template <int D, bool MX>
+using SAccT = typename std::conditional<MX, v16f, v16i>::type;
+
+template <int D, bool MX>
+__device__ __forceinline__ SAccT<D, MX> qk_subtile(uint8_t* stage, const QFrag<D, MX>& q, int t,
+                                                   int lane, const v16i& bias) {
+    if constexpr (MX)
+        return qk_subtile_mx<D>(stage, q, t, lane);
+    else
+        return qk_subtile_i8<D>(stage, q, t, lane, bias);
+}
+
+// O^T += V^T P^T for one staged 64-key tile.  A operand: V^T row (channel
+// 32 db + lane % 32), keys [16 half, +16) and [32 + 16 half, +16); B: the
+// packed P of the tile (byte 16 t + e of lane l = key 32 t + 16 (l / 32) + e).
+template <int D, bool MX>
+__device__ __forceinline__ void pv_tile(uint8_t* stage, const v8i& pf, int lane, v16f* O) {
+    const int half = lane >> 5, col = lane & 31;
+    v8i av[D / 32];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[t] = qk_subtile_mx<D>(stage, q, t, lane);
-    } else {
-        constexpr int NC = D / 32;
-        const int half = lane >> 5, col = lane & 31;
-        v4i kf[2][NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            kf[0][c] = *(const v4i*)k_lds_addr<D, false>(stage, kappa(col), 2 * c + half);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t + 1 < 4) {
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    kf[(t + 1) & 1][c] = *(const v4i*)k_lds_addr<D, false>(
-                        stage, 32 * (t + 1) + kappa(col), 2 * c + half);
-            }
-            v16i acc = {0};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) acc = mfma_i8_32x32x32(kf[t & 1][c], q.f[c], acc);
-            S[t] = acc;
-        }
+    for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + col;
+        const v4i lo = *(const v4i*)v_lds_addr<D, MX>(stage, d, half);
+        const v4i hi = *(const v4i*)v_lds_addr<D, MX>(stage, d, 2 + half);
+        av[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) O[db] = mfma_f8_32x32x64(av[db], pf, O[db]);
 }
 
 template <int D, bool MX>
@@ -242,12 +301,33 @@ __device__ __forceinline__ void load_qfrag(QFrag<D, MX>& q, const uint8_t* qbase
     }
 }
 
+// Instruction order of the full-tile loop body for the machine scheduler:
+// the LDS reads of the first QK operands and the row max first, then each
+// MFMA (QK of the next tile, PV of the previous one) followed by one or two
+// LDS operand reads and a slice of the softmax VALU work, so the matrix core
+// and the vector ALU run side by side within one wave.
+template <int D, bool MX>
+__device__ __forceinline__ void interleave() {
+    constexpr int kMfma = (MX ? 2 * (D / 64) : 2 * (D / 32)) + D / 32;   // QK + PV
+    constexpr int kReads = 2 * (MX ? D / 64 : D / 32) + 2 * (D / 32);   // b128 operand reads
+    constexpr int kLead = (MX ? D / 64 : D / 32) + 2;                    // issued before the first MFMA
+    constexpr int kValu = MX ? 10 : 16;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);    // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);       // VALU
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        if (kLead + i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    }
+}
+
 template <int D, bool MX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_fwd(AttnArgs a, float alpha) {
     using G = Geo<D, MX>;
-    constexpr int kNT = 4;              // 32-key sub-tiles per tile
+    using SAcc = SAccT<D, MX>;
     constexpr int kDB = D / 32;         // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * G::kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * G::kStageBytes];
 
     const int Lqp = pad128(a.Lq), Lkp = pad128(a.Lk);
     const int nqb = Lqp / kBM;
@@ -277,168 +357,210 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t* ksc = MX ? (const uint8_t*)a.k_scale + (int64_t)bhk * Lkp * (D / 32) : nullptr;
     const uint8_t* vbase = a.v + (int64_t)bhk * D * Lkp;
 
-    // Number of KV tiles this block visits.
-    int ntiles = Lkp / kBN;
+    // KV tiles this block visits (causal: up to its last query row).  Tiles
+    // past the real keys of the padded length are never visited.
+    int ntiles = (a.Lk + kBN - 1) / kBN;
     if (a.causal) ntiles = min(ntiles, (qb * kBM + kBM - 1) / kBN + 1);
-
-    QFrag<D, MX> qf;
-    load_qfrag<D, MX>(qf, qbase, qsc, qrow, lane);
-    float q_s = 0.0f;
-    if constexpr (!MX) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
-    const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
 
     using Dma = TileDma<D, MX, 4>;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)Lkp * G::kRowBytes);
     const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(MX ? ksc : kbase, MX ? (int64_t)Lkp * (D / 32) : 16);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (int64_t)D * Lkp);
-    Dma::issue(smem, krs, ksrs, vrs, Lkp, 0, wave, lane);
-    // INT8: the two 64-key block scales of the next tile, folded with q_scale
-    // and alpha (c = fp32(fp32(q_s k_s) alpha)); prefetched one tile ahead.
-    const int kb_per_tile = MX ? 0 : kBN / a.k_block;
-    float ksn[2] = {0.0f, 0.0f};
-    if constexpr (!MX) {
-        ksn[0] = kscale_f[0];
-        ksn[1] = kscale_f[kb_per_tile - 1];
+    auto stage_of = [&](int kt) { return smem + (kt % kStages) * G::kStageBytes; };
+    // DMA instructions one tile costs every wave (wave 0 of MXFP4 issues one
+    // more, for the K scales; counting without it only waits longer)
+    constexpr int kDma = Dma::kKRegions / 4 + Dma::kVRegions / 4;
+
+    // tiles 0, 1 and 2 in flight before the loop; tile j + 3 is issued in
+    // step j, two steps before its K is read
+    Dma::issue(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane);
+    if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
+    if (ntiles > 2) Dma::issue(stage_of(2), krs, ksrs, vrs, Lkp, 2, wave, lane);
+
+    QFrag<D, MX> qf;
+    load_qfrag<D, MX>(qf, qbase, qsc, qrow, lane);
+    // Score scale of tile kt: c = fp32(fp32(q_s k_s) alpha) for INT8 (a 64-key
+    // tile lies inside one K scale block), alpha for MXFP4.
+    float q_s = 0.0f;
+    if constexpr (!MX) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
+    const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
+    // (read through the constant address space: a scalar load, which does not
+    // queue behind the LDS DMA in the vector memory counter)
+    const __attribute__((address_space(4))) float* kscale_c =
+        (const __attribute__((address_space(4))) float*)kscale_f;
+    auto tile_c = [&](int kt) -> float {
+        if constexpr (MX) return alpha;
+        else return (q_s * kscale_c[kt * kBN / a.k_block]) * alpha;
+    };
+
+    // PV(j - 1) at j = 0 multiplies P = 0 with the V region of the last
+    // stage; zero it so that stale LDS bytes (which may be e4m3 NaN codes)
+    // add exactly 0.
+    {
+        uint8_t* vz = stage_of(kStages - 1) + G::kVOff;
+        for (int i = tid; i < G::kVBytes / 16; i += kThreads) *(v4i*)(vz + 16 * i) = v4i{0, 0, 0, 0};
     }
+    if (ntiles > 2)
+        dma_barrier<2 * kDma>();   // tile 0 has landed (tiles 1, 2 may be in flight)
+    else if (ntiles > 1)
+        dma_barrier<kDma>();
+    else
+        dma_barrier<0>();
+
+    // Scores of the current tile and P of the previous one live in one of two
+    // register sets (A, B) that swap roles every iteration (no copies).
+    const v16i sbias = MX ? v16i{0} : score_bias();
+    SAcc SA[kNT], SB[kNT];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) SA[t] = qk_subtile<D, MX>(stage_of(0), qf, t, lane, sbias);
+    float c_cur = tile_c(0);
 
     v16f O[kDB];
 #pragma unroll
     for (int i = 0; i < kDB; ++i) O[i] = v16f{0};
     float m = -INFINITY, l = 0.0f;
+    v8i PA = {0, 0, 0, 0, 0, 0, 0, 0}, PB;
+    // O's rescale for a new row max is applied one iteration late, just
+    // before the next PV product joins O, when no MFMA writing O is in flight.
+    float sc_pend = 1.0f;
+    int pend = 0;
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        uint8_t* stage = smem + (kt & 1) * G::kStageBytes;
-        wait_dma();
-        __syncthreads();
-        float ksc_t[2] = {ksn[0], ksn[1]};
-        if (kt + 1 < ntiles) {
-            Dma::issue(smem + ((kt + 1) & 1) * G::kStageBytes, krs, ksrs, vrs, Lkp, kt + 1, wave, lane);
-            if constexpr (!MX) {
-                ksn[0] = kscale_f[(kt + 1) * kb_per_tile];
-                ksn[1] = kscale_f[(kt + 1) * kb_per_tile + kb_per_tile - 1];
+    // One pipeline step: S holds the scores of tile j, P the packed P of tile
+    // j-1; on return Sn holds the scores of tile j+1 and Pn the P of tile j.
+    // FULL steps (no key of tile j masked for any row of the block) are one
+    // basic block; the others mask per 32-key sub-tile, which is wave-uniformly
+    // empty, crossing (keys tested one by one) or full for this wave's rows.
+    auto step = [&](int j, SAcc* S, SAcc* Sn, const v8i& P, v8i& Pn, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        // every wave's part of tile j+1 has landed (tile j+2 may be in flight)
+        // and all waves finished step j-1
+        if (j + 2 < ntiles)
+            dma_barrier<kDma>();
+        else
+            dma_barrier<0>();
+        if (j + 3 < ntiles) Dma::issue(stage_of(j + 3), krs, ksrs, vrs, Lkp, j + 3, wave, lane);
+        const float c_nxt = (j + 1 < ntiles) ? tile_c(j + 1) : 0.0f;
+        if (pend) {
+#pragma unroll
+            for (int i = 0; i < kDB; ++i) O[i] *= sc_pend;
+        }
+        const int key0 = j * kBN;
+        // K of tile j+1 (past the last tile: a stale stage, result unused) and
+        // V of tile j-1 (stage of tile j + kStages - 1 = j - 1 modulo kStages)
+        uint8_t* st_k = stage_of(j + 1);
+        uint8_t* st_v = stage_of(j + kStages - 1);
+
+        int st[kNT];   // 0 empty, 1 crossing, 2 full
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            if constexpr (FULL) {
+                st[t] = 2;
+            } else {
+                const int lo = key0 + 32 * t, hi = lo + 31;
+                const bool empty = lo >= a.Lk || (a.causal && lo > q0w + 31);
+                const bool whole = hi < a.Lk && (!a.causal || hi <= q0w);
+                st[t] = empty ? 0 : (whole ? 2 : 1);
             }
         }
-
-        const int key0 = kt * kBN;
-        // waves whose every key of this tile is causally masked skip it
-        if (a.causal && key0 > q0w + 31) continue;
-        const bool full = (key0 + kBN <= a.Lk) && (!a.causal || key0 + kBN - 1 <= q0w);
-
-        // S holds int32 (INT8) or fp32 (MXFP4) scores of the 4 sub-tiles;
-        // element (t, e) is key key0 + 32 t + 16 half + e of query qrow.
-        using SAcc = typename std::conditional<MX, v16f, v16i>::type;
-        float c[kNT];
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) c[t] = MX ? alpha : (q_s * ksc_t[t < 2 ? 0 : 1]) * alpha;
-
-        // The tile body, instantiated once for full tiles and once for tiles
-        // that cross the causal diagonal or the ragged end.  In the latter,
-        // each 32-key sub-tile is (wave-uniformly) empty, crossing or full for
-        // this wave's 32 rows: empty sub-tiles skip their MFMAs and exps and
-        // only crossing ones test keys one by one.
-        auto tile_body = [&](auto full_tag) {
-            constexpr bool FULL = decltype(full_tag)::value;
-            int st[kNT];   // 0 empty, 1 crossing, 2 full
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) {
-                if constexpr (FULL) {
-                    st[t] = 2;
-                } else {
-                    const int lo = key0 + 32 * t, hi = lo + 31;
-                    const bool empty = lo >= a.Lk || (a.causal && lo > q0w + 31);
-                    const bool whole = hi < a.Lk && (!a.causal || hi <= q0w);
-                    st[t] = empty ? 0 : (whole ? 2 : 1);
-                }
-            }
-            auto visible = [&](int t, int e) {
-                const int key = key0 + 32 * t + 16 * half + e;
-                return key < a.Lk && (!a.causal || key <= qrow);
-            };
-            SAcc S[kNT];
-            if constexpr (FULL) {
-                qk_tile<D, MX>(stage, qf, lane, S);
-            } else {
-#pragma unroll
-                for (int t = 0; t < kNT; ++t) {
-                    if (st[t] == 0) continue;
-                    if constexpr (MX)
-                        S[t] = qk_subtile_mx<D>(stage, qf, t, lane);
-                    else
-                        S[t] = qk_subtile_i8<D>(stage, qf, t, lane);
-                }
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) {
-                if (st[t] == 2) {
-                    auto mx = S[t][0];
-#pragma unroll
-                    for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
-                    tmax = fmaxf(tmax, (float)mx * c[t]);   // rounding is monotone
-                } else if (st[t] == 1) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        tmax = fmaxf(tmax, visible(t, e) ? (float)S[t][e] * c[t] : -INFINITY);
-                }
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-
-            // ---- online softmax update -------------------------------------
-            const float m_new = fmaxf(m, tmax);
-            if (__any(m_new > m)) {
-                const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-                l *= sc;
-#pragma unroll
-                for (int i = 0; i < kDB; ++i) O[i] *= sc;
-            }
-            m = m_new;
-            const float mb = (m_new == -INFINITY ? 0.0f : m_new) - kLog2Fp8Max;
-
-            // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
-            // accumulates q (so l = 448 * sum p).  Packed into the PV B operand:
-            // byte 16 t' + e of group u is key 64 u + 32 t' + 16 half + e; the PV
-            // MFMAs of group u follow its conversion so they overlap group u+1's.
-            uint8_t* vb = stage + G::kKBytes + G::kKScaleBytes;
-            float ls = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (st[2 * u] == 0 && st[2 * u + 1] == 0) continue;
-                v8i pf;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const int t = 2 * u + w / 4, e0 = 4 * (w % 4);
-                    if (st[t] == 0) {
-                        pf[w] = 0;
-                        continue;
-                    }
-                    float p[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float xv = __builtin_fmaf((float)S[t][e0 + j], c[t], -mb);
-                        if (st[t] == 1 && !visible(t, e0 + j)) xv = -INFINITY;
-                        p[j] = __builtin_amdgcn_exp2f(xv);
-                    }
-                    ls += (p[0] + p[1]) + (p[2] + p[3]);
-                    uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], 0);
-                    pk = cvt_pk_fp8<true>(p[2], p[3], pk);
-                    pf[w] = (int)pk;
-                }
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) {
-                    const int d = 32 * db + col;
-                    const v4i lo = *(const v4i*)v_lds_addr(vb, d, 4 * u + half);
-                    const v4i hi = *(const v4i*)v_lds_addr(vb, d, 4 * u + 2 + half);
-                    const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    O[db] = mfma_f8_32x32x64(av, pf, O[db]);
-                }
-            }
-            l += ls;
+        auto visible = [&](int t, int e) {
+            const int key = key0 + 32 * t + 16 * half + e;
+            return key < a.Lk && (!a.causal || key <= qrow);
         };
-        if (full)
-            tile_body(std::true_type{});
-        else
-            tile_body(std::false_type{});
+
+        // PV of tile j-1 first (its operands are ready; O was rescaled above),
+        // alongside the row max of tile j
+        pv_tile<D, MX>(st_v, P, lane, O);
+
+        // row max of tile j
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            if (st[t] == 2) {
+                auto mx = S[t][0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
+                tmax = fmaxf(tmax, score_f(mx) * c_cur);   // rounding is monotone
+            } else if (st[t] == 1) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c_cur : -INFINITY);
+            }
+        }
+        const float m_new = fmaxf(m, half_pair_max(tmax));
+        const float mb = (FULL || m_new != -INFINITY ? m_new : 0.0f) - kLog2Fp8Max;
+
+        // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448)));
+        // l accumulates q (so l = 448 * sum p).  Packed as the PV B operand.
+        float ls = 0.0f;
+        auto pack = [&](int t) {
+#pragma unroll
+            for (int w = 4 * t; w < 4 * t + 4; ++w) {
+                const int e0 = 4 * (w % 4);
+                if (st[t] == 0) {
+                    Pn[w] = 0;
+                    continue;
+                }
+                float p[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float xv = __builtin_fmaf(score_f(S[t][e0 + jj]), c_cur, -mb);
+                    if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
+                    p[jj] = __builtin_amdgcn_exp2f(xv);
+                }
+                ls += (p[0] + p[1]) + (p[2] + p[3]);
+                uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], 0);
+                pk = cvt_pk_fp8<true>(p[2], p[3], pk);
+                Pn[w] = (int)pk;
+            }
+        };
+
+        // QK of tile j+1 around the exps of tile j
+        Sn[0] = qk_subtile<D, MX>(st_k, qf, 0, lane, sbias);
+        pack(0);
+        Sn[1] = qk_subtile<D, MX>(st_k, qf, 1, lane, sbias);
+        pack(1);
+
+        const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+        l = l * sc + ls;
+        pend = __any(m_new > m);
+        sc_pend = sc;
+        m = m_new;
+        c_cur = c_nxt;
+        // Pin the softmax results to this step's block: otherwise they are sunk
+        // past the next step's rescale branch, away from the MFMAs they overlap.
+        asm volatile("" ::"v"(Pn), "v"(l));
+    };
+
+    // Tiles [0, n_full) are full for every wave of the block.
+    int n_full = a.Lk / kBN;
+    if (a.causal) n_full = min(n_full, qb * (kBM / kBN));
+    n_full = min(n_full, ntiles);
+    int j = 0;
+    for (; j + 2 <= n_full; j += 2) {
+        step(j, SA, SB, PA, PB, std::true_type{});
+        step(j + 1, SB, SA, PB, PA, std::true_type{});
     }
+    auto rotate = [&]() {
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) SA[t] = SB[t];
+        PA = PB;
+    };
+    if (j < n_full) {
+        step(j, SA, SB, PA, PB, std::true_type{});
+        rotate();
+        ++j;
+    }
+    for (; j < ntiles; ++j) {
+        step(j, SA, SB, PA, PB, std::false_type{});
+        rotate();
+    }
+    // PV of the last tile (its stage is not overwritten: no DMA was issued
+    // after the last tile), after the last pending rescale
+    if (pend) {
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) O[i] *= sc_pend;
+    }
+    pv_tile<D, MX>(stage_of(ntiles - 1), PA, lane, O);
 
     // ---- epilogue: out = (O * v_scale) / l (times the reciprocal of l), written
     // with the caller's strides
@@ -454,23 +576,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int d0 = 32 * db + 8 * i + 4 * half;
                 float o[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[j] = (O[db][4 * i + j] * vs[d0 + j]) * inv_l;
+                for (int jj = 0; jj < 4; ++jj)
+                    o[jj] = (O[db][4 * i + jj] * vs[d0 + jj]) * inv_l;
                 if (a.out.dtype == kOutF32) {
                     *(float4*)((float*)a.out.ptr + ooff + d0) = make_float4(o[0], o[1], o[2], o[3]);
                 } else {
                     uint32_t w[2];
 #pragma unroll
-                    for (int j = 0; j < 4; j += 2) {
+                    for (int jj = 0; jj < 4; jj += 2) {
                         uint32_t h0, h1;
                         if (a.out.dtype == kOutBF16) {
-                            h0 = __builtin_bit_cast(uint16_t, (__bf16)o[j]);
-                            h1 = __builtin_bit_cast(uint16_t, (__bf16)o[j + 1]);
+                            h0 = __builtin_bit_cast(uint16_t, (__bf16)o[jj]);
+                            h1 = __builtin_bit_cast(uint16_t, (__bf16)o[jj + 1]);
                         } else {
-                            h0 = __builtin_bit_cast(uint16_t, (_Float16)o[j]);
-                            h1 = __builtin_bit_cast(uint16_t, (_Float16)o[j + 1]);
+                            h0 = __builtin_bit_cast(uint16_t, (_Float16)o[jj]);
+                            h1 = __builtin_bit_cast(uint16_t, (_Float16)o[jj + 1]);
                         }
-                        w[j / 2] = h0 | (h1 << 16);
+                        w[jj / 2] = h0 | (h1 << 16);
                     }
                     *(uint2*)((uint16_t*)a.out.ptr + ooff + d0) = make_uint2(w[0], w[1]);
                 }
@@ -479,7 +601,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // Test hook: int32 S = Q8 K8^T through the same staging and qk_subtile_i8 as
-// the attention kernel.  One wave per (32 queries, 128 keys, b*h).
+// the attention kernel.  One wave per (32 queries, one KV tile of keys, b*h).
 template <int D>
 __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* k, int Lqp, int Lkp,
                                                  int q0, int k0, int nq, int nk, int32_t* out) {
@@ -489,7 +611,7 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* 
     const int qg = blockIdx.x, kg = blockIdx.y, bh = blockIdx.z;
     const uint8_t* qbase = (const uint8_t*)q + (int64_t)bh * Lqp * D;
     const uint8_t* kbase = (const uint8_t*)k + (int64_t)bh * Lkp * D + (int64_t)k0 * D;
-    // stage K rows [k0 + 128 kg, +128); the V part of the stage is not used
+    // stage K rows [k0 + kBN kg, +kBN); the V part of the stage is not used
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)nk * D);
     TileDma<D, false, 1>::issue(stage, krs, krs, krs, 0, kg, 0, lane, false);
     wait_dma();
@@ -497,13 +619,13 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* 
     QFrag<D, false> qf;
     load_qfrag<D, false>(qf, qbase, nullptr, q0 + 32 * qg + col, lane);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const v16i s = qk_subtile_i8<D>(stage, qf, t, lane);
+    for (int t = 0; t < kNT; ++t) {
+        const v16i s = qk_subtile_i8<D>(stage, qf, t, lane, score_bias());
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int key = 128 * kg + 32 * t + 16 * half + e;   // relative to k0
+            const int key = kBN * kg + 32 * t + 16 * half + e;   // relative to k0
             const int qq = 32 * qg + col;                         // relative to q0
-            out[((int64_t)bh * nq + qq) * nk + key] = s[e];
+            out[((int64_t)bh * nq + qq) * nk + key] = s[e] - kSBias;
         }
     }
 }
@@ -527,7 +649,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_debug_qk(const int8_t* q, const int8_t* k, int B, int H, int Lqp, int Lkp,
                            int D, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t stream) {
-    dim3 grid(nq / 32, nk / 128, B * H);
+    dim3 grid(nq / 32, nk / kBN, B * H);
     if (D == 128)
         k_debug_qk<128><<<grid, 64, 0, stream>>>(q, k, Lqp, Lkp, q0, k0, nq, nk, out);
     else

@@ -98,6 +98,13 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 }
 
 // ---- wave reductions ------------------------------------------------------
+// Max of v over the lane pair (l % 32, l % 32 + 32): v_permlane32_swap hands
+// each lane both halves' values without an LDS round trip.
+__device__ __forceinline__ float half_pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

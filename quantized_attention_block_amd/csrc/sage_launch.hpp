@@ -24,7 +24,7 @@ struct OutView {
     int dtype;   // kOutF16 / kOutBF16 / kOutF32
 };
 
-constexpr int kKvTile = 128;       // KV tile of the attention kernel (and padding unit)
+constexpr int kKvTile = 64;        // KV tile of the attention kernel (online-softmax block)
 constexpr int kMeanChunk = 256;    // tokens per partial sum of the K mean
 constexpr int kDecodeTile = 256;   // decode split length (tokens)
 

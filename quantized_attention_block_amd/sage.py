@@ -81,6 +81,7 @@ def lib():
         st = ctypes.c_int
         L.sage_last_error.restype = ctypes.c_char_p
         L.sage_version.restype = ctypes.c_int32
+        L.sage_attn_kv_tile.restype = ctypes.c_int32
         L.sage_decode_num_splits.argtypes = [ctypes.c_int32] * 3
         L.sage_decode_num_splits.restype = ctypes.c_int32
         L.sage_quantize_qk_workspace_size.argtypes = [_T, _T, ctypes.POINTER(QkParams),
@@ -278,6 +279,11 @@ def sage_attention(q, k, v, *, causal=False, sm_scale=0.0, mode=QK_INT8, k_block
     v_q, v_s = sage_quantize_v(v)
     return sage_attn_fwd(qk, v_q, v_s, causal=causal, sm_scale=sm_scale, out=out,
                          out_dtype=q.dtype)
+
+
+def sage_attn_kv_tile() -> int:
+    """Keys per KV tile of sage_attn_fwd's online softmax."""
+    return int(lib().sage_attn_kv_tile())
 
 
 def sage_decode_num_splits(window: int, mtp: int, max_ctx: int) -> int:

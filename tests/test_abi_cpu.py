@@ -33,7 +33,13 @@ def test_exports_every_declared_symbol(S):
     assert len(names) >= 13
     for n in names:
         assert hasattr(S.lib(), n), n
-    assert S.lib().sage_version() == 1
+    assert S.lib().sage_version() == 2   # 0.2: adds sage_attn_kv_tile
+
+
+def test_attn_kv_tile_is_the_one_parity_tests_emulate(S):
+    # the oracle's online-softmax block in the attention parity tests, smoke and
+    # the CPU baseline is the fixed constant 64; the library must use the same
+    assert S.sage_attn_kv_tile() == 64
 
 
 def test_decode_split_plan_matches_page_and_oracle(S, orc):

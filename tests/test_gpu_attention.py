@@ -2,7 +2,7 @@
 
 * int32 QK score tiles of the attention kernel's own QK step are bit-exact
   against the oracle's integer product;
-* outputs match the quantization-emulating oracle (same 128-key tiles) to
+* outputs match the quantization-emulating oracle (same KV tiles) to
   cosine >= 0.999 and max-abs <= 1e-2 (fp32 outputs; bf16 outputs add half a
   bf16 ulp of the value for their own final rounding), and exact fp64
   attention to cosine >= 0.99 where the quantized method itself reaches it
@@ -22,7 +22,7 @@ from tests._util import canon, cosine, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-BN = 128   # KV tile of the kernel (part of the emulation's numeric definition)
+BN = 64   # KV tile of the kernel (part of the emulation's numeric definition)
 COS_EMUL, MAXABS_EMUL, COS_EXACT = 0.999, 1e-2, 0.99
 
 
