@@ -208,8 +208,10 @@ int32_t sage_attn_kv_tile(void);
  * MFMA; P is requantized per tile with the tile's largest per-token V scale.
  * D must be 128; the page size must be a multiple of 32 that divides 256 or
  * is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
- * below ctx_lens[b] must be valid page indices (device data is not checked),
- * and ctx_lens[b] <= params.max_ctx.
+ * below ctx_lens[b] must be valid page indices, and ctx_lens[b] <=
+ * params.max_ctx; device data is not validated, but a page id outside
+ * [0, P) reads page 0 and a length beyond the page table's coverage is
+ * clamped to it, so bad device data gives wrong numbers, never a fault.
  */
 typedef struct {
     float sm_scale;        /* <= 0: 1/sqrt(D)                  */

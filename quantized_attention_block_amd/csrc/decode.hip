@@ -15,33 +15,32 @@
 // with the tile's largest V scale as the conversion scale.
 //
 // gfx950 design: one block (4 waves) per (sequence, KV head, 256-token tile).
-// The 64 query rows of a KV head (MTP x query heads per KV head, padded) are
-// quantized once into LDS.  Wave w computes S^T for keys [64 w, 64 w + 64) of
-// the tile on v_mfma_f32_32x32x64 (e4m3 x e4m3), reading the K rows straight
-// from the paged cache into the A operand (each cache byte is read once per
-// block; the loads are issued first so that HBM latency overlaps the Q
-// quantization).  After a cross-wave max / sum through LDS, P (scaled by the
-// per-token V scale) is written to LDS as e4m3 and wave w computes O^T for
-// channels [32 w, 32 w + 32) over all 256 keys, with the transposed V cache
-// [page][Hkv][D][page_size] feeding the A operand directly.  Partials (m, l,
-// O) go to the workspace; a second kernel merges them.
+// The block copies the tile's K rows and V^T rows global -> LDS with 16-byte
+// buffer_load ... lds instructions whose buffer descriptor is the page (one
+// page per instruction), right after two scalar round trips (context length,
+// page ids), so the whole tile is in flight at once.  Wave w then owns query
+// rows [16 w, +16) of the KV head for the whole tile: S^T on
+// v_mfma_f32_16x16x128 (e4m3 x e4m3; the Q row is quantized in registers and
+// is the B operand), with K rows fed in an order that leaves each lane 32
+// consecutive keys of one query row per 128-key group, which is exactly the
+// B operand layout of the PV product O^T = V^T P^T.  Row max and sum need
+// only lane shuffles: no LDS round trip and one block barrier in total.
+// Partials (m, l, O) go to the workspace; a second kernel merges them.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
+
+#include <type_traits>
 
 namespace sage {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;            // query rows per KV head (padded)
+constexpr int kRows = 64;            // query rows per KV head (padded): 16 per wave
 constexpr int kTile = kDecodeTile;   // 256 keys per split
 constexpr int kD = 128;
 constexpr int kPartStride = kD + 4;  // floats per partial row: O[D], m, l, pad
 
-__device__ __forceinline__ int kappa_dec(int r) {
-    return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-}
-
-// Keeps the first n (< 16) bytes of v, zeroes the rest.
+// Keeps the first n bytes of v (all for n >= 16, none for n <= 0), zeroes the rest.
 __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -57,226 +56,293 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// LDS K tile [256 keys][128 B]: chunk c of key k is stored at chunk
+// c ^ dk_swz(k).  One 16-lane read pass fetches keys {32 a + 4 m + b} (a, b in
+// 0..3) at one chunk; the XOR puts the 8 keys of each parity on 8 distinct
+// chunks, so the pass touches 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int dk_swz(int key) { return ((key >> 5) & 3) | (((key >> 1) & 1) << 2); }
+
+// LDS V^T tile [page-block][128 d][PW keys], PW = min(page, 256), n = PW / 16
+// chunks per row (n = 2^LGN): chunk c of row d is stored at c ^ dv_swz(d).
+// One read pass fetches 16 consecutive rows at one chunk; 16 / n rows share a
+// 256-byte bank sweep and the XOR separates the sweeps.
+template <int LGN>
+__device__ __forceinline__ int dv_swz(int d) { return (d >> (4 - LGN)) & ((1 << LGN) - 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* scalar_ptr(const T* p) {
+    return (const __attribute__((address_space(4))) T*)p;
+}
+
+// PW: keys per page-block, min(page, 256) (a page of at most 256 keys divides
+// 256; a larger page holds the whole tile at offset t0 % page).
+template <int PW>
 __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float alpha) {
+    constexpr int kNpb = kTile / PW;                 // page-blocks per tile
+    constexpr int kLgn = PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
     const int s = blockIdx.x, bk = blockIdx.y;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
-    const int ctx = a.ctx_lens[b];
+    // context lengths beyond what the page table covers are clamped to it
+    const int ctx = min(scalar_ptr(a.ctx_lens)[b], a.max_pages * a.page);
     if (ctx <= 0) return;
     const int G = a.Hq / a.Hkv, R = a.MTP * G;
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int T = lo_b / kTile + s;
     if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
-    const int t0 = T * kTile;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 31, half = lane >> 5;
-    const int32_t* ptab = a.page_table + (int64_t)b * a.pt_stride;
+    const int t0 = T * kTile, last = ctx - 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, q4 = lane >> 4;
 
-    __shared__ __attribute__((aligned(16))) uint8_t q8s[kRows][kD];
-    __shared__ __attribute__((aligned(16))) uint8_t p8s[kRows][kTile];
-    __shared__ float qss[kRows], kss[kTile], vss[kTile];
-    __shared__ float red_m[4][kRows], red_l[4][kRows], red_v[4];
+    __shared__ __attribute__((aligned(16))) uint8_t kt_s[kTile * kD];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_s[kTile * kD];
+    __shared__ __attribute__((aligned(16))) float kss[kTile], vss[kTile];
 
-    // ---- 1. issue the K loads of this wave's 64 keys (A operand rows) -----
-    // sub-tile t, row r = col: key 64 wave + 32 t + kappa(col); 32 bytes of
-    // D-slice [64 c + 32 half, +32) per (t, c).
-    uint4 kreg[2][2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int kpos = t0 + 64 * wave + 32 * t + kappa_dec(col);
-        const uint8_t* row = nullptr;
-        if (kpos < ctx) {
-            const int pg = ptab[kpos / a.page];
-            row = a.k_cache + (((int64_t)pg * a.Hkv + hk) * a.page + kpos % a.page) * kD;
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                kreg[t][c][j] = row ? *(const uint4*)(row + 64 * c + 32 * half + 16 * j)
-                                    : make_uint4(0, 0, 0, 0);
-    }
-    // ---- 2. issue the V^T loads of this wave's channels (A operand of PV)
-    // row d = 32 wave + col; keys [64 u + 32 half, +32) of the tile.
-    uint4 vreg[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int kpos = t0 + 64 * u + 32 * half;
-        const uint8_t* src = nullptr;
-        if (kpos < ctx) {
-            const int pg = ptab[kpos / a.page];
-            src = a.v_cache + (((int64_t)pg * a.Hkv + hk) * kD + 32 * wave + col) * a.page +
-                  kpos % a.page;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            vreg[u][j] = src ? *(const uint4*)(src + 16 * j) : make_uint4(0, 0, 0, 0);
-            // page slots at or beyond ctx may hold any bytes (e4m3 NaN codes
-            // included) and 0 * NaN would poison the product: zero them
-            const int nv = ctx - (kpos + 16 * j);
-            if (src && nv < 16) vreg[u][j] = keep_bytes(vreg[u][j], nv);
-        }
-    }
-    // ---- 3. per-token scales of the tile ----------------------------------
+    // ---- 1. this lane's Q slice: row r = 16 wave + c16, channels [32 q4, +32)
+    // (rows past R read row 0 of the head, in bounds, and are zeroed below)
+    const int r = 16 * wave + c16;
+    const int mt = (r < R ? r : 0) / G, gq = (r < R ? r : 0) % G;
+    uint4 qraw[4];
     {
-        const int kpos = t0 + tid;
-        float ks = 0.0f, vs = 0.0f;
-        if (kpos < ctx) {
-            const int pg = ptab[kpos / a.page];
-            const int64_t o = ((int64_t)pg * a.Hkv + hk) * a.page + kpos % a.page;
-            ks = a.k_scale[o];
-            vs = a.v_scale[o];
-        }
-        kss[tid] = ks;
-        vss[tid] = vs;
-        // the tile's largest V scale over keys inside [lo_b, ctx)
-        float vm = (kpos >= lo_b && kpos < ctx) ? vs : 0.0f;
-        vm = wave_max(vm);
-        if (lane == 0) red_v[wave] = vm;
-    }
-    // ---- 4. Q rows -> e4m3 with a per-row scale ------------------------------
-    // thread: rows tid / 16 + 16 i, 8 channels [8 (tid % 16), +8)
+        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM +
+                             (int64_t)(hk * G + gq) * a.q_sH + 32 * q4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tid / 16 + 16 * i, ch = tid % 16;
-        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < R) {
-            const int mt = r / G, g = r % G;
-            const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM +
-                                 (int64_t)(hk * G + g) * a.q_sH + 8 * ch;
-            const uint4 u = *(const uint4*)qp;
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        for (int i = 0; i < 4; ++i) qraw[i] = *(const uint4*)(qp + 8 * i);
+    }
+
+    // ---- 2. page ids of the tile's page-blocks (scalar loads, all in flight
+    // at once).  Page-block i is page t0 / page + i; a block that starts past
+    // the context uses the last token's page, so every copy below reads inside
+    // a real page; page ids outside [0, num_pages) read page 0.
+    const int koff = a.page > kTile ? t0 % a.page : 0;   // tile offset inside a large page
+    const auto* ptab = scalar_ptr(a.page_table + (int64_t)b * a.pt_stride);
+    const int p0 = __builtin_amdgcn_readfirstlane(t0 / a.page);
+    const int pl = __builtin_amdgcn_readfirstlane(last / a.page);
+    int pid[kNpb];
+#pragma unroll
+    for (int i = 0; i < kNpb; ++i) pid[i] = ptab[min(p0 + i, pl)];
+#pragma unroll
+    for (int i = 0; i < kNpb; ++i) pid[i] = (unsigned)pid[i] < (unsigned)a.num_pages ? pid[i] : 0;
+
+    // per-token scales of key t0 + tid (issued before the copies)
+    float ks, vs;
+    {
+        const int pbs = tid / PW;
+        int pg = pid[0];
+#pragma unroll
+        for (int i = 1; i < kNpb; ++i) pg = pbs == i ? pid[i] : pg;
+        const int64_t o = ((int64_t)pg * a.Hkv + hk) * a.page + (koff + tid % PW);
+        ks = a.k_scale[o];
+        vs = a.v_scale[o];
+    }
+
+    // ---- 3. tile copies: 8 K and 8 V^T instructions per wave, 1 KB each.
+    // Instruction i = wave + 4 j fills LDS chunks [64 i, +64) of each tile;
+    // both tiles hold 128 n chunks per page-block (n = PW / 16), so it lies in
+    // page-block (wave + 4 j) / (2 n) = j >> (log2 n - 1), a constant.
+    const int kpage = a.page * kD;                   // bytes of one page of one KV head
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = wave + 4 * j;
+        constexpr int kShift = kLgn - 1;
+        const int pg = pid[j >> kShift];
+        // K: keys [8 i, +8) of the tile
+        const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+        const int key = 8 * i + (lane >> 3);
+        const int kc = (lane & 7) ^ dk_swz(key);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + 1024 * i, 16,
+                                                 (koff + key % PW) * kD + 16 * kc, 0, 0, 0);
+        // V^T: rows d of page-block (j >> kShift), chunks c
+        const int within = ((64 * i) & ((128 << kLgn) - 1)) + lane;
+        const int d = within >> kLgn, c = (within & ((1 << kLgn) - 1)) ^ dv_swz<kLgn>(d);
+        const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16, d * a.page + koff + 16 * c,
+                                                 0, 0, 0);
+    }
+    // keep the Q arithmetic below (which waits for the Q loads) from being
+    // scheduled in between the copy instructions
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. Q row -> e4m3 with a per-row scale (the B operand of QK) ---------
+    v8i qf;
+    float qs;
+    {
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                x[2 * k] = bf16_bits_to_f32(w[k] & 0xFFFF);
-                x[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+                x[8 * i + 2 * k] = r < R ? bf16_bits_to_f32(w[k] & 0xFFFF) : 0.0f;
+                x[8 * i + 2 * k + 1] = r < R ? bf16_bits_to_f32(w[k] >> 16) : 0.0f;
             }
         }
         float am = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+        for (int k = 0; k < 32; ++k) am = fmaxf(am, fabsf(x[k]));
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
         const float inv = am > 0.0f ? kFp8Max / am : 0.0f;
-        uint32_t c0 = cvt_pk_fp8<false>(x[0] * inv, x[1] * inv, 0);
-        c0 = cvt_pk_fp8<true>(x[2] * inv, x[3] * inv, c0);
-        uint32_t c1 = cvt_pk_fp8<false>(x[4] * inv, x[5] * inv, 0);
-        c1 = cvt_pk_fp8<true>(x[6] * inv, x[7] * inv, c1);
-        *(uint2*)&q8s[r][8 * ch] = make_uint2(c0, c1);
-        if (ch == 0) qss[r] = am / kFp8Max;
-    }
-    __syncthreads();
-    const float vmax = fmaxf(fmaxf(red_v[0], red_v[1]), fmaxf(red_v[2], red_v[3]));
-
-    // ---- 5. S^T = K Q^T for this wave's 64 keys x 64 rows ---------------------
-    float x[2][2][16];   // [query block][sub-tile][e]
-    float rmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = 32 * qb + col;
-        const float qs = qss[r];
-        const int mt = r / G;
-        const int pos = ctx - a.MTP + mt;
-        const int lo = a.window > 0 ? pos - a.window + 1 : 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            v16f acc = {0};
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const v4i blo = *(const v4i*)&q8s[r][64 * c + 32 * half];
-                const v4i bhi = *(const v4i*)&q8s[r][64 * c + 32 * half + 16];
-                const v8i bq = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-                const uint4 k0 = kreg[t][c][0], k1 = kreg[t][c][1];
-                const v8i ak = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
-                                (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
-                acc = mfma_f8_32x32x64(ak, bq, acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int kl = 64 * wave + 32 * t + 16 * half + e;
-                const int kpos = t0 + kl;
-                const bool ok = r < R && kpos < ctx && kpos <= pos && kpos >= lo;
-                const float xv = ((acc[e] * qs) * kss[kl]) * alpha;
-                x[qb][t][e] = ok ? xv : -INFINITY;
-                rmax[qb] = fmaxf(rmax[qb], x[qb][t][e]);
-            }
+        for (int w = 0; w < 8; ++w) {
+            uint32_t c0 = cvt_pk_fp8<false>(x[4 * w] * inv, x[4 * w + 1] * inv, 0);
+            qf[w] = (int)cvt_pk_fp8<true>(x[4 * w + 2] * inv, x[4 * w + 3] * inv, c0);
         }
-        rmax[qb] = fmaxf(rmax[qb], __shfl_xor(rmax[qb], 32));
-        if (half == 0) red_m[wave][r] = rmax[qb];
+        qs = am / kFp8Max;
     }
-    __syncthreads();
 
-    // ---- 6. p = 2^(x - m); P' = p * v_scale -> e4m3 with the tile's vmax ----
-    const float pinv = vmax > 0.0f ? kFp8Max / vmax : 0.0f;
+    const int kpos_s = t0 + tid;
+    kss[tid] = kpos_s < ctx ? ks : 0.0f;
+    vss[tid] = kpos_s < ctx ? vs : 0.0f;
+    __syncthreads();   // every wave's copies have landed (vmcnt(0)) and the scales are in LDS
+
+    // the tile's largest V scale over keys inside [lo_b, ctx)
+    float vmax;
+    {
+        const float4 v4 = *(const float4*)&vss[4 * lane];
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        float vm = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = 32 * qb + col;
-        const float M = fmaxf(fmaxf(red_m[0][r], red_m[1][r]), fmaxf(red_m[2][r], red_m[3][r]));
-        const float Mb = M == -INFINITY ? 0.0f : M;
-        float ls = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const int kp = t0 + 4 * lane + i;
+            vm = fmaxf(vm, (kp >= lo_b && kp < ctx) ? vv[i] : 0.0f);
+        }
+        vmax = wave_max(vm);
+    }
+
+    // ---- 5. S^T for 256 keys x this wave's 16 rows: MFMA (g, m) holds, in
+    // element i of lane l, key 128 g + 32 (l / 16) + 4 m + i of query row r.
+    v4f S[2][8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            uint32_t pk[4];
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                float pp[4];
+        for (int m = 0; m < 8; ++m) {
+            const int key = 128 * g + 32 * (c16 >> 2) + 4 * m + (c16 & 3);   // A row c16
+            const int sw = dk_swz(key);
+            const uint8_t* krow = kt_s + key * kD;
+            const v4i lo = *(const v4i*)(krow + 16 * ((2 * q4) ^ sw));
+            const v4i hi = *(const v4i*)(krow + 16 * ((2 * q4 + 1) ^ sw));
+            S[g][m] = mfma_f8_16x16x128(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf,
+                                        v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+
+    // ---- 6. masked scores, row max and sum over the 4 lanes of the row -------
+    const int pos = ctx - a.MTP + mt;
+    const int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    // A tile whose every key is visible to every query row (all but the first
+    // and last tiles of a window) skips the per-key mask; rows past R are
+    // padding whose results are never stored.
+    const bool all_vis = t0 + kTile - 1 <= ctx - a.MTP && (a.window <= 0 || t0 >= ctx - a.window);
+    float rmax = -INFINITY;
+    auto scores = [&](auto all_tag) {
+        constexpr bool ALL = decltype(all_tag)::value;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = 4 * w4 + j;
-                    const int kl = 64 * wave + 32 * t + 16 * half + e;
-                    const float p = __builtin_amdgcn_exp2f(x[qb][t][e] - Mb);
-                    ls += p;
-                    pp[j] = (p * vss[kl]) * pinv;
+        for (int g = 0; g < 2; ++g) {
+            const int kl0 = 128 * g + 32 * q4;         // tile-relative key of element (m, i) = kl0 + 4 m + i
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 k4 = *(const float4*)&kss[kl0 + 4 * m];
+                const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float xv = ((S[g][m][i] * qs) * kk[i]) * alpha;
+                    if constexpr (ALL) {
+                        S[g][m][i] = xv;
+                    } else {
+                        const int key = t0 + kl0 + 4 * m + i;
+                        const bool ok = r < R && key < ctx && key <= pos && key >= lo;
+                        S[g][m][i] = ok ? xv : -INFINITY;
+                    }
+                    rmax = fmaxf(rmax, S[g][m][i]);
                 }
-                uint32_t v = cvt_pk_fp8<false>(pp[0], pp[1], 0);
-                pk[w4] = cvt_pk_fp8<true>(pp[2], pp[3], v);
             }
-            *(uint4*)&p8s[r][64 * wave + 32 * t + 16 * half] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
-        ls += __shfl_xor(ls, 32);
-        if (half == 0) red_l[wave][r] = ls;
-    }
-    __syncthreads();
-
-    // ---- 7. O^T = V^T P^T for channels [32 wave, +32) ---------------------------
-    const float back = vmax / kFp8Max;
+    };
+    if (all_vis)
+        scores(std::true_type{});
+    else
+        scores(std::false_type{});
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float Mb = rmax == -INFINITY ? 0.0f : rmax;
+    // p = 2^(x - m); P' = p * v_scale -> e4m3 with the tile's vmax, packed as
+    // the B operand of PV (byte 4 m + i of group g = key kl0 + 4 m + i)
+    const float pinv = vmax > 0.0f ? kFp8Max / vmax : 0.0f;
+    float ls = 0.0f;
+    v8i pf[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = 32 * qb + col;
-        v16f acc = {0};
+    for (int g = 0; g < 2; ++g) {
+        const int kl0 = 128 * g + 32 * q4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const v4i blo = *(const v4i*)&p8s[r][64 * u + 32 * half];
-            const v4i bhi = *(const v4i*)&p8s[r][64 * u + 32 * half + 16];
-            const v8i bp = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-            const uint4 v0 = vreg[u][0], v1 = vreg[u][1];
-            const v8i av = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                            (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-            acc = mfma_f8_32x32x64(av, bp, acc);
-        }
-        if (r < R) {
-            float* prow = a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartStride;
+        for (int m = 0; m < 8; ++m) {
+            const float4 v4 = *(const float4*)&vss[kl0 + 4 * m];
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            float pp[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * wave + 8 * i + 4 * half;
-                *(float4*)(prow + d0) = make_float4(acc[4 * i] * back, acc[4 * i + 1] * back,
-                                                    acc[4 * i + 2] * back, acc[4 * i + 3] * back);
+                const float p = __builtin_amdgcn_exp2f(S[g][m][i] - Mb);
+                ls += p;
+                pp[i] = (p * vv[i]) * pinv;
             }
-            if (wave == 0 && half == 0) {
-                const float M = fmaxf(fmaxf(red_m[0][r], red_m[1][r]), fmaxf(red_m[2][r], red_m[3][r]));
-                const float L = red_l[0][r] + red_l[1][r] + red_l[2][r] + red_l[3][r];
-                prow[kD] = M;
-                prow[kD + 1] = L;
+            const uint32_t c0 = cvt_pk_fp8<false>(pp[0], pp[1], 0);
+            pf[g][m] = (int)cvt_pk_fp8<true>(pp[2], pp[3], c0);
+        }
+    }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+
+    // ---- 7. O^T = V^T P^T: element i of lane l of d-block db is channel
+    // 16 db + 4 (l / 16) + i of query row r
+    const bool all_in = t0 + kTile <= ctx;   // no page slot past the context in this tile
+    v4f O[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        const int d = 16 * db + c16;
+        const int sw = dv_swz<kLgn>(d);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int k0 = 128 * g + 32 * q4;           // tile-relative first key of this lane's 32
+            const int pb = k0 / PW, c = (k0 % PW) / 16;
+            const uint8_t* vrow = vt_s + (pb * 128 + d) * PW;
+            // keys at or beyond ctx may hold any bytes (e4m3 NaN codes
+            // included) and 0 * NaN would poison the product: zero them
+            uint4 lo4 = *(const uint4*)(vrow + 16 * (c ^ sw));
+            uint4 hi4 = *(const uint4*)(vrow + 16 * ((c + 1) ^ sw));
+            if (!all_in) {
+                const int nv = ctx - (t0 + k0);
+                lo4 = keep_bytes(lo4, nv);
+                hi4 = keep_bytes(hi4, nv - 16);
             }
+            const v8i av = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                            (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+            O[db] = mfma_f8_16x16x128(av, pf[g], O[db]);
+        }
+    }
+    if (r < R) {
+        const float back = vmax / kFp8Max;
+        float* prow = a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartStride;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            *(float4*)(prow + 16 * db + 4 * q4) =
+                make_float4(O[db][0] * back, O[db][1] * back, O[db][2] * back, O[db][3] * back);
+        if (q4 == 0) {
+            prow[kD] = rmax;
+            prow[kD + 1] = ls;
         }
     }
 }
 
 // Merge of the split partials of one (sequence, KV head, row): m* = max m_s,
 // out = sum 2^(m_s - m*) O_s / sum 2^(m_s - m*) l_s (fp32, split order), bf16.
-// One wave per row: lane s holds split s's (m, l) (splits beyond 64 are
-// folded in lane order); the weights are broadcast and every lane then merges
-// two output channels over all splits with coalesced loads.
+// One wave per row; the weights are broadcast and every lane merges two
+// output channels over all splits with coalesced loads.
 constexpr int kMergeRowsPerBlock = 4;
+constexpr int kMergeBatch = 32;
 
 __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
@@ -285,31 +351,45 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     const int bk = rowg / kRows, r = rowg % kRows;
     if (bk >= a.B * a.Hkv || r >= R) return;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
-    const int ctx = a.ctx_lens[b];
+    const int ctx = min(a.ctx_lens[b], a.max_pages * a.page);
     const int G = a.Hq / a.Hkv;
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
     const float* base = a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartStride;
     const int64_t sstride = (int64_t)kRows * kPartStride;
-    float M = -INFINITY;
-    for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, base[sp * sstride + kD]);
-    M = wave_max(M);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int s0 = 0; s0 < nsp; s0 += 64) {
-        const int sp = s0 + lane;
-        float w = 0.0f, lw = 0.0f;
-        if (sp < nsp) {
-            const float ms = base[sp * sstride + kD];
-            w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            lw = w * base[sp * sstride + kD + 1];
+    // Splits are taken kMergeBatch at a time with every load of a batch in
+    // flight at once: lane s holds split s's (m, l), every lane two output
+    // channels of each split.  With at most kMergeBatch splits (windowed
+    // decode) this is the plain two-step merge; longer contexts carry a
+    // running max across batches and rescale the running sums.
+    float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = 0; s0 < nsp; s0 += kMergeBatch) {
+        const int n = min(kMergeBatch, nsp - s0);
+        float2 ml = make_float2(-INFINITY, 0.0f);
+        if (lane < n) ml = *(const float2*)(base + (s0 + lane) * sstride + kD);
+        float2 o[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+            o[u] = u < n ? *(const float2*)(base + (s0 + u) * sstride + 2 * lane) : make_float2(0.0f, 0.0f);
+        const float Mn = fmaxf(M, wave_max(ml.x));
+        if (Mn == -INFINITY) continue;               // no visible key so far
+        if (M != -INFINITY && M != Mn) {
+            const float sc = __builtin_amdgcn_exp2f(M - Mn);
+            L *= sc;
+            o0 *= sc;
+            o1 *= sc;
         }
-        const int n = min(64, nsp - s0);
-        for (int j = 0; j < n; ++j) {
-            const float wj = __shfl(w, j);
-            L = L + __shfl(lw, j);
-            const float2 o = *(const float2*)(base + (s0 + j) * sstride + 2 * lane);
-            o0 = o0 + wj * o.x;
-            o1 = o1 + wj * o.y;
+        M = Mn;
+        const float w = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
+        const float lw = w * ml.y;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            if (u < n) {
+                const float wj = __shfl(w, u);
+                L = L + __shfl(lw, u);
+                o0 = o0 + wj * o[u].x;
+                o1 = o1 + wj * o[u].y;
+            }
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -324,7 +404,12 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid(a.num_splits, a.B * a.Hkv);
-    k_paged_decode<<<grid, kThreads, 0, stream>>>(a, alpha);
+    switch (a.page < kTile ? a.page : kTile) {
+        case 32: k_paged_decode<32><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        case 64: k_paged_decode<64><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        case 128: k_paged_decode<128><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        default: k_paged_decode<256><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+    }
     const int rows = a.B * a.Hkv * kRows;
     k_decode_merge<<<(rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock, 64 * kMergeRowsPerBlock, 0,
                      stream>>>(a);

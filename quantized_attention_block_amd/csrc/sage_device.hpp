@@ -37,6 +37,11 @@ __device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b, v16i c) {
 __device__ __forceinline__ v16f mfma_f8_32x32x64(v8i a, v8i b, v16f c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// e4m3 x e4m3 16x16x128: lane l supplies row / column l % 16 and K-slice
+// [32 (l / 16), +32); element i of the result is row 4 (l / 16) + i, column l % 16
+__device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 // E2M1 x E2M1 with per-lane E8M0 scales (byte 0 of sa / sb); only the first
 // four dwords of a and b are read.
 __device__ __forceinline__ v16f mfma_f4_32x32x64(v8i a, v8i b, v16f c, int sa, int sb) {
