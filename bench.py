@@ -3,7 +3,9 @@
 One step = quantize Q/K (K channel mean + INT8 blocks) + quantize V (e4m3,
 per-channel scale, transposed) + fused quantized attention, on the
 LLM-prefill workload (B=2, H=32, Lq=Lk=4096, D=128, bf16, causal), inputs
-resident in HBM.  Prints one JSON line:
+resident in HBM, launched eagerly; the same step replayed from a HIP graph
+(each replay first checked bit-equal to an eager step) is reported beside it.
+Prints one JSON line:
 
   value        = 4 B H Lq Lk D / t_step  (the metric's own formula, TOPS)
   roofline     = the attention kernel alone: algorithmic ops (unmasked causal
@@ -78,8 +80,9 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
     qk = sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, want_mean=False)
     v_q, v_s = sage.sage_quantize_v(inp.v)
     out = torch.empty((w.B, w.Lq, w.H, w.D), dtype=torch.bfloat16, device=dev)
-    ws_qk = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    ws_qk = torch.empty(max(16, sage.sage_quantize_qk_workspace_size(inp.q, inp.k, mode=mode)),
+                        dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(sage.sage_quantize_v_workspace_size(inp.v), dtype=torch.uint8, device=dev)
 
     def quant():
         sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, workspace=ws_qk, into=qk)
@@ -92,6 +95,12 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
         quant()
         attn()
 
+    # untimed pre-warm (~0.2 s of steps) so clocks have settled before the
+    # W warm-up steps and the K timed ones
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -100,6 +109,30 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
         step()
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / steps
+    # The same step captured once in a HIP graph and replayed (context): each
+    # replay is first checked bit for bit against an eager step, with eager
+    # work in between.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        step()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError(f"{wname}: graph replay differs from the eager step")
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_step_graph = (time.perf_counter() - t0) / steps
     # attention kernel alone, HIP events on its stream
     attn()
     t_attn = min(_events_time(attn, max(steps, 10), stream) for _ in range(3))
@@ -110,7 +143,8 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
     peak = PEAK_MXFP4_MIX_TOPS if mode == sage.QK_MXFP4 else PEAK_MFMA_TOPS
     achieved = ops_alg / t_attn / 1e12
     src = ["attn_fwd.hip", "sage_device.hpp"]
-    return dict(w=w, t_step=t_step, t_attn=t_attn, value=literal / t_step / 1e12,
+    return dict(w=w, t_step=t_step, t_step_graph=t_step_graph, t_attn=t_attn,
+                value=literal / t_step / 1e12,
                 attn_literal_tops=literal / t_attn / 1e12,
                 roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                           "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -234,7 +268,8 @@ def main():
     w = r["w"]
     extra = {"attn_kernel_us": round(r["t_attn"] * 1e6, 1),
              "attn_kernel_tops_literal": round(r["attn_literal_tops"], 1),
-             "quantize_us": round((r["t_step"] - r["t_attn"]) * 1e6, 1)}
+             "quantize_us": round((r["t_step"] - r["t_attn"]) * 1e6, 1),
+             "ms_per_step_hip_graph": round(r["t_step_graph"] * 1e3, 4)}
     if not args.no_decode:
         extra["paged_decode"] = decode_bench(args.steps, args.warmup, dev)
     if args.all:

@@ -286,22 +286,29 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
     char* ws = (char*)workspace;
     const sage::HalfView qv = half_view(q), kv = half_view(k);
     float* mu = nullptr;
+    double* partial = nullptr;
     size_t off = 0;
     if (params->smooth_k) {
-        double* partial = (double*)(ws + off);
+        // channel sums of K per token chunk (binary64); the INT8 quantizer
+        // finishes the mean itself, the MXFP4 path in a separate step
+        partial = (double*)(ws + off);
         off += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * s.D * sizeof(double));
         mu = k_mean ? (float*)k_mean->data : (float*)(ws + off);
         off += align256((size_t)s.B * s.H * s.D * sizeof(float));
-        hipError_t e = sage::launch_k_mean(kv, s.B, s.H, s.Lk, s.D, partial, mu, strm);
+        hipError_t e = sage::launch_k_mean_partial(kv, s.B, s.H, s.Lk, s.D, partial, strm);
         if (e != hipSuccess) return launch_status(e, "k mean");
     }
     hipError_t e;
     if (params->mode == SAGE_QK_INT8) {
-        e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->q_block,
-                                       params->k_block, mu, (int8_t*)q_out->data,
+        e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->k_block, partial,
+                                       k_mean ? (float*)k_mean->data : nullptr, (int8_t*)q_out->data,
                                        (float*)q_scale->data, (int8_t*)k_out->data,
                                        (float*)k_scale->data, strm);
     } else {
+        if (partial) {
+            e = sage::launch_k_mean_final(partial, s.B, s.H, s.Lk, s.D, mu, strm);
+            if (e != hipSuccess) return launch_status(e, "k mean");
+        }
         float* mu_rot = (float*)(ws + off);
         e = sage::launch_quant_qk_mxfp4(
             qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, mu, hadamard ? hadamard->bf16_mat : nullptr,
@@ -316,7 +323,8 @@ sage_status sage_quantize_v_workspace_size(const sage_tensor* v, size_t* bytes) 
     sage_status st = check_half_view(v, "v");
     if (st) return st;
     if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes: null");
-    *bytes = align256((size_t)v->shape[0] * v->shape[2] * v->shape[3] * sizeof(uint32_t));
+    *bytes = align256((size_t)v->shape[0] * v->shape[2] * sage::mean_chunks((int)v->shape[1]) *
+                      v->shape[3] * sizeof(float));
     return ok();
 }
 
@@ -330,13 +338,13 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out, cons
     const int64_t os[4] = {B, H, D, sage::pad128(Lk)}, ss[3] = {B, H, D};
     if ((st = check_exact(v_out, "v_out", SAGE_FP8_E4M3FN, 4, os))) return st;
     if ((st = check_exact(v_scale, "v_scale", SAGE_F32, 3, ss))) return st;
-    const size_t need = align256((size_t)B * H * D * sizeof(uint32_t));
+    const size_t need = align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float));
     if (!workspace || workspace_bytes < need)
         return fail(SAGE_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(SAGE_ERR_ALIGNMENT, "workspace not 16-byte aligned");
     if ((st = check_device())) return st;
-    hipError_t e = sage::launch_quant_v(half_view(v), B, H, Lk, D, (uint32_t*)workspace,
+    hipError_t e = sage::launch_quant_v(half_view(v), B, H, Lk, D, (float*)workspace,
                                         (uint8_t*)v_out->data, (float*)v_scale->data,
                                         (hipStream_t)stream);
     return launch_status(e, "quantize v");

@@ -31,18 +31,24 @@ constexpr int kDecodeTile = 256;   // decode split length (tokens)
 __host__ __device__ inline int pad128(int L) { return (L + 127) / 128 * 128; }
 inline int mean_chunks(int L) { return (L + kMeanChunk - 1) / kMeanChunk; }
 
-// K mean: partial fp64 sums [B*H, nchunk, D] then mu fp32 [B*H, D].
-hipError_t launch_k_mean(const HalfView& k, int B, int H, int L, int D, double* partial,
-                         float* mu, hipStream_t stream);
+// K mean: partial binary64 sums [B*H, nchunk, D] (nchunk = mean_chunks(L));
+// the final mean mu fp32 [B*H, D] (sum in chunk order / L).
+hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, double* partial,
+                                 hipStream_t stream);
+hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D, float* mu,
+                               hipStream_t stream);
 
-// INT8 block quantization of Q (q_block rows) and smoothed K (k_block rows).
+// INT8 block quantization of Q (128-row blocks) and smoothed K (k_block rows,
+// 64 or 128), finishing the K mean from mean_partial (NULL: no smoothing)
+// and writing it to mu_out (may be NULL).
 hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
-                                int Lk, int D, int q_block, int k_block, const float* mu,
-                                int8_t* q_out, float* q_scale, int8_t* k_out, float* k_scale,
-                                hipStream_t stream);
+                                int Lk, int D, int k_block, const double* mean_partial,
+                                float* mu_out, int8_t* q_out, float* q_scale, int8_t* k_out,
+                                float* k_scale, hipStream_t stream);
 
-// V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales.
-hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, uint32_t* amax_ws,
+// V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales;
+// amax_partial: fp32 [B*H, mean_chunks(Lk), D] scratch.
+hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
                           uint8_t* v_out, float* v_scale, hipStream_t stream);
 
 // Hadamard rotation (optional) + MXFP4 quantization of Q and smoothed K.

@@ -228,6 +228,24 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
     return QuantizedQK(mode, q_out, q_sc, k_out, k_sc, mean, Lq, Lk, q_block, k_block)
 
 
+def sage_quantize_qk_workspace_size(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8,
+                                    q_block: int = 128, k_block: int = 64,
+                                    smooth_k: bool = True) -> int:
+    """Bytes of device workspace sage_quantize_qk needs for these inputs."""
+    prm = QkParams(mode, q_block, k_block, int(smooth_k))
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_quantize_qk_workspace_size(ctypes.byref(desc(q)), ctypes.byref(desc(k)),
+                                                 ctypes.byref(prm), ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def sage_quantize_v_workspace_size(v: torch.Tensor) -> int:
+    """Bytes of device workspace sage_quantize_v needs for this input."""
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_quantize_v_workspace_size(ctypes.byref(desc(v)), ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
 def sage_quantize_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None, into=None):
     """v: logical [B, Lk, H, D] fp16/bf16.  Returns (e4m3 [B,H,D,pad128(Lk)],
     fp32 per-channel scales [B,H,D]); `into` reuses such a pair."""
