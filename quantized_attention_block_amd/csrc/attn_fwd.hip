@@ -16,19 +16,20 @@
 //
 // gfx950 design:
 //  - Block = 4 waves = 128 query rows (one Q scale block); each wave owns 32
-//    query rows for the whole KV loop (Q fragments stay in VGPRs).
+//    query rows for the whole KV loop (Q fragments stay in VGPRs).  Three
+//    blocks share a CU (<= 168 VGPRs per lane, 48 KB of LDS per block), so
+//    while one wave waits on an MFMA result, an LDS read or a barrier, the
+//    other waves of its SIMD issue VALU and MFMA work.  (A software-pipelined
+//    form of the loop, QK of tile j+1 and PV of tile j-1 around the softmax of
+//    tile j, needs ~226 VGPRs and so runs two waves per SIMD; it measured
+//    7-10 % slower.)
 //  - KV tiles of 64 keys are copied global -> LDS with 16-byte
 //    buffer_load ... lds instructions (no staging registers) into a ring of
-//    five LDS stages, two steps ahead of use; one barrier per tile.  16-byte
-//    chunks are XOR-swizzled per row so the MFMA operand reads do not
-//    collide on LDS banks.
-//  - Software pipeline per wave: step j issues the PV MFMAs of tile j-1 and
-//    the QK MFMAs of tile j+1 in the same basic block as the softmax VALU
-//    work (row max, convert, exp2, FP8 pack) of tile j, so the matrix cores
-//    run while the vector ALUs work.  O's rescale for tile j's new row max is
-//    applied at the top of step j+1, before PV(j) joins O.  Stage use in
-//    step j: K of j+1 and V of j-1 are read, V of j waits for the next step,
-//    j+2 and j+3 are landing.
+//    three LDS stages, two tiles ahead of use.  The per-tile barrier waits
+//    only for the tile it needs (s_waitcnt vmcnt(N) + s_barrier; the release
+//    fence of __syncthreads() would drain every copy in flight).  16-byte
+//    chunks are XOR-swizzled per row so the MFMA operand reads do not collide
+//    on LDS banks.
 //  - The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_i32_32x32x32_i8: each lane then holds one query and, per 32-key
 //    sub-tile, 16 consecutive keys (K rows are fed to the A operand in a
@@ -52,7 +53,8 @@ namespace {
 constexpr int kBM = 128;            // query rows per block
 constexpr int kBN = kKvTile;        // keys per KV tile
 constexpr int kNT = kBN / 32;       // 32-key sub-tiles per tile
-constexpr int kStages = 5;          // LDS ring depth: tiles j-1 .. j+3 in step j
+constexpr int kStages = 3;          // LDS ring: tile j read, j+1 and j+2 landing
+constexpr int kWavesPerSimd = 3;    // occupancy target: 3 blocks of 4 waves per CU
 constexpr int kThreads = 256;
 constexpr float kLog2Fp8Max = 8.807354922057604f;   // log2(448)
 static_assert(kBN == 64, "the PV operand packing assumes 64-key tiles");
@@ -301,29 +303,9 @@ __device__ __forceinline__ void load_qfrag(QFrag<D, MX>& q, const uint8_t* qbase
     }
 }
 
-// Instruction order of the full-tile loop body for the machine scheduler:
-// the LDS reads of the first QK operands and the row max first, then each
-// MFMA (QK of the next tile, PV of the previous one) followed by one or two
-// LDS operand reads and a slice of the softmax VALU work, so the matrix core
-// and the vector ALU run side by side within one wave.
 template <int D, bool MX>
-__device__ __forceinline__ void interleave() {
-    constexpr int kMfma = (MX ? 2 * (D / 64) : 2 * (D / 32)) + D / 32;   // QK + PV
-    constexpr int kReads = 2 * (MX ? D / 64 : D / 32) + 2 * (D / 32);   // b128 operand reads
-    constexpr int kLead = (MX ? D / 64 : D / 32) + 2;                    // issued before the first MFMA
-    constexpr int kValu = MX ? 10 : 16;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);    // DS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);       // VALU
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        if (kLead + i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-    }
-}
-
-template <int D, bool MX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_fwd(AttnArgs a, float alpha) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_attn_fwd(
+    AttnArgs a, float alpha) {
     using G = Geo<D, MX>;
     using SAcc = SAccT<D, MX>;
     constexpr int kDB = D / 32;         // 32-row blocks of O^T
@@ -371,21 +353,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // more, for the K scales; counting without it only waits longer)
     constexpr int kDma = Dma::kKRegions / 4 + Dma::kVRegions / 4;
 
-    // tiles 0, 1 and 2 in flight before the loop; tile j + 3 is issued in
-    // step j, two steps before its K is read
+    // tiles 0 and 1 in flight before the loop; tile j + 2 is issued in step j
     Dma::issue(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane);
     if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
-    if (ntiles > 2) Dma::issue(stage_of(2), krs, ksrs, vrs, Lkp, 2, wave, lane);
 
     QFrag<D, MX> qf;
     load_qfrag<D, MX>(qf, qbase, qsc, qrow, lane);
     // Score scale of tile kt: c = fp32(fp32(q_s k_s) alpha) for INT8 (a 64-key
-    // tile lies inside one K scale block), alpha for MXFP4.
+    // tile lies inside one K scale block), alpha for MXFP4.  (Read through the
+    // constant address space: a scalar load, which does not queue behind the
+    // LDS DMA in the vector memory counter.)
     float q_s = 0.0f;
     if constexpr (!MX) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
     const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
-    // (read through the constant address space: a scalar load, which does not
-    // queue behind the LDS DMA in the vector memory counter)
     const __attribute__((address_space(4))) float* kscale_c =
         (const __attribute__((address_space(4))) float*)kscale_f;
     auto tile_c = [&](int kt) -> float {
@@ -393,62 +373,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         else return (q_s * kscale_c[kt * kBN / a.k_block]) * alpha;
     };
 
-    // PV(j - 1) at j = 0 multiplies P = 0 with the V region of the last
-    // stage; zero it so that stale LDS bytes (which may be e4m3 NaN codes)
-    // add exactly 0.
-    {
-        uint8_t* vz = stage_of(kStages - 1) + G::kVOff;
-        for (int i = tid; i < G::kVBytes / 16; i += kThreads) *(v4i*)(vz + 16 * i) = v4i{0, 0, 0, 0};
-    }
-    if (ntiles > 2)
-        dma_barrier<2 * kDma>();   // tile 0 has landed (tiles 1, 2 may be in flight)
-    else if (ntiles > 1)
-        dma_barrier<kDma>();
-    else
-        dma_barrier<0>();
-
-    // Scores of the current tile and P of the previous one live in one of two
-    // register sets (A, B) that swap roles every iteration (no copies).
     const v16i sbias = MX ? v16i{0} : score_bias();
-    SAcc SA[kNT], SB[kNT];
-#pragma unroll
-    for (int t = 0; t < kNT; ++t) SA[t] = qk_subtile<D, MX>(stage_of(0), qf, t, lane, sbias);
-    float c_cur = tile_c(0);
-
     v16f O[kDB];
 #pragma unroll
     for (int i = 0; i < kDB; ++i) O[i] = v16f{0};
     float m = -INFINITY, l = 0.0f;
-    v8i PA = {0, 0, 0, 0, 0, 0, 0, 0}, PB;
-    // O's rescale for a new row max is applied one iteration late, just
-    // before the next PV product joins O, when no MFMA writing O is in flight.
-    float sc_pend = 1.0f;
-    int pend = 0;
+    v8i pf = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    // One pipeline step: S holds the scores of tile j, P the packed P of tile
-    // j-1; on return Sn holds the scores of tile j+1 and Pn the P of tile j.
-    // FULL steps (no key of tile j masked for any row of the block) are one
-    // basic block; the others mask per 32-key sub-tile, which is wave-uniformly
-    // empty, crossing (keys tested one by one) or full for this wave's rows.
-    auto step = [&](int j, SAcc* S, SAcc* Sn, const v8i& P, v8i& Pn, auto full_tag) {
+    // One KV tile.  FULL steps (no key of the tile masked for any row of the
+    // block) have no per-key tests; the others mask per 32-key sub-tile, which
+    // is wave-uniformly empty, crossing (keys tested one by one) or full for
+    // this wave's rows.
+    auto step = [&](int j, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        // every wave's part of tile j+1 has landed (tile j+2 may be in flight)
-        // and all waves finished step j-1
-        if (j + 2 < ntiles)
+        // every wave's part of tile j has landed (tile j+1 may be in flight)
+        // and all waves finished step j-1, whose stage tile j+2 reuses
+        if (j + 1 < ntiles)
             dma_barrier<kDma>();
         else
             dma_barrier<0>();
-        if (j + 3 < ntiles) Dma::issue(stage_of(j + 3), krs, ksrs, vrs, Lkp, j + 3, wave, lane);
-        const float c_nxt = (j + 1 < ntiles) ? tile_c(j + 1) : 0.0f;
-        if (pend) {
-#pragma unroll
-            for (int i = 0; i < kDB; ++i) O[i] *= sc_pend;
-        }
+        if (j + 2 < ntiles) Dma::issue(stage_of(j + 2), krs, ksrs, vrs, Lkp, j + 2, wave, lane);
+        const float c = tile_c(j);
+        uint8_t* stage = stage_of(j);
         const int key0 = j * kBN;
-        // K of tile j+1 (past the last tile: a stale stage, result unused) and
-        // V of tile j-1 (stage of tile j + kStages - 1 = j - 1 modulo kStages)
-        uint8_t* st_k = stage_of(j + 1);
-        uint8_t* st_v = stage_of(j + kStages - 1);
 
         int st[kNT];   // 0 empty, 1 crossing, 2 full
 #pragma unroll
@@ -467,11 +414,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             return key < a.Lk && (!a.causal || key <= qrow);
         };
 
-        // PV of tile j-1 first (its operands are ready; O was rescaled above),
-        // alongside the row max of tile j
-        pv_tile<D, MX>(st_v, P, lane, O);
+        // S: element (t, e) is key key0 + 32 t + 16 half + e of query qrow
+        SAcc S[kNT];
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) S[t] = qk_subtile<D, MX>(stage, qf, t, lane, sbias);
 
-        // row max of tile j
+        // row max (on the integer scores for INT8: rounding is monotone)
         float tmax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
@@ -479,56 +427,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 auto mx = S[t][0];
 #pragma unroll
                 for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
-                tmax = fmaxf(tmax, score_f(mx) * c_cur);   // rounding is monotone
+                tmax = fmaxf(tmax, score_f(mx) * c);
             } else if (st[t] == 1) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c_cur : -INFINITY);
+                    tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c : -INFINITY);
             }
         }
         const float m_new = fmaxf(m, half_pair_max(tmax));
+        if (__any(m_new > m)) {   // online-softmax rescale, skipped when no row's max moved
+            const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+            l *= sc;
+#pragma unroll
+            for (int i = 0; i < kDB; ++i) O[i] *= sc;
+        }
+        m = m_new;
         const float mb = (FULL || m_new != -INFINITY ? m_new : 0.0f) - kLog2Fp8Max;
 
-        // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448)));
-        // l accumulates q (so l = 448 * sum p).  Packed as the PV B operand.
+        // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
+        // accumulates q (so l = 448 * sum p).  Packed as the PV B operand:
+        // byte 16 t + e = key 32 t + 16 half + e of the tile.  The low-word
+        // conversion keeps the high word of its third operand, which the
+        // high-word conversion overwrites: the word's stale value is passed, so
+        // no register has to be zeroed first.
         float ls = 0.0f;
-        auto pack = [&](int t) {
 #pragma unroll
-            for (int w = 4 * t; w < 4 * t + 4; ++w) {
-                const int e0 = 4 * (w % 4);
-                if (st[t] == 0) {
-                    Pn[w] = 0;
-                    continue;
-                }
-                float p[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float xv = __builtin_fmaf(score_f(S[t][e0 + jj]), c_cur, -mb);
-                    if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
-                    p[jj] = __builtin_amdgcn_exp2f(xv);
-                }
-                ls += (p[0] + p[1]) + (p[2] + p[3]);
-                uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], 0);
-                pk = cvt_pk_fp8<true>(p[2], p[3], pk);
-                Pn[w] = (int)pk;
+        for (int w = 0; w < 8; ++w) {
+            const int t = w / 4, e0 = 4 * (w % 4);
+            if (st[t] == 0) {
+                pf[w] = 0;
+                continue;
             }
-        };
-
-        // QK of tile j+1 around the exps of tile j
-        Sn[0] = qk_subtile<D, MX>(st_k, qf, 0, lane, sbias);
-        pack(0);
-        Sn[1] = qk_subtile<D, MX>(st_k, qf, 1, lane, sbias);
-        pack(1);
-
-        const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-        l = l * sc + ls;
-        pend = __any(m_new > m);
-        sc_pend = sc;
-        m = m_new;
-        c_cur = c_nxt;
-        // Pin the softmax results to this step's block: otherwise they are sunk
-        // past the next step's rescale branch, away from the MFMAs they overlap.
-        asm volatile("" ::"v"(Pn), "v"(l));
+            float p[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float xv = __builtin_fmaf(score_f(S[t][e0 + jj]), c, -mb);
+                if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
+                p[jj] = __builtin_amdgcn_exp2f(xv);
+            }
+            ls += (p[0] + p[1]) + (p[2] + p[3]);
+            uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], (uint32_t)pf[w]);
+            pk = cvt_pk_fp8<true>(p[2], p[3], pk);
+            pf[w] = (int)pk;
+        }
+        pv_tile<D, MX>(stage, pf, lane, O);
+        l += ls;
     };
 
     // Tiles [0, n_full) are full for every wave of the block.
@@ -536,31 +479,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (a.causal) n_full = min(n_full, qb * (kBM / kBN));
     n_full = min(n_full, ntiles);
     int j = 0;
-    for (; j + 2 <= n_full; j += 2) {
-        step(j, SA, SB, PA, PB, std::true_type{});
-        step(j + 1, SB, SA, PB, PA, std::true_type{});
-    }
-    auto rotate = [&]() {
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) SA[t] = SB[t];
-        PA = PB;
-    };
-    if (j < n_full) {
-        step(j, SA, SB, PA, PB, std::true_type{});
-        rotate();
-        ++j;
-    }
-    for (; j < ntiles; ++j) {
-        step(j, SA, SB, PA, PB, std::false_type{});
-        rotate();
-    }
-    // PV of the last tile (its stage is not overwritten: no DMA was issued
-    // after the last tile), after the last pending rescale
-    if (pend) {
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) O[i] *= sc_pend;
-    }
-    pv_tile<D, MX>(stage_of(ntiles - 1), PA, lane, O);
+    for (; j < n_full; ++j) step(j, std::true_type{});
+    for (; j < ntiles; ++j) step(j, std::false_type{});
 
     // ---- epilogue: out = (O * v_scale) / l (times the reciprocal of l), written
     // with the caller's strides
