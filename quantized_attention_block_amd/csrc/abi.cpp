@@ -199,9 +199,16 @@ size_t qk_ws_bytes(const QkShape& s, const sage_qk_params* p) {
     if (p->smooth_k) {
         n += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * s.D * sizeof(double));
         n += align256((size_t)s.B * s.H * s.D * sizeof(float));   // mu when k_mean is NULL
+        n += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * sizeof(int32_t));   // arrival flags
     }
     if (p->mode == SAGE_QK_MXFP4) n += align256((size_t)s.B * s.H * s.D * sizeof(float));
     return n;
+}
+
+// V: channel amax per token chunk (fp32), then one arrival flag per chunk
+size_t v_ws_bytes(int B, int Lk, int H, int D) {
+    return align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float)) +
+           align256((size_t)B * H * sage::mean_chunks(Lk) * sizeof(int32_t));
 }
 
 }  // namespace
@@ -287,25 +294,28 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
     const sage::HalfView qv = half_view(q), kv = half_view(k);
     float* mu = nullptr;
     double* partial = nullptr;
+    int* counters = nullptr;
     size_t off = 0;
     if (params->smooth_k) {
-        // channel sums of K per token chunk (binary64); the INT8 quantizer
-        // finishes the mean itself, the MXFP4 path in a separate step
+        // K channel sums per token chunk (binary64), the mean, arrival flags
         partial = (double*)(ws + off);
         off += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * s.D * sizeof(double));
         mu = k_mean ? (float*)k_mean->data : (float*)(ws + off);
         off += align256((size_t)s.B * s.H * s.D * sizeof(float));
-        hipError_t e = sage::launch_k_mean_partial(kv, s.B, s.H, s.Lk, s.D, partial, strm);
-        if (e != hipSuccess) return launch_status(e, "k mean");
+        counters = (int*)(ws + off);
+        off += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * sizeof(int32_t));
     }
     hipError_t e;
     if (params->mode == SAGE_QK_INT8) {
-        e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->k_block, partial,
+        e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->k_block,
+                                       params->smooth_k != 0, partial, counters,
                                        k_mean ? (float*)k_mean->data : nullptr, (int8_t*)q_out->data,
                                        (float*)q_scale->data, (int8_t*)k_out->data,
                                        (float*)k_scale->data, strm);
     } else {
         if (partial) {
+            e = sage::launch_k_mean_partial(kv, s.B, s.H, s.Lk, s.D, partial, strm);
+            if (e != hipSuccess) return launch_status(e, "k mean");
             e = sage::launch_k_mean_final(partial, s.B, s.H, s.Lk, s.D, mu, strm);
             if (e != hipSuccess) return launch_status(e, "k mean");
         }
@@ -323,8 +333,7 @@ sage_status sage_quantize_v_workspace_size(const sage_tensor* v, size_t* bytes) 
     sage_status st = check_half_view(v, "v");
     if (st) return st;
     if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes: null");
-    *bytes = align256((size_t)v->shape[0] * v->shape[2] * sage::mean_chunks((int)v->shape[1]) *
-                      v->shape[3] * sizeof(float));
+    *bytes = v_ws_bytes((int)v->shape[0], (int)v->shape[1], (int)v->shape[2], (int)v->shape[3]);
     return ok();
 }
 
@@ -338,13 +347,15 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out, cons
     const int64_t os[4] = {B, H, D, sage::pad128(Lk)}, ss[3] = {B, H, D};
     if ((st = check_exact(v_out, "v_out", SAGE_FP8_E4M3FN, 4, os))) return st;
     if ((st = check_exact(v_scale, "v_scale", SAGE_F32, 3, ss))) return st;
-    const size_t need = align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float));
+    const size_t need = v_ws_bytes(B, Lk, H, D);
     if (!workspace || workspace_bytes < need)
         return fail(SAGE_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(SAGE_ERR_ALIGNMENT, "workspace not 16-byte aligned");
     if ((st = check_device())) return st;
+    const size_t partial_bytes = align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float));
     hipError_t e = sage::launch_quant_v(half_view(v), B, H, Lk, D, (float*)workspace,
+                                        (int*)((char*)workspace + partial_bytes),
                                         (uint8_t*)v_out->data, (float*)v_scale->data,
                                         (hipStream_t)stream);
     return launch_status(e, "quantize v");

@@ -160,13 +160,6 @@ struct TileDma {
     }
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    // raw buffer, stride 0, bounds = bytes; dword 3 = gfx9 raw-buffer config
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
-                                             0x00020000);
-}
-
 __device__ __forceinline__ void wait_dma() {
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's LDS DMA has landed
 }

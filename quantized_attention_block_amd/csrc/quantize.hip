@@ -15,6 +15,10 @@
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #pragma clang fp contract(off)
 
 namespace sage {
@@ -132,8 +136,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
                                                          const double* mean_partial, int nchunk,
                                                          float* mu_out, int8_t* q_out,
                                                          float* q_scale, int8_t* k_out,
-                                                         float* k_scale) {
+                                                         float* k_scale, int* zero, int nzero) {
     using G = Rows16<D>;
+    // clears the arrival flags of the single-read K quantizer launched next
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < nzero; i += kThreads) zero[i] = 0;
     const bool isq = (int)blockIdx.y < nqb;
     const int blk = isq ? blockIdx.y : blockIdx.y - nqb;   // 128-row block
     const int L = isq ? Lq : Lk;
@@ -349,6 +356,330 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
     }
 }
 
+// ---- single-read K and V quantizers -----------------------------------------
+// When every block of the grid can be resident at once, K (and V) are read
+// from HBM once instead of twice: a block holds one 256-token chunk of one head
+// in registers, publishes that chunk's channel sums (K) or channel amax (V),
+// waits for the other chunks of its head, finishes the statistic and
+// quantizes the rows it holds.  The chunk results are the numbers the
+// two-kernel path computes (k_mean_partial / k_v_amax: same chunks, same
+// summation order), so both paths give identical outputs.  The blocks of a
+// head meet at arrival flags in the workspace, cleared by the launch before;
+// the host takes this path only when the whole grid fits on the device at
+// once, so every block a flag waits for is running, and the wait is bounded
+// regardless.
+constexpr int kMaxSpin = 1 << 20;   // polls (~1 us each) before giving up
+//
+// Every value exchanged between blocks (chunk results, flags) is read and
+// written with device-scope atomic accesses, which are coherent across the
+// XCDs' L2 caches by themselves; a full release/acquire fence would instead
+// write back and invalidate a whole L2 per block, which serializes (measured:
+// ~250 us per kernel).  A writer waits for its stores to complete before the
+// block's arrival is counted.
+template <typename T>
+__device__ __forceinline__ void publish(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T fetch(const T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// op-fold of p[0], p[stride], ..., p[(n - 1) stride] in index order, eight
+// loads in flight at a time
+template <typename T, typename Op>
+__device__ __forceinline__ T fold_published(const T* p, int64_t stride, int n, T acc, Op op) {
+    int c = 0;
+    for (; c + 8 <= n; c += 8) {
+        T v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = fetch(p + (c + j) * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = op(acc, v[j]);
+    }
+    for (; c < n; ++c) acc = op(acc, fetch(p + c * stride));
+    return acc;
+}
+
+// Arrival flags, one word per chunk of a head: a block's chunk results are
+// complete (its own stores acknowledged) before it sets its flag, and a block
+// leaves when every flag of its head is set.  Separate words rather than one
+// counter: device-scope read-modify-writes of one address serialize (16
+// arrivals on one counter took ~12 us).
+__device__ __forceinline__ void head_barrier(int* flags, int chunk, int nchunk) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's published stores completed
+    __syncthreads();
+    if (threadIdx.x == 0) publish(flags + chunk, 1);
+    if (threadIdx.x < 64) {   // wave 0 polls, one flag per lane and pass
+        for (int i = 0; i < kMaxSpin; ++i) {
+            int missing = 0;
+            for (int c = threadIdx.x; c < nchunk; c += 64) missing |= fetch(flags + c) == 0;
+            if (!__any(missing)) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    __syncthreads();
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8t(const uint4& u, float out[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = BF16 ? bf16_bits_to_f32(w[i] & 0xFFFF) : f16_bits_to_f32(w[i] & 0xFFFF);
+        out[2 * i + 1] = BF16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
+    }
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+
+// INT8 smoothed K.  Grid (B*H, chunks of 256 tokens); a thread owns channels
+// [8 c8, +8) of rows r0 + kRowsPerPass p.  Rows are read through a buffer
+// resource that ends with row L - 1, so rows past L read as zeros.
+// Quantization blocks (k_block 64 or 128 rows) lie inside a chunk; rows past
+// L get code 0, rows past pad128(L) are not written.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_k_fused(
+    HalfView k, int H, int L, int k_block, int nchunk, double* partial, int* cnt, float* mu_out,
+    int8_t* k_out, float* k_scale) {
+    using G = Rows<D>;
+    constexpr int kPasses = kMeanChunk / G::kRowsPerPass;   // 16 (D 128) or 8 (D 64)
+    constexpr int kPer64 = 64 / G::kRowsPerPass;            // passes per 64-row block
+    constexpr int kB64 = kMeanChunk / 64;                   // 64-row blocks per chunk
+    const int bh = blockIdx.x, b = bh / H, h = bh % H, chunk = blockIdx.y;
+    const int c8 = threadIdx.x % G::kLanesPerRow, r0 = threadIdx.x / G::kLanesPerRow;
+    const int row0 = chunk * kMeanChunk;
+    const int Lp = pad128(L);
+
+    uint4 raw[kPasses];
+    {
+        const uint16_t* head = (const uint16_t*)k.ptr + (int64_t)b * k.sB + (int64_t)h * k.sH;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(L - 1) * k.sL + D) * 2);
+        const int off = (int)(((int64_t)(row0 + r0) * k.sL + 8 * c8) * 2);
+        const int step = (int)(G::kRowsPerPass * k.sL * 2);
+        // four passes in flight at a time: with every block of the grid
+        // loading at once, unthrottled requests left some blocks waiting ~3x
+        // longer than the median for their rows
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            raw[p] = load16(rs, off + p * step);
+            if (p % 4 == 3 && p + 1 < kPasses) __builtin_amdgcn_s_waitcnt(0x3f70);
+        }
+    }
+
+    // chunk channel sums in binary64: rows ascending per thread, then the
+    // threads of a channel in row order (zero rows add nothing)
+    __shared__ double sm[kThreads][8 + 1];
+    {
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            float x[8];
+            unpack8t<BF16>(raw[p], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm[threadIdx.x][i] = acc[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        double s = 0.0;
+        for (int r = 0; r < G::kRowsPerPass; ++r) s += sm[r * G::kLanesPerRow + d / 8][d % 8];
+        publish(&partial[((int64_t)bh * nchunk + chunk) * D + d], s);
+    }
+    // conversions are redone after the barrier rather than kept live across it
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
+    head_barrier(cnt + (int64_t)bh * nchunk, chunk, nchunk);
+
+    __shared__ float mu_s[D];
+    __shared__ float red[kThreads / 64][kB64];
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        const double acc = fold_published(partial + (int64_t)bh * nchunk * D + d, (int64_t)D, nchunk, 0.0,
+                                          [](double x, double y) { return x + y; });
+        const float m = L > 0 ? (float)(acc / (double)L) : 0.0f;
+        mu_s[d] = m;
+        if (chunk == 0 && mu_out) mu_out[(int64_t)bh * D + d] = m;
+    }
+    __syncthreads();
+    float mu8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mu8[i] = mu_s[8 * c8 + i];
+
+    // amax of fp32(K - mu) per 64-row block (a 128-row block is two of them)
+    float am[kB64];
+#pragma unroll
+    for (int j = 0; j < kB64; ++j) am[j] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        float x[8];
+        unpack8t<BF16>(raw[p], x);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i] - mu8[i]));
+        if (row0 + p * G::kRowsPerPass + r0 < L) am[p / kPer64] = fmaxf(am[p / kPer64], m);
+    }
+#pragma unroll
+    for (int j = 0; j < kB64; ++j) am[j] = wave_max(am[j]);
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int j = 0; j < kB64; ++j) red[threadIdx.x / 64][j] = am[j];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
+    __syncthreads();
+    float ba[kB64];   // amax of the quantization block holding 64-row block j
+    {
+        float bm[kB64];
+#pragma unroll
+        for (int j = 0; j < kB64; ++j) {
+            bm[j] = red[0][j];
+#pragma unroll
+            for (int w = 1; w < kThreads / 64; ++w) bm[j] = fmaxf(bm[j], red[w][j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kB64; ++j) ba[j] = k_block == 64 ? bm[j] : fmaxf(bm[j & ~1], bm[j | 1]);
+    }
+
+    const __amdgpu_buffer_rsrc_t os = make_rsrc(k_out + (int64_t)bh * Lp * D, (int64_t)Lp * D);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int row = row0 + p * G::kRowsPerPass + r0;
+        const float a = ba[p / kPer64];
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        float x[8];
+        unpack8t<BF16>(raw[p], x);
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = __builtin_rintf((x[i] - mu8[i]) * inv);
+            r = fminf(127.0f, fmaxf(-127.0f, r));
+            if (row >= L) r = 0.0f;
+            w[i / 4] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i % 4));
+        }
+        // rows past pad128(L) fall outside the resource and are dropped
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_uint2(w[0], w[1])),
+                                              os, row * D + 8 * c8, 0, 0);
+    }
+    if (threadIdx.x == 0) {
+        const int nsc = Lp / k_block;
+#pragma unroll
+        for (int j = 0; j < kB64; ++j) {
+            if (k_block == 128 && (j & 1)) continue;
+            const int idx = (row0 + 64 * j) / k_block;
+            if (idx < nsc) k_scale[(int64_t)bh * nsc + idx] = ba[j] > 0.0f ? ba[j] / 127.0f : 0.0f;
+        }
+    }
+}
+
+__global__ void k_zero_i32(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// V: one block per 256 keys of one head; chunk channel amax, head barrier,
+// amax over the chunks, then e4m3 codes transposed through an LDS tile
+// [D][256 keys] (as in k_v_quant: per channel, 4 keys' codes packed per
+// dword; 16-byte chunks XOR-swizzled by row) written as V^T rows.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_v_fused(
+    HalfView v, int H, int L, int nchunk, float* partial, int* cnt, uint8_t* v_out, float* v_scale) {
+    constexpr int kKeys = kMeanChunk;                      // 256
+    constexpr int kGroups = D / 8;                         // 8-channel groups
+    constexpr int kKeyGroups = kThreads / kGroups;         // 4-key groups per pass (16 or 32)
+    constexpr int kPasses = kKeys / (4 * kKeyGroups);      // 4 or 2
+    const int bh = blockIdx.x, b = bh / H, h = bh % H, chunk = blockIdx.y;
+    const int k0 = chunk * kKeys;
+    const int Lp = pad128(L);
+    const int c8 = threadIdx.x % kGroups, kg0 = threadIdx.x / kGroups;
+
+    uint4 raw[kPasses][4];   // keys k0 + 4 (p kKeyGroups + kg0) + j
+    {
+        const uint16_t* head = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)h * v.sH;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(L - 1) * v.sL + D) * 2);
+        const int off = (int)(((int64_t)(k0 + 4 * kg0) * v.sL + 8 * c8) * 2);
+        const int sk = (int)(v.sL * 2), sp = (int)(4 * kKeyGroups * v.sL * 2);
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw[p][j] = load16(rs, off + p * sp + j * sk);
+            if (p + 1 < kPasses) __builtin_amdgcn_s_waitcnt(0x3f70);   // four rows in flight (see K)
+        }
+    }
+
+    // LDS: the chunk-amax exchange, later the transpose tile
+    constexpr int kTileWords = D * kKeys / 4;
+    constexpr int kRedWords = kThreads * 9;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kTileWords > kRedWords ? kTileWords : kRedWords];
+    float(*sm)[9] = (float(*)[9])lds;
+    {
+        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x[8];
+                unpack8t<BF16>(raw[p][j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(x[i]));
+            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm[threadIdx.x][i] = m[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        float r = 0.0f;
+        for (int g = 0; g < kKeyGroups; ++g) r = fmaxf(r, sm[g * kGroups + d / 8][d % 8]);
+        publish(&partial[((int64_t)bh * nchunk + chunk) * D + d], r);
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm("" : "+v"(raw[p][j].x), "+v"(raw[p][j].y), "+v"(raw[p][j].z), "+v"(raw[p][j].w));
+    head_barrier(cnt + (int64_t)bh * nchunk, chunk, nchunk);
+
+    __shared__ float inv_s[D];
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        const float a = fold_published(partial + (int64_t)bh * nchunk * D + d, (int64_t)D, nchunk, 0.0f,
+                                       [](float x, float y) { return fmaxf(x, y); });
+        inv_s[d] = a > 0.0f ? kFp8Max / a : 0.0f;
+        if (chunk == 0) v_scale[(int64_t)bh * D + d] = a / kFp8Max;
+    }
+    __syncthreads();
+    float inv8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) inv8[i] = inv_s[8 * c8 + i];
+    auto word = [](int d, int kg) { return d * (kKeys / 4) + 4 * ((kg >> 2) ^ ((d >> 3) & 7)) + (kg & 3); };
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int kg = p * kKeyGroups + kg0;
+        float x[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) unpack8t<BF16>(raw[p][j], x[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t c = cvt_pk_fp8<false>(x[0][i] * inv8[i], x[1][i] * inv8[i], 0);
+            c = cvt_pk_fp8<true>(x[2][i] * inv8[i], x[3][i] * inv8[i], c);
+            lds[word(8 * c8 + i, kg)] = c;
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < D * (kKeys / 16); c += kThreads) {
+        const int d = c / (kKeys / 16), j = c % (kKeys / 16);
+        const int key = k0 + 16 * j;
+        if (key < Lp) {
+            const uint4 val = *(const uint4*)&lds[word(d, 4 * j)];
+            *(uint4*)(v_out + ((int64_t)bh * D + d) * Lp + key) = val;
+        }
+    }
+}
+
 // ---- MXFP4 -------------------------------------------------------------------
 // mu * H per (b, h) in fp32 (channel-ascending sums), so that the rotated
 // smoothed key is rot(K) - rot(mu).
@@ -474,6 +805,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
 
 }  // namespace
 
+// Blocks of kThreads threads of `kernel` the current device holds at once (0
+// if unknown); cached per device and kernel.
+static int resident_blocks(const void* kernel) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, kernel);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    int n = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) == hipSuccess)
+        n = cus * per_cu;
+    cache.emplace(key, n);
+    return n;
+}
+
+// The single-read path: the grid fits on the device at once, token rows do not
+// overlap (sL >= D, so rows past L fall outside the buffer resource) and byte
+// offsets within one head fit in 32 bits.
+static bool single_read_ok(const HalfView& x, int L, int D, int64_t blocks, const void* kernel) {
+    if (x.sL < D || (int64_t)(pad128(L) + kMeanChunk) * x.sL * 2 >= 0x7FFFFFFF) return false;
+    return blocks <= resident_blocks(kernel);
+}
+
 hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, double* partial,
                                  hipStream_t stream) {
     const int nchunk = mean_chunks(L);
@@ -496,25 +855,47 @@ hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D
 }
 
 hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
-                                int Lk, int D, int k_block, const double* mean_partial,
-                                float* mu_out, int8_t* q_out, float* q_scale, int8_t* k_out,
-                                float* k_scale, hipStream_t stream) {
+                                int Lk, int D, int k_block, bool smooth, double* mean_partial,
+                                int* counters, float* mu_out, int8_t* q_out, float* q_scale,
+                                int8_t* k_out, float* k_scale, hipStream_t stream) {
     const int nqb = pad128(Lq) / 128, nkb = pad128(Lk) / 128;
     const int nchunk = mean_chunks(Lk);
-    dim3 grid(B * H, nqb + nkb);
-    if (D == 128)
-        k_quant_int8<128><<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb, mean_partial,
-                                                             nchunk, mu_out, q_out, q_scale, k_out, k_scale);
-    else
-        k_quant_int8<64><<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb, mean_partial,
-                                                            nchunk, mu_out, q_out, q_scale, k_out, k_scale);
+    const int BH = B * H;
+    auto quant = D == 128 ? k_quant_int8<128> : k_quant_int8<64>;
+    if (smooth) {
+        auto kfused = D == 128 ? (k.bf16 ? k_quant_k_fused<128, true> : k_quant_k_fused<128, false>)
+                               : (k.bf16 ? k_quant_k_fused<64, true> : k_quant_k_fused<64, false>);
+        if (single_read_ok(k, Lk, D, BH * nchunk, (const void*)kfused)) {
+            // Q blocks (clearing the flags), then K read once
+            quant<<<dim3(BH, nqb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb, nullptr, nchunk,
+                                                          nullptr, q_out, q_scale, nullptr, nullptr,
+                                                          counters, BH * nchunk);
+            kfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(k, H, Lk, k_block, nchunk, mean_partial,
+                                                              counters, mu_out, k_out, k_scale);
+            return hipGetLastError();
+        }
+        const hipError_t e = launch_k_mean_partial(k, B, H, Lk, D, mean_partial, stream);
+        if (e != hipSuccess) return e;
+    }
+    quant<<<dim3(BH, nqb + nkb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb,
+                                                        smooth ? mean_partial : nullptr, nchunk, mu_out,
+                                                        q_out, q_scale, k_out, k_scale, nullptr, 0);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
-                          uint8_t* v_out, float* v_scale, hipStream_t stream) {
+                          int* counters, uint8_t* v_out, float* v_scale, hipStream_t stream) {
     const int nchunk = mean_chunks(Lk);
-    dim3 g1(B * H, nchunk), g2(B * H, pad128(Lk) / 128);
+    const int BH = B * H;
+    auto vfused = D == 128 ? (v.bf16 ? k_quant_v_fused<128, true> : k_quant_v_fused<128, false>)
+                           : (v.bf16 ? k_quant_v_fused<64, true> : k_quant_v_fused<64, false>);
+    if (single_read_ok(v, Lk, D, BH * nchunk, (const void*)vfused)) {
+        k_zero_i32<<<1, kThreads, 0, stream>>>(counters, BH * nchunk);
+        vfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, counters,
+                                                          v_out, v_scale);
+        return hipGetLastError();
+    }
+    dim3 g1(BH, nchunk), g2(BH, pad128(Lk) / 128);
     if (D == 128) {
         k_v_amax<128><<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial);
         k_v_quant<128><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out, v_scale);

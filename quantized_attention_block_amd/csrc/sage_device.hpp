@@ -110,6 +110,14 @@ __device__ __forceinline__ float half_pair_max(float v) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Raw buffer resource over [base, base + bytes): stride 0, loads past the end
+// return 0 and stores past it are dropped (bounds clamped to 2^31 - 1).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                             0x00020000);   // gfx9 raw-buffer config
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

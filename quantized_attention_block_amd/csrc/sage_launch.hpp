@@ -38,18 +38,20 @@ hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, 
 hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D, float* mu,
                                hipStream_t stream);
 
-// INT8 block quantization of Q (128-row blocks) and smoothed K (k_block rows,
-// 64 or 128), finishing the K mean from mean_partial (NULL: no smoothing)
-// and writing it to mu_out (may be NULL).
+// INT8 block quantization of Q (128-row blocks) and K (k_block rows, 64 or
+// 128), K smoothed by its channel mean when `smooth` (written to mu_out when
+// not NULL).  Scratch: mean_partial fp64 [B*H, mean_chunks(Lk), D] and
+// counters int32 [B*H, mean_chunks(Lk)] (arrival flags; used when smooth).
 hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
-                                int Lk, int D, int k_block, const double* mean_partial,
-                                float* mu_out, int8_t* q_out, float* q_scale, int8_t* k_out,
-                                float* k_scale, hipStream_t stream);
+                                int Lk, int D, int k_block, bool smooth, double* mean_partial,
+                                int* counters, float* mu_out, int8_t* q_out, float* q_scale,
+                                int8_t* k_out, float* k_scale, hipStream_t stream);
 
-// V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales;
-// amax_partial: fp32 [B*H, mean_chunks(Lk), D] scratch.
+// V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales.
+// Scratch: amax_partial fp32 [B*H, mean_chunks(Lk), D], counters int32
+// [B*H, mean_chunks(Lk)] (arrival flags).
 hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
-                          uint8_t* v_out, float* v_scale, hipStream_t stream);
+                          int* counters, uint8_t* v_out, float* v_scale, hipStream_t stream);
 
 // Hadamard rotation (optional) + MXFP4 quantization of Q and smoothed K.
 // hadamard_bf16 / hadamard_f16: 128x128 +-1 matrices (NULL: no rotation);
