@@ -199,16 +199,16 @@ size_t qk_ws_bytes(const QkShape& s, const sage_qk_params* p) {
     if (p->smooth_k) {
         n += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * s.D * sizeof(double));
         n += align256((size_t)s.B * s.H * s.D * sizeof(float));   // mu when k_mean is NULL
-        n += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * sizeof(int32_t));   // arrival flags
+        n += align256((size_t)sage::quant_sync_words((int64_t)s.B * s.H, s.Lk) * sizeof(uint64_t));
     }
     if (p->mode == SAGE_QK_MXFP4) n += align256((size_t)s.B * s.H * s.D * sizeof(float));
     return n;
 }
 
-// V: channel amax per token chunk (fp32), then one arrival flag per chunk
+// V: channel amax per token chunk (fp32), then the head-synchronization words
 size_t v_ws_bytes(int B, int Lk, int H, int D) {
     return align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float)) +
-           align256((size_t)B * H * sage::mean_chunks(Lk) * sizeof(int32_t));
+           align256((size_t)sage::quant_sync_words((int64_t)B * H, Lk) * sizeof(uint64_t));
 }
 
 }  // namespace
@@ -294,21 +294,21 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
     const sage::HalfView qv = half_view(q), kv = half_view(k);
     float* mu = nullptr;
     double* partial = nullptr;
-    int* counters = nullptr;
+    uint64_t* sync = nullptr;
     size_t off = 0;
     if (params->smooth_k) {
-        // K channel sums per token chunk (binary64), the mean, arrival flags
+        // K channel sums per token chunk (binary64), the mean, head-sync words
         partial = (double*)(ws + off);
         off += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * s.D * sizeof(double));
         mu = k_mean ? (float*)k_mean->data : (float*)(ws + off);
         off += align256((size_t)s.B * s.H * s.D * sizeof(float));
-        counters = (int*)(ws + off);
-        off += align256((size_t)s.B * s.H * sage::mean_chunks(s.Lk) * sizeof(int32_t));
+        sync = (uint64_t*)(ws + off);
+        off += align256((size_t)sage::quant_sync_words((int64_t)s.B * s.H, s.Lk) * sizeof(uint64_t));
     }
     hipError_t e;
     if (params->mode == SAGE_QK_INT8) {
         e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->k_block,
-                                       params->smooth_k != 0, partial, counters,
+                                       params->smooth_k != 0, partial, sync,
                                        k_mean ? (float*)k_mean->data : nullptr, (int8_t*)q_out->data,
                                        (float*)q_scale->data, (int8_t*)k_out->data,
                                        (float*)k_scale->data, strm);
@@ -355,7 +355,7 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out, cons
     if ((st = check_device())) return st;
     const size_t partial_bytes = align256((size_t)B * H * sage::mean_chunks(Lk) * D * sizeof(float));
     hipError_t e = sage::launch_quant_v(half_view(v), B, H, Lk, D, (float*)workspace,
-                                        (int*)((char*)workspace + partial_bytes),
+                                        (uint64_t*)((char*)workspace + partial_bytes),
                                         (uint8_t*)v_out->data, (float*)v_scale->data,
                                         (hipStream_t)stream);
     return launch_status(e, "quantize v");

@@ -136,11 +136,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
                                                          const double* mean_partial, int nchunk,
                                                          float* mu_out, int8_t* q_out,
                                                          float* q_scale, int8_t* k_out,
-                                                         float* k_scale, int* zero, int nzero) {
+                                                         float* k_scale) {
     using G = Rows16<D>;
-    // clears the arrival flags of the single-read K quantizer launched next
-    if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = threadIdx.x; i < nzero; i += kThreads) zero[i] = 0;
     const bool isq = (int)blockIdx.y < nqb;
     const int blk = isq ? blockIdx.y : blockIdx.y - nqb;   // 128-row block
     const int L = isq ? Lq : Lk;
@@ -363,19 +360,17 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
 // waits for the other chunks of its head, finishes the statistic and
 // quantizes the rows it holds.  The chunk results are the numbers the
 // two-kernel path computes (k_mean_partial / k_v_amax: same chunks, same
-// summation order), so both paths give identical outputs.  The blocks of a
-// head meet at arrival flags in the workspace, cleared by the launch before;
-// the host takes this path only when the whole grid fits on the device at
-// once, so every block a flag waits for is running, and the wait is bounded
-// regardless.
+// summation order), so both paths give identical outputs.  The host takes
+// this path only when the whole grid fits on the device at once, so every
+// block a head waits for is running; the wait is bounded regardless.
 constexpr int kMaxSpin = 1 << 20;   // polls (~1 us each) before giving up
-//
-// Every value exchanged between blocks (chunk results, flags) is read and
-// written with device-scope atomic accesses, which are coherent across the
-// XCDs' L2 caches by themselves; a full release/acquire fence would instead
-// write back and invalidate a whole L2 per block, which serializes (measured:
-// ~250 us per kernel).  A writer waits for its stores to complete before the
-// block's arrival is counted.
+
+// Every value exchanged between blocks (chunk results, flags, epochs) is read
+// and written with device-scope atomic accesses, which are coherent across
+// the XCDs' L2 caches by themselves; a full release/acquire fence would
+// instead write back and invalidate a whole L2 per block, which serializes
+// (measured: ~250 us per kernel).  A writer waits for its stores to complete
+// before its arrival is published.
 template <typename T>
 __device__ __forceinline__ void publish(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -401,24 +396,44 @@ __device__ __forceinline__ T fold_published(const T* p, int64_t stride, int n, T
     return acc;
 }
 
-// Arrival flags, one word per chunk of a head: a block's chunk results are
-// complete (its own stores acknowledged) before it sets its flag, and a block
-// leaves when every flag of its head is set.  Separate words rather than one
+// Meeting point of the chunks of one head, with no clearing launch.  The
+// blocks read the head's epoch word e when they start; each publishes, on its
+// chunk's flag, the token of e + 1 once its chunk results are complete, and
+// leaves when every flag of the head holds that token; the head's first chunk
+// then stores e + 1.  A token also encodes the chunk count, so flags left by
+// an earlier call -- same layout, one epoch behind, or another layout -- never
+// match, and the workspace needs no initialization (a stale or garbage 64-bit
+// word equals the token only by chance).  Separate flags rather than one
 // counter: device-scope read-modify-writes of one address serialize (16
 // arrivals on one counter took ~12 us).
-__device__ __forceinline__ void head_barrier(int* flags, int chunk, int nchunk) {
+struct HeadSync {
+    uint64_t* flags;   // [B*H, nchunk]
+    uint64_t* epoch;   // [B*H]
+};
+
+__device__ __forceinline__ uint64_t head_token(uint64_t e, int nchunk) {
+    return ((e + 1) << 32) | (0x9E3779B9u ^ (uint32_t)nchunk);
+}
+
+__device__ __forceinline__ void head_arrive(const HeadSync& hs, int bh, int chunk, int nchunk, uint64_t token) {
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's published stores completed
     __syncthreads();
-    if (threadIdx.x == 0) publish(flags + chunk, 1);
+    if (threadIdx.x == 0) publish(hs.flags + (int64_t)bh * nchunk + chunk, token);
+}
+
+__device__ __forceinline__ void head_wait(const HeadSync& hs, int bh, int chunk, int nchunk, uint64_t e,
+                                          uint64_t token) {
     if (threadIdx.x < 64) {   // wave 0 polls, one flag per lane and pass
+        const uint64_t* f = hs.flags + (int64_t)bh * nchunk;
         for (int i = 0; i < kMaxSpin; ++i) {
             int missing = 0;
-            for (int c = threadIdx.x; c < nchunk; c += 64) missing |= fetch(flags + c) == 0;
+            for (int c = threadIdx.x; c < nchunk; c += 64) missing |= fetch(f + c) != token;
             if (!__any(missing)) break;
             __builtin_amdgcn_s_sleep(4);
         }
     }
     __syncthreads();
+    if (chunk == 0 && threadIdx.x == 0) publish(hs.epoch + bh, e + 1);
 }
 
 template <bool BF16>
@@ -435,15 +450,78 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
 }
 
-// INT8 smoothed K.  Grid (B*H, chunks of 256 tokens); a thread owns channels
-// [8 c8, +8) of rows r0 + kRowsPerPass p.  Rows are read through a buffer
-// resource that ends with row L - 1, so rows past L read as zeros.
-// Quantization blocks (k_block 64 or 128 rows) lie inside a chunk; rows past
-// L get code 0, rows past pad128(L) are not written.
+// One 128-row INT8 block of Q: amax over the valid rows, scale amax / 127,
+// codes clamp(rne(x * (127 / amax)), -127, 127), padded rows code 0 (the
+// arithmetic of k_quant_int8's Q blocks).  A thread owns channels [8 c8, +8)
+// of rows r0 + kRowsPerPass p; rows are read through a buffer resource that
+// ends with row L - 1 (rows past L read as zeros).  red: LDS [4] floats.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_k_fused(
-    HalfView k, int H, int L, int k_block, int nchunk, double* partial, int* cnt, float* mu_out,
-    int8_t* k_out, float* k_scale) {
+__device__ __forceinline__ void quant_q_block(const HalfView& q, int b, int h, int bh, int blk, int L,
+                                              int8_t* q_out, float* q_scale, float* red) {
+    using G = Rows<D>;
+    constexpr int kPasses = 128 / G::kRowsPerPass;   // 8 (D 128) or 4 (D 64)
+    const int c8 = threadIdx.x % G::kLanesPerRow, r0 = threadIdx.x / G::kLanesPerRow;
+    const int row0 = blk * 128, Lp = pad128(L);
+    uint4 raw[kPasses];
+    {
+        const uint16_t* head = (const uint16_t*)q.ptr + (int64_t)b * q.sB + (int64_t)h * q.sH;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(L - 1) * q.sL + D) * 2);
+        const int off = (int)(((int64_t)(row0 + r0) * q.sL + 8 * c8) * 2);
+        const int step = (int)(G::kRowsPerPass * q.sL * 2);
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) raw[p] = load16(rs, off + p * step);
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        float x[8];
+        unpack8t<BF16>(raw[p], x);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+        if (row0 + p * G::kRowsPerPass + r0 < L) am = fmaxf(am, m);
+    }
+    am = wave_max(am);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = am;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
+    __syncthreads();
+    float amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const __amdgpu_buffer_rsrc_t os = make_rsrc(q_out + (int64_t)bh * Lp * D, (int64_t)Lp * D);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int row = row0 + p * G::kRowsPerPass + r0;
+        float x[8];
+        unpack8t<BF16>(raw[p], x);
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = __builtin_rintf(x[i] * inv);
+            r = fminf(127.0f, fmaxf(-127.0f, r));
+            if (row >= L) r = 0.0f;
+            w[i / 4] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i % 4));
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
+                                                                 make_uint2(w[0], w[1])),
+                                              os, row * D + 8 * c8, 0, 0);
+    }
+    if (threadIdx.x == 0) q_scale[(int64_t)bh * (Lp / 128) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    __syncthreads();   // red is reused
+}
+
+// INT8 Q and smoothed K in one launch.  Grid (B*H, chunks of 256 K tokens);
+// block (bh, c) holds K chunk c of head bh and also quantizes the Q blocks
+// c, c + nchunk, ... of that head between publishing its chunk sums and
+// waiting for the other chunks.  For K a thread owns channels [8 c8, +8) of
+// rows r0 + kRowsPerPass p.  Quantization blocks (k_block 64 or 128 rows) lie
+// inside a chunk; rows past L get code 0, rows past pad128(L) are not written.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_qk_fused(
+    HalfView q, HalfView k, int H, int Lq, int L, int k_block, int nchunk, double* partial, HeadSync hs,
+    float* mu_out, int8_t* q_out, float* q_scale, int8_t* k_out, float* k_scale) {
     using G = Rows<D>;
     constexpr int kPasses = kMeanChunk / G::kRowsPerPass;   // 16 (D 128) or 8 (D 64)
     constexpr int kPer64 = 64 / G::kRowsPerPass;            // passes per 64-row block
@@ -452,6 +530,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int c8 = threadIdx.x % G::kLanesPerRow, r0 = threadIdx.x / G::kLanesPerRow;
     const int row0 = chunk * kMeanChunk;
     const int Lp = pad128(L);
+    const uint64_t e = fetch(hs.epoch + bh);
+    const uint64_t token = head_token(e, nchunk);
 
     uint4 raw[kPasses];
     {
@@ -491,13 +571,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int r = 0; r < G::kRowsPerPass; ++r) s += sm[r * G::kLanesPerRow + d / 8][d % 8];
         publish(&partial[((int64_t)bh * nchunk + chunk) * D + d], s);
     }
-    // conversions are redone after the barrier rather than kept live across it
+    // conversions are redone after the wait rather than kept live across it
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
-    head_barrier(cnt + (int64_t)bh * nchunk, chunk, nchunk);
+    head_arrive(hs, bh, chunk, nchunk, token);
+
+    __shared__ float red[kThreads / 64][kB64];
+    const int nqb = pad128(Lq) / 128;
+    for (int qb = chunk; qb < nqb; qb += nchunk)
+        quant_q_block<D, BF16>(q, b, h, bh, qb, Lq, q_out, q_scale, &red[0][0]);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
+    head_wait(hs, bh, chunk, nchunk, e, token);
 
     __shared__ float mu_s[D];
-    __shared__ float red[kThreads / 64][kB64];
     if (threadIdx.x < D) {
         const int d = threadIdx.x;
         const double acc = fold_published(partial + (int64_t)bh * nchunk * D + d, (int64_t)D, nchunk, 0.0,
@@ -562,7 +649,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             w[i / 4] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i % 4));
         }
         // rows past pad128(L) fall outside the resource and are dropped
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_uint2(w[0], w[1])),
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
+                                                                 make_uint2(w[0], w[1])),
                                               os, row * D + 8 * c8, 0, 0);
     }
     if (threadIdx.x == 0) {
@@ -576,17 +664,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 }
 
-__global__ void k_zero_i32(int* p, int n) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
-
 // V: one block per 256 keys of one head; chunk channel amax, head barrier,
 // amax over the chunks, then e4m3 codes transposed through an LDS tile
 // [D][256 keys] (as in k_v_quant: per channel, 4 keys' codes packed per
 // dword; 16-byte chunks XOR-swizzled by row) written as V^T rows.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_v_fused(
-    HalfView v, int H, int L, int nchunk, float* partial, int* cnt, uint8_t* v_out, float* v_scale) {
+    HalfView v, int H, int L, int nchunk, float* partial, HeadSync hs, uint8_t* v_out, float* v_scale) {
     constexpr int kKeys = kMeanChunk;                      // 256
     constexpr int kGroups = D / 8;                         // 8-channel groups
     constexpr int kKeyGroups = kThreads / kGroups;         // 4-key groups per pass (16 or 32)
@@ -595,6 +679,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int k0 = chunk * kKeys;
     const int Lp = pad128(L);
     const int c8 = threadIdx.x % kGroups, kg0 = threadIdx.x / kGroups;
+    const uint64_t e = fetch(hs.epoch + bh);
+    const uint64_t token = head_token(e, nchunk);
 
     uint4 raw[kPasses][4];   // keys k0 + 4 (p kKeyGroups + kg0) + j
     {
@@ -641,7 +727,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             asm("" : "+v"(raw[p][j].x), "+v"(raw[p][j].y), "+v"(raw[p][j].z), "+v"(raw[p][j].w));
-    head_barrier(cnt + (int64_t)bh * nchunk, chunk, nchunk);
+    head_arrive(hs, bh, chunk, nchunk, token);
+    head_wait(hs, bh, chunk, nchunk, e, token);
 
     __shared__ float inv_s[D];
     if (threadIdx.x < D) {
@@ -830,7 +917,7 @@ static int resident_blocks(const void* kernel) {
 // offsets within one head fit in 32 bits.
 static bool single_read_ok(const HalfView& x, int L, int D, int64_t blocks, const void* kernel) {
     if (x.sL < D || (int64_t)(pad128(L) + kMeanChunk) * x.sL * 2 >= 0x7FFFFFFF) return false;
-    return blocks <= resident_blocks(kernel);
+    return kernel == nullptr || blocks <= resident_blocks(kernel);
 }
 
 hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, double* partial,
@@ -856,43 +943,41 @@ hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D
 
 hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
                                 int Lk, int D, int k_block, bool smooth, double* mean_partial,
-                                int* counters, float* mu_out, int8_t* q_out, float* q_scale,
+                                uint64_t* sync, float* mu_out, int8_t* q_out, float* q_scale,
                                 int8_t* k_out, float* k_scale, hipStream_t stream) {
     const int nqb = pad128(Lq) / 128, nkb = pad128(Lk) / 128;
     const int nchunk = mean_chunks(Lk);
     const int BH = B * H;
-    auto quant = D == 128 ? k_quant_int8<128> : k_quant_int8<64>;
-    if (smooth) {
-        auto kfused = D == 128 ? (k.bf16 ? k_quant_k_fused<128, true> : k_quant_k_fused<128, false>)
-                               : (k.bf16 ? k_quant_k_fused<64, true> : k_quant_k_fused<64, false>);
-        if (single_read_ok(k, Lk, D, BH * nchunk, (const void*)kfused)) {
-            // Q blocks (clearing the flags), then K read once
-            quant<<<dim3(BH, nqb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb, nullptr, nchunk,
-                                                          nullptr, q_out, q_scale, nullptr, nullptr,
-                                                          counters, BH * nchunk);
-            kfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(k, H, Lk, k_block, nchunk, mean_partial,
-                                                              counters, mu_out, k_out, k_scale);
+    if (smooth && q.bf16 == k.bf16) {
+        auto fused = D == 128 ? (k.bf16 ? k_quant_qk_fused<128, true> : k_quant_qk_fused<128, false>)
+                              : (k.bf16 ? k_quant_qk_fused<64, true> : k_quant_qk_fused<64, false>);
+        if (single_read_ok(k, Lk, D, BH * nchunk, (const void*)fused) && single_read_ok(q, Lq, D, 0, nullptr)) {
+            const HeadSync hs = {sync, sync + (int64_t)BH * nchunk};
+            fused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nchunk, mean_partial, hs,
+                                                             mu_out, q_out, q_scale, k_out, k_scale);
             return hipGetLastError();
         }
+    }
+    if (smooth) {
         const hipError_t e = launch_k_mean_partial(k, B, H, Lk, D, mean_partial, stream);
         if (e != hipSuccess) return e;
     }
+    auto quant = D == 128 ? k_quant_int8<128> : k_quant_int8<64>;
     quant<<<dim3(BH, nqb + nkb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb,
                                                         smooth ? mean_partial : nullptr, nchunk, mu_out,
-                                                        q_out, q_scale, k_out, k_scale, nullptr, 0);
+                                                        q_out, q_scale, k_out, k_scale);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
-                          int* counters, uint8_t* v_out, float* v_scale, hipStream_t stream) {
+                          uint64_t* sync, uint8_t* v_out, float* v_scale, hipStream_t stream) {
     const int nchunk = mean_chunks(Lk);
     const int BH = B * H;
     auto vfused = D == 128 ? (v.bf16 ? k_quant_v_fused<128, true> : k_quant_v_fused<128, false>)
                            : (v.bf16 ? k_quant_v_fused<64, true> : k_quant_v_fused<64, false>);
     if (single_read_ok(v, Lk, D, BH * nchunk, (const void*)vfused)) {
-        k_zero_i32<<<1, kThreads, 0, stream>>>(counters, BH * nchunk);
-        vfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, counters,
-                                                          v_out, v_scale);
+        const HeadSync hs = {sync, sync + (int64_t)BH * nchunk};
+        vfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, hs, v_out, v_scale);
         return hipGetLastError();
     }
     dim3 g1(BH, nchunk), g2(BH, pad128(Lk) / 128);

@@ -40,18 +40,22 @@ hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D
 
 // INT8 block quantization of Q (128-row blocks) and K (k_block rows, 64 or
 // 128), K smoothed by its channel mean when `smooth` (written to mu_out when
-// not NULL).  Scratch: mean_partial fp64 [B*H, mean_chunks(Lk), D] and
-// counters int32 [B*H, mean_chunks(Lk)] (arrival flags; used when smooth).
+// not NULL).  Scratch (used when smooth): mean_partial fp64 [B*H,
+// mean_chunks(Lk), D] and sync uint64 [quant_sync_words(B*H, Lk)].
 hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int H, int Lq,
                                 int Lk, int D, int k_block, bool smooth, double* mean_partial,
-                                int* counters, float* mu_out, int8_t* q_out, float* q_scale,
+                                uint64_t* sync, float* mu_out, int8_t* q_out, float* q_scale,
                                 int8_t* k_out, float* k_scale, hipStream_t stream);
 
 // V -> e4m3 transposed [B, H, D, pad128(Lk)] with per-channel scales.
-// Scratch: amax_partial fp32 [B*H, mean_chunks(Lk), D], counters int32
-// [B*H, mean_chunks(Lk)] (arrival flags).
+// Scratch: amax_partial fp32 [B*H, mean_chunks(Lk), D] and sync uint64
+// [quant_sync_words(B*H, Lk)].
 hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
-                          int* counters, uint8_t* v_out, float* v_scale, hipStream_t stream);
+                          uint64_t* sync, uint8_t* v_out, float* v_scale, hipStream_t stream);
+
+// Words of the quantizers' head-synchronization scratch (arrival flags and
+// epochs; needs no initialization).
+inline int64_t quant_sync_words(int64_t BH, int Lk) { return BH * mean_chunks(Lk) + BH; }
 
 // Hadamard rotation (optional) + MXFP4 quantization of Q and smoothed K.
 // hadamard_bf16 / hadamard_f16: 128x128 +-1 matrices (NULL: no rotation);
