@@ -111,3 +111,68 @@ def test_mxfp4_with_hadamard(dev, orc, name, kw):
         step = np.repeat(2.0 ** (oe.astype(np.float32) - 127), 32, axis=-1) * 2.0
         diff = np.abs(deq(g4, ge) - deq(o4, oe))
         assert (diff[same_e] <= step[same_e] + 1e-30).all()
+
+
+def _same_qk(a, b):
+    for f in ("q", "q_scale", "k", "k_scale", "k_mean"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_single_read_sync_words(dev):
+    """The single-read quantizers meet per head through flags in the
+    workspace that carry per-call epoch tokens: results must not depend on
+    what the workspace held before -- random bytes, the previous call of the
+    same shape, or a call of another shape in between."""
+    w = wl.WORKLOADS["llm_prefill"]
+    inp = wl.make_prefill(w, device=dev, Lq=520, Lk=520, B=1, H=3)
+    other = wl.make_prefill(w, device=dev, Lq=1500, Lk=1500, B=1, H=2)
+    say("quantizer sync words", "llm_prefill 520 x 3 heads, 1500 x 2 heads between")
+    ref_qk = sage.sage_quantize_qk(inp.q, inp.k)
+    ref_v = sage.sage_quantize_v(inp.v)
+    nq = max(sage.sage_quantize_qk_workspace_size(inp.q, inp.k),
+             sage.sage_quantize_qk_workspace_size(other.q, other.k))
+    nv = max(sage.sage_quantize_v_workspace_size(inp.v), sage.sage_quantize_v_workspace_size(other.v))
+    wq = torch.empty(nq, dtype=torch.uint8, device=dev)
+    wv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(11)
+    for trial in range(5):
+        if trial == 0:   # garbage
+            wq.copy_(torch.randint(0, 256, (nq,), dtype=torch.uint8, generator=g))
+            wv.copy_(torch.randint(0, 256, (nv,), dtype=torch.uint8, generator=g))
+        if trial == 3:   # another layout on the same words
+            sage.sage_quantize_qk(other.q, other.k, workspace=wq)
+            sage.sage_quantize_v(other.v, workspace=wv)
+        if trial == 4:   # all zero
+            wq.zero_()
+            wv.zero_()
+        got = sage.sage_quantize_qk(inp.q, inp.k, workspace=wq)
+        got_v = sage.sage_quantize_v(inp.v, workspace=wv)
+        torch.cuda.synchronize()
+        _same_qk(got, ref_qk)
+        assert torch.equal(got_v[0].view(torch.uint8), ref_v[0].view(torch.uint8))
+        assert torch.equal(got_v[1], ref_v[1])
+
+
+def test_two_pass_path_bit_exact(dev, orc):
+    """More chunks than the device holds at once (9 heads x 258 chunks of 256
+    tokens): the quantizers take the two-pass kernels, whose results must be
+    the oracle's too."""
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_prefill(w, device=dev, Lq=66000, Lk=66000, B=1, H=9)
+    say("two-pass quantizers", "tiny distribution, 9 heads x 66000 tokens, D 64")
+    qk = sage.sage_quantize_qk(inp.q, inp.k)
+    v_q, v_s = sage.sage_quantize_v(inp.v)
+    torch.cuda.synchronize()
+    qc, kc, vc = canon(inp.q), canon(inp.k), canon(inp.v)
+    L = kc.shape[2]
+    mu_g = qk.k_mean.cpu().numpy()
+    assert np.array_equal(mu_g, orc.k_mean(kc))
+    q8, qs = orc.quant_int8(qc, 128)
+    k8, ks = orc.quant_int8(orc.smooth_k(kc, mu_g), 64)
+    assert np.array_equal(qk.q.cpu().numpy()[:, :, :L], q8)
+    assert np.array_equal(qk.k.cpu().numpy()[:, :, :L], k8)
+    assert np.array_equal(qk.q_scale.cpu().numpy(), qs)
+    assert np.array_equal(qk.k_scale.cpu().numpy()[..., :ks.shape[-1]], ks)
+    v8, vs = orc.quant_v_fp8(vc)
+    assert np.array_equal(u8(v_q).transpose(0, 1, 3, 2)[:, :, :L], v8)
+    assert np.array_equal(v_s.cpu().numpy(), vs)
