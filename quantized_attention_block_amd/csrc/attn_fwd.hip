@@ -195,6 +195,11 @@ struct QFrag {
 // Integer comparison of biased scores orders them like S.
 constexpr int kSBias = 0x4B400000;
 constexpr float kSBiasF = 12582912.0f;   // 1.5 * 2^23
+// Row max of raw scores: integer max for INT8, fmaxf for MXFP4 (scores are
+// finite, so fmaxf's NaN rule never applies; a compare-and-select does not
+// map to v_max3_f32).
+__device__ __forceinline__ int vmax(int a, int b) { return a > b ? a : b; }
+__device__ __forceinline__ float vmax(float a, float b) { return fmaxf(a, b); }
 __device__ __forceinline__ float score_f(int biased) { return __int_as_float(biased) - kSBiasF; }
 __device__ __forceinline__ float score_f(float s) { return s; }
 
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             if (st[t] == 2) {
                 auto mx = S[t][0];
 #pragma unroll
-                for (int e = 1; e < 16; ++e) mx = S[t][e] > mx ? S[t][e] : mx;
+                for (int e = 1; e < 16; ++e) mx = vmax(mx, S[t][e]);
                 tmax = fmaxf(tmax, score_f(mx) * c);
             } else if (st[t] == 1) {
 #pragma unroll
