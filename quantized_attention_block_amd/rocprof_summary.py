@@ -26,10 +26,8 @@ KERNELS = {
     "k_attn_fwd<128, false>": ("attn_fwd_llm_prefill", ["attn_fwd.hip", "sage_device.hpp"]),
     "k_paged_decode<128>": ("paged_decode", ["decode.hip", "sage_device.hpp"]),
     "k_decode_merge": ("decode_merge", ["decode.hip", "sage_device.hpp"]),
-    "k_quant_int8<128>": ("quant_int8_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
-    "k_v_quant<128>": ("v_quant_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
-    "k_mean_partial<128>": ("k_mean_partial_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
-    "k_v_amax<128>": ("v_amax_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
+    "k_quant_qk_fused<128, true>": ("quant_qk_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
+    "k_quant_v_fused<128, true>": ("quant_v_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
 }
 
 
