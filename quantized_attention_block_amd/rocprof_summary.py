@@ -9,6 +9,10 @@ traffic <fetch_dir> <write_dir> <cal_fetch_dir> <cal_write_dir> <copy_bytes> <ou
     (known bytes / counter reading of a plain copy of copy_bytes), keyed by
     kernel and workload, with the hash of the kernel's source files so a
     reader can tell when the numbers no longer describe the code.
+counters <kernel fragment> <MFMA instructions per wave-step> <out.txt> <label=pass_dir[,pass_dir...]>...
+    SQ / GRBM counters of one kernel (rocprofv3 --pmc passes over the same
+    command, one directory per pass) per workload label, as per-wave-step
+    instruction counts and pipe utilisations.  MI355X: 8 XCDs, 1024 SIMDs.
 """
 import csv
 import glob
@@ -92,9 +96,46 @@ def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_bytes, out)
         f.write("\n")
 
 
+def counters(frag, mfma_per_step, out, groups):
+    n_xcd, n_simd = 8, 1024
+    lines = ["# rocprofv3 --pmc counter summary of kernels matching '%s' (average per dispatch)" % frag,
+             "# per wave-step = per wave and per KV tile (SQ_INSTS_MFMA / %d)" % mfma_per_step,
+             "# SQ_*_CYCLES and SQ_WAVE_CYCLES count quad-cycles; GRBM_GUI_ACTIVE is summed over XCDs"]
+    for g in groups:
+        label, dirs = g.split("=", 1)
+        m = {}
+        for d in dirs.split(","):
+            for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                for r in csv.DictReader(open(fn)):
+                    if frag in r["Kernel_Name"]:
+                        m.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        m = {k: sum(v) / len(v) for k, v in m.items()}
+        steps = m["SQ_INSTS_MFMA"] / mfma_per_step
+        gui = m["GRBM_GUI_ACTIVE"] / n_xcd
+        lines.append("")
+        lines.append("[%s] wave-steps per dispatch %.0f, GPU cycles %.0f" % (label, steps, gui))
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+                  "SQ_INSTS_LDS", "SQ_INSTS_SMEM", "SQ_INSTS_BRANCH"):
+            if c in m:
+                lines.append("  %-26s %8.1f per wave-step" % (c, m[c] / steps))
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * gui)
+        lines.append("  MFMA busy                  %8.3f of SIMD cycles" % busy)
+        lines.append("  MFMA co-executing VALU     %8.3f of MFMA-busy cycles"
+                     % (m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]))
+        lines.append("  SIMD cycles per wave-step  %8.0f" % (n_simd * gui / steps))
+        lines.append("  resident waves per SIMD    %8.2f" % (4 * m["SQ_WAVE_CYCLES"] / (n_simd * gui)))
+        lines.append("  waiting for an instruction %8.3f of wave cycles (SQ_WAIT_INST_ANY)"
+                     % (m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]))
+        lines.append("  LDS bank conflicts         %8.0f cycles per dispatch" % m.get("SQ_LDS_BANK_CONFLICT", 0.0))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4:])
+    elif sys.argv[1] == "counters":
+        counters(sys.argv[2], int(sys.argv[3]), sys.argv[4], sys.argv[5:])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:6], int(sys.argv[6]), sys.argv[7])
     else:
