@@ -86,6 +86,15 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     constexpr int kLgn = PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
     const int s = blockIdx.x, bk = blockIdx.y;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
+    // A page table of at most 64 pages per sequence is read whole, one entry
+    // per lane, in flight together with the context length (the tile's pages
+    // depend on it); longer tables are read after it.
+    const bool row_in_lanes = a.max_pages <= 64;
+    int prow = 0;
+    if (row_in_lanes) {
+        const int l = (int)(threadIdx.x & 63);
+        prow = a.page_table[(int64_t)b * a.pt_stride + (l < a.max_pages ? l : 0)];
+    }
     // context lengths beyond what the page table covers are clamped to it
     const int ctx = min(scalar_ptr(a.ctx_lens)[b], a.max_pages * a.page);
     if (ctx <= 0) return;
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     const int pl = __builtin_amdgcn_readfirstlane(last / a.page);
     int pid[kNpb];
 #pragma unroll
-    for (int i = 0; i < kNpb; ++i) pid[i] = ptab[min(p0 + i, pl)];
+    for (int i = 0; i < kNpb; ++i)
+        pid[i] = row_in_lanes ? __builtin_amdgcn_readlane(prow, min(p0 + i, pl)) : ptab[min(p0 + i, pl)];
 #pragma unroll
     for (int i = 0; i < kNpb; ++i) pid[i] = (unsigned)pid[i] < (unsigned)a.num_pages ? pid[i] : 0;
 
