@@ -121,7 +121,10 @@ typedef struct sage_hadamard sage_hadamard;
  *      k_out   FP4X2 [B, H, SAGE_PAD(Lk), D/2]   k_scale E8M0 [B, H, SAGE_PAD(Lk), D/32]
  *  q, k: F16 or BF16 logical [B, L, H, D], D in {64, 128}, any B/L/H strides.
  *  k_mean: optional F32 [B, H, D] output of mu (NULL: kept in the workspace).
- *  workspace: sage_quantize_qk_workspace_size bytes.
+ *  workspace: sage_quantize_qk_workspace_size bytes, 16-byte aligned.  Its
+ *    contents need no initialization and may be anything between calls; the
+ *    blocks of one call exchange per-chunk K statistics and arrival flags
+ *    through it, so calls that share a workspace must not overlap in time.
  */
 typedef struct {
     int32_t mode;       /* sage_qk_mode                              */
@@ -147,6 +150,9 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k,
  *   v_out   FP8_E4M3FN [B, H, D, SAGE_PAD(Lk)]  ("transposed V": keys contiguous;
  *           keys >= Lk are 0)
  *   v_scale F32 [B, H, D]
+ *   workspace: sage_quantize_v_workspace_size bytes, 16-byte aligned; as for
+ *           sage_quantize_qk it needs no initialization, and calls sharing it
+ *           must not overlap in time.
  */
 sage_status sage_quantize_v_workspace_size(const sage_tensor* v, size_t* bytes);
 sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
