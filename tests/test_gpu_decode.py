@@ -90,3 +90,16 @@ def test_page_placement_invariance(dev):
                             inp.v_scale[perm], inv[inp.page_table.long()].int(), inp.ctx_lens)
     b = _run(moved, dev, 1024, 2000, w.sm_scale)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("page,ctx,window", [(32, 3000, 1024), (32, 4500, 0)])
+def test_paged_decode_long_page_tables(dev, orc, page, ctx, window):
+    """More than 64 pages per sequence: the page ids are read after the
+    context length instead of whole in lanes (94 and 141 pages here)."""
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("v", 9, 3, 4, 16, 1, 128, page, ctx, window)
+    inp = wl.make_decode(w)
+    inp.ctx_lens[1] = ctx - 300
+    say("paged decode long table", page, ctx, window)
+    g = _run(inp, dev, w.window, w.ctx, base.sm_scale)
+    _check(g, _oracle(orc, inp, w.window, base.sm_scale), _oracle(orc, inp, w.window, base.sm_scale, False))
