@@ -176,3 +176,50 @@ def test_two_pass_path_bit_exact(dev, orc):
     v8, vs = orc.quant_v_fp8(vc)
     assert np.array_equal(u8(v_q).transpose(0, 1, 3, 2)[:, :, :L], v8)
     assert np.array_equal(v_s.cpu().numpy(), vs)
+
+
+def test_step_replayed_from_a_hip_graph(dev):
+    """quantize_qk + quantize_v + attention captured in a HIP graph: every
+    replay reproduces the eager step bit for bit, also after the workspaces
+    served an eager call of another shape in between (the single-read
+    quantizers' epoch words live there and advance on every call)."""
+    w = wl.WORKLOADS["llm_prefill"]
+    inp = wl.make_prefill(w, device=dev, Lq=1100, Lk=1100, B=1, H=3)
+    other = wl.make_prefill(w, device=dev, Lq=700, Lk=700, B=1, H=2)
+    say("graph replay of a step", "llm_prefill 1100 x 3 heads")
+    nq = max(sage.sage_quantize_qk_workspace_size(inp.q, inp.k),
+             sage.sage_quantize_qk_workspace_size(other.q, other.k))
+    nv = max(sage.sage_quantize_v_workspace_size(inp.v), sage.sage_quantize_v_workspace_size(other.v))
+    wq = torch.empty(nq, dtype=torch.uint8, device=dev)
+    wv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, workspace=wq)
+    vq, vs = sage.sage_quantize_v(inp.v, workspace=wv)
+    out = sage.sage_attn_fwd(qk, vq, vs, causal=True, sm_scale=w.sm_scale)
+
+    def step():
+        sage.sage_quantize_qk(inp.q, inp.k, workspace=wq, into=qk)
+        sage.sage_quantize_v(inp.v, workspace=wv, into=(vq, vs))
+        sage.sage_attn_fwd(qk, vq, vs, causal=True, sm_scale=w.sm_scale, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (qk.q, qk.q_scale, qk.k, qk.k_scale, qk.k_mean, vq.view(torch.uint8), vs, out)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in (qk.q, qk.q_scale, qk.k, qk.k_scale, qk.k_mean, vq.view(torch.uint8), vs, out):
+            t.zero_()
+        if r == 2:
+            sage.sage_quantize_qk(other.q, other.k, workspace=wq)
+            sage.sage_quantize_v(other.v, workspace=wv)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (qk.q, qk.q_scale, qk.k, qk.k_scale, qk.k_mean, vq.view(torch.uint8), vs, out)
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), (r, i)
