@@ -382,17 +382,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // block) have no per-key tests; the others mask per 32-key sub-tile, which
     // is wave-uniformly empty, crossing (keys tested one by one) or full for
     // this wave's rows.
-    auto step = [&](int j, auto full_tag) {
+    // STG: the LDS stage of tile j (= j % kStages) as a compile-time constant,
+    // so that every LDS operand address is a per-lane offset plus an
+    // immediate; kStages means "compute it".
+    auto step = [&](int j, auto full_tag, auto stage_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
+        constexpr int STG = decltype(stage_tag)::value;
+        uint8_t* stage = STG < kStages ? smem + STG * G::kStageBytes : stage_of(j);
+        uint8_t* stage2 = STG < kStages ? smem + ((STG + 2) % kStages) * G::kStageBytes : stage_of(j + 2);
         // every wave's part of tile j has landed (tile j+1 may be in flight)
         // and all waves finished step j-1, whose stage tile j+2 reuses
         if (j + 1 < ntiles)
             dma_barrier<kDma>();
         else
             dma_barrier<0>();
-        if (j + 2 < ntiles) Dma::issue(stage_of(j + 2), krs, ksrs, vrs, Lkp, j + 2, wave, lane);
+        if (j + 2 < ntiles) Dma::issue(stage2, krs, ksrs, vrs, Lkp, j + 2, wave, lane);
         const float c = tile_c(j);
-        uint8_t* stage = stage_of(j);
         const int key0 = j * kBN;
 
         int st[kNT];   // 0 empty, 1 crossing, 2 full
@@ -477,8 +482,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (a.causal) n_full = min(n_full, qb * (kBM / kBN));
     n_full = min(n_full, ntiles);
     int j = 0;
-    for (; j < n_full; ++j) step(j, std::true_type{});
-    for (; j < ntiles; ++j) step(j, std::false_type{});
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using SR = std::integral_constant<int, kStages>;
+    static_assert(kStages == 3, "the full-tile loop is unrolled once per stage");
+    for (; j + 3 <= n_full; j += 3) {
+        step(j, std::true_type{}, S0{});
+        step(j + 1, std::true_type{}, S1{});
+        step(j + 2, std::true_type{}, S2{});
+    }
+    for (; j < n_full; ++j) step(j, std::true_type{}, SR{});
+    for (; j < ntiles; ++j) step(j, std::false_type{}, SR{});
 
     // ---- epilogue: out = (O * v_scale) / l (times the reciprocal of l), written
     // with the caller's strides
