@@ -380,17 +380,18 @@ __device__ __forceinline__ T fetch(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// op-fold of p[0], p[stride], ..., p[(n - 1) stride] in index order, eight
-// loads in flight at a time
+// op-fold of p[0], p[stride], ..., p[(n - 1) stride] in index order, sixteen
+// loads in flight at a time (one round trip for a 4096-token head)
 template <typename T, typename Op>
 __device__ __forceinline__ T fold_published(const T* p, int64_t stride, int n, T acc, Op op) {
+    constexpr int kBatch = 16;
     int c = 0;
-    for (; c + 8 <= n; c += 8) {
-        T v[8];
+    for (; c + kBatch <= n; c += kBatch) {
+        T v[kBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = fetch(p + (c + j) * stride);
+        for (int j = 0; j < kBatch; ++j) v[j] = fetch(p + (c + j) * stride);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = op(acc, v[j]);
+        for (int j = 0; j < kBatch; ++j) acc = op(acc, v[j]);
     }
     for (; c < n; ++c) acc = op(acc, fetch(p + c * stride));
     return acc;
