@@ -111,6 +111,8 @@ def test_qk_tiles_full_size_sampled(dev, orc):
     ("llm_prefill", dict(Lq=520, Lk=520, B=1, H=2), True),     # ragged causal
     ("llm_prefill", dict(Lq=333, Lk=333, B=1, H=2), False),
     ("video_dit", dict(Lq=1000, Lk=1000, H=2), False),         # strided views, ragged
+    ("tiny", dict(Lq=200, Lk=700), False),                     # Lq != Lk, D 64
+    ("llm_prefill", dict(Lq=700, Lk=200, B=1, H=2), False),    # Lq != Lk, D 128
 ])
 def test_int8_attention_matches_oracle(dev, orc, name, kw, causal):
     w = wl.WORKLOADS[name]
