@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define SAGE_VERSION_MAJOR 0
-#define SAGE_VERSION_MINOR 2
+#define SAGE_VERSION_MINOR 3
 #define SAGE_PAD(L) ((((L) + 127) / 128) * 128)
 
 typedef enum {
@@ -249,6 +249,18 @@ int32_t sage_decode_num_splits(int32_t window, int32_t mtp, int32_t max_ctx);
  * threads and calls; destroy it once no enqueued work uses it. */
 sage_status sage_hadamard_create(int32_t R, int32_t device, void* stream, sage_hadamard** out);
 sage_status sage_hadamard_destroy(sage_hadamard* h);
+
+/* Bound on the wait inside sage_quantize_qk (INT8 with smooth_k) and
+ * sage_quantize_v.  When the whole grid fits on the device at once, each
+ * block holds one 256-token chunk of a head and waits for the other chunks'
+ * statistics (channel sums of K, channel amax of V), so the inputs are read
+ * from HBM once.  A block that has not seen every chunk of its head after
+ * `us` microseconds (other streams' kernels may hold part of the device)
+ * computes the head's statistic itself from the inputs, in the same order:
+ * the outputs are identical, only slower.  Default 2000; 0 is allowed (tests
+ * use it to take that path).  Process-wide; affects launches made after the
+ * call.  Returns SAGE_ERR_INVALID_ARG outside [0, 1000000]. */
+sage_status sage_set_quant_wait_us(int32_t us);
 
 /* Test hook: int32 S = Q8 K8^T for query rows [q0, q0 + nq) and keys
  * [k0, k0 + nk) of every (b, h), computed by the attention kernel's own QK

@@ -219,6 +219,12 @@ const char* sage_last_error(void) { return g_err; }
 
 int32_t sage_version(void) { return (SAGE_VERSION_MAJOR << 16) | SAGE_VERSION_MINOR; }
 
+sage_status sage_set_quant_wait_us(int32_t us) {
+    if (us < 0 || us > 1000000) return fail(SAGE_ERR_INVALID_ARG, "wait %d us outside [0, 1e6]", us);
+    sage::set_quant_wait_us(us);
+    return ok();
+}
+
 int32_t sage_attn_kv_tile(void) { return sage::kKvTile; }
 
 int32_t sage_decode_num_splits(int32_t window, int32_t mtp, int32_t max_ctx) {

@@ -15,6 +15,8 @@
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
+#include <atomic>
+#include <chrono>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -363,7 +365,6 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
 // summation order), so both paths give identical outputs.  The host takes
 // this path only when the whole grid fits on the device at once, so every
 // block a head waits for is running; the wait is bounded regardless.
-constexpr int kMaxSpin = 1 << 20;   // polls (~1 us each) before giving up
 
 // Every value exchanged between blocks (chunk results, flags, epochs) is read
 // and written with device-scope atomic accesses, which are coherent across
@@ -397,23 +398,46 @@ __device__ __forceinline__ T fold_published(const T* p, int64_t stride, int n, T
     return acc;
 }
 
-// Meeting point of the chunks of one head, with no clearing launch.  The
-// blocks read the head's epoch word e when they start; each publishes, on its
-// chunk's flag, the token of e + 1 once its chunk results are complete, and
-// leaves when every flag of the head holds that token; the head's first chunk
-// then stores e + 1.  A token also encodes the chunk count, so flags left by
-// an earlier call -- same layout, one epoch behind, or another layout -- never
-// match, and the workspace needs no initialization (a stale or garbage 64-bit
-// word equals the token only by chance).  Separate flags rather than one
-// counter: device-scope read-modify-writes of one address serialize (16
-// arrivals on one counter took ~12 us).
+// Meeting point of the chunks of one head, with no clearing launch.  Each
+// block publishes, on its chunk's flag, the call's token once its chunk
+// results are complete, and waits until every flag of the head holds it.
+// The token mixes a number the host draws afresh for every launch with the
+// head's epoch word e, which every block reads when it starts and chunk 0's
+// block alone advances to e + 1 once its own wait is over.  Flags therefore
+// never match across launches -- nor across replays of one captured launch,
+// which share the host number but not the epoch -- and the workspace needs no
+// initialization.  Separate flags rather than one counter, and one epoch
+// writer rather than every block: device-scope writes to one address
+// serialize (16 arrivals on one counter took ~12 us; 16 blocks storing the
+// epoch cost ~3 us per launch).
+//
+// The wait is bounded in time.  If the other chunks do not all arrive -- the
+// host checks that the grid fits on the device, but kernels of other streams
+// may hold part of it -- the block withdraws its arrival (flag 0, never a
+// token) and computes its head's statistic itself from the inputs, in the
+// same order, so the result is the same, only slower.  A block that starts
+// after chunk 0 advanced the epoch carries the next token, meets nobody, and
+// withdraws.  So when a launch ends every flag of a head is 0 or the token of
+// the epoch that launch started with, never the token the next one will wait
+// for.
 struct HeadSync {
-    uint64_t* flags;   // [B*H, nchunk]
-    uint64_t* epoch;   // [B*H]
+    uint64_t* flags;      // [B*H, nchunk]
+    uint64_t* epoch;      // [B*H]
+    uint64_t nonce;       // drawn by the host for each launch
+    int64_t wait_ticks;   // wall-clock ticks a block waits for its head
 };
 
-__device__ __forceinline__ uint64_t head_token(uint64_t e, int nchunk) {
-    return ((e + 1) << 32) | (0x9E3779B9u ^ (uint32_t)nchunk);
+// splitmix64 output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", 2014)
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint64_t head_token(const HeadSync& hs, uint64_t e) {
+    const uint64_t t = mix64(hs.nonce ^ mix64(e));
+    return t ? t : 1;
 }
 
 __device__ __forceinline__ void head_arrive(const HeadSync& hs, int bh, int chunk, int nchunk, uint64_t token) {
@@ -422,19 +446,36 @@ __device__ __forceinline__ void head_arrive(const HeadSync& hs, int bh, int chun
     if (threadIdx.x == 0) publish(hs.flags + (int64_t)bh * nchunk + chunk, token);
 }
 
-__device__ __forceinline__ void head_wait(const HeadSync& hs, int bh, int chunk, int nchunk, uint64_t e,
-                                          uint64_t token) {
+// true when every chunk of the head arrived in time
+__device__ __forceinline__ bool head_wait(const HeadSync& hs, int bh, int chunk, int nchunk, uint64_t e,
+                                          uint64_t token, int* met_lds) {
     if (threadIdx.x < 64) {   // wave 0 polls, one flag per lane and pass
         const uint64_t* f = hs.flags + (int64_t)bh * nchunk;
-        for (int i = 0; i < kMaxSpin; ++i) {
+        const int64_t t0 = wall_clock64();
+        int met = 0;
+        for (int i = 1;; ++i) {
             int missing = 0;
             for (int c = threadIdx.x; c < nchunk; c += 64) missing |= fetch(f + c) != token;
-            if (!__any(missing)) break;
+            if (!__any(missing)) {
+                met = 1;
+                break;
+            }
+            // the clock is read every 16 polls only (a read delays the next
+            // poll about as much as a poll takes); lane 0's reading decides,
+            // so the wave leaves the loop as one
+            if (hs.wait_ticks == 0 ||
+                ((i & 15) == 0 && __builtin_amdgcn_readfirstlane((int)(wall_clock64() - t0 > hs.wait_ticks))))
+                break;
             __builtin_amdgcn_s_sleep(4);
+        }
+        if (threadIdx.x == 0) {   // the thread that published the arrival
+            *met_lds = met;
+            if (!met) publish(hs.flags + (int64_t)bh * nchunk + chunk, (uint64_t)0);
+            if (chunk == 0) publish(hs.epoch + bh, e + 1);
         }
     }
     __syncthreads();
-    if (chunk == 0 && threadIdx.x == 0) publish(hs.epoch + bh, e + 1);
+    return *met_lds != 0;
 }
 
 template <bool BF16>
@@ -532,23 +573,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int row0 = chunk * kMeanChunk;
     const int Lp = pad128(L);
     const uint64_t e = fetch(hs.epoch + bh);
-    const uint64_t token = head_token(e, nchunk);
+    const uint64_t token = head_token(hs, e);
 
+    const uint16_t* khead = (const uint16_t*)k.ptr + (int64_t)b * k.sB + (int64_t)h * k.sH;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(khead, ((int64_t)(L - 1) * k.sL + D) * 2);
+    // rows r0 + kRowsPerPass p of chunk c, channels [8 c8, +8)
+    auto row_off = [&](int c, int p) {
+        return (int)(((int64_t)(c * kMeanChunk + p * G::kRowsPerPass + r0) * k.sL + 8 * c8) * 2);
+    };
     uint4 raw[kPasses];
-    {
-        const uint16_t* head = (const uint16_t*)k.ptr + (int64_t)b * k.sB + (int64_t)h * k.sH;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(L - 1) * k.sL + D) * 2);
-        const int off = (int)(((int64_t)(row0 + r0) * k.sL + 8 * c8) * 2);
-        const int step = (int)(G::kRowsPerPass * k.sL * 2);
+    auto load_chunk = [&]() {
         // four passes in flight at a time: with every block of the grid
         // loading at once, unthrottled requests left some blocks waiting ~3x
         // longer than the median for their rows
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            raw[p] = load16(rs, off + p * step);
+            raw[p] = load16(krs, row_off(chunk, p));
             if (p % 4 == 3 && p + 1 < kPasses) __builtin_amdgcn_s_waitcnt(0x3f70);
         }
-    }
+    };
+    load_chunk();
 
     // chunk channel sums in binary64: rows ascending per thread, then the
     // threads of a channel in row order (zero rows add nothing)
@@ -583,13 +627,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         quant_q_block<D, BF16>(q, b, h, bh, qb, Lq, q_out, q_scale, &red[0][0]);
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
-    head_wait(hs, bh, chunk, nchunk, e, token);
+    __shared__ int met_s;
+    const bool met = head_wait(hs, bh, chunk, nchunk, e, token, &met_s);
 
     __shared__ float mu_s[D];
+    double acc = 0.0;   // channel sum over the head (thread d < D)
+    if (met) {
+        if (threadIdx.x < D)
+            acc = fold_published(partial + (int64_t)bh * nchunk * D + threadIdx.x, (int64_t)D, nchunk, 0.0,
+                                 [](double x, double y) { return x + y; });
+    } else {
+        // every chunk's sums from the inputs, in the order of the published ones
+        for (int c = 0; c < nchunk; ++c) {
+            double cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+            for (int p = 0; p < kPasses; ++p) {
+                float x[8];
+                unpack8t<BF16>(load16(krs, row_off(c, p)), x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cs[i] += (double)x[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm[threadIdx.x][i] = cs[i];
+            __syncthreads();
+            if (threadIdx.x < D) {
+                const int d = threadIdx.x;
+                double s = 0.0;
+                for (int r = 0; r < G::kRowsPerPass; ++r) s += sm[r * G::kLanesPerRow + d / 8][d % 8];
+                acc += s;
+            }
+            __syncthreads();
+        }
+    }
     if (threadIdx.x < D) {
         const int d = threadIdx.x;
-        const double acc = fold_published(partial + (int64_t)bh * nchunk * D + d, (int64_t)D, nchunk, 0.0,
-                                          [](double x, double y) { return x + y; });
         const float m = L > 0 ? (float)(acc / (double)L) : 0.0f;
         mu_s[d] = m;
         if (chunk == 0 && mu_out) mu_out[(int64_t)bh * D + d] = m;
@@ -681,21 +752,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int Lp = pad128(L);
     const int c8 = threadIdx.x % kGroups, kg0 = threadIdx.x / kGroups;
     const uint64_t e = fetch(hs.epoch + bh);
-    const uint64_t token = head_token(e, nchunk);
+    const uint64_t token = head_token(hs, e);
 
+    const uint16_t* vhead = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)h * v.sH;
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhead, ((int64_t)(L - 1) * v.sL + D) * 2);
     uint4 raw[kPasses][4];   // keys k0 + 4 (p kKeyGroups + kg0) + j
-    {
-        const uint16_t* head = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)h * v.sH;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(L - 1) * v.sL + D) * 2);
+    auto load_chunk = [&]() {
         const int off = (int)(((int64_t)(k0 + 4 * kg0) * v.sL + 8 * c8) * 2);
         const int sk = (int)(v.sL * 2), sp = (int)(4 * kKeyGroups * v.sL * 2);
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) raw[p][j] = load16(rs, off + p * sp + j * sk);
+            for (int j = 0; j < 4; ++j) raw[p][j] = load16(vrs, off + p * sp + j * sk);
             if (p + 1 < kPasses) __builtin_amdgcn_s_waitcnt(0x3f70);   // four rows in flight (see K)
         }
-    }
+    };
+    load_chunk();
 
     // LDS: the chunk-amax exchange, later the transpose tile
     constexpr int kTileWords = D * kKeys / 4;
@@ -729,13 +801,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int j = 0; j < 4; ++j)
             asm("" : "+v"(raw[p][j].x), "+v"(raw[p][j].y), "+v"(raw[p][j].z), "+v"(raw[p][j].w));
     head_arrive(hs, bh, chunk, nchunk, token);
-    head_wait(hs, bh, chunk, nchunk, e, token);
+    __shared__ int met_s;
+    const bool met = head_wait(hs, bh, chunk, nchunk, e, token, &met_s);
 
     __shared__ float inv_s[D];
+    float a = 0.0f;   // channel amax over the head (thread d < D)
+    if (met) {
+        if (threadIdx.x < D)
+            a = fold_published(partial + (int64_t)bh * nchunk * D + threadIdx.x, (int64_t)D, nchunk, 0.0f,
+                               [](float x, float y) { return fmaxf(x, y); });
+    } else {
+        // every chunk's amax from the inputs (max is order-free)
+        float mm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+        for (int row = kg0; row < nchunk * kKeys; row += kKeyGroups) {
+            float x[8];
+            unpack8t<BF16>(load16(vrs, (int)(((int64_t)row * v.sL + 8 * c8) * 2)), x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mm[i] = fmaxf(mm[i], fabsf(x[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm[threadIdx.x][i] = mm[i];
+        __syncthreads();
+        if (threadIdx.x < D)
+            for (int g = 0; g < kKeyGroups; ++g) a = fmaxf(a, sm[g * kGroups + threadIdx.x / 8][threadIdx.x % 8]);
+        __syncthreads();
+    }
     if (threadIdx.x < D) {
         const int d = threadIdx.x;
-        const float a = fold_published(partial + (int64_t)bh * nchunk * D + d, (int64_t)D, nchunk, 0.0f,
-                                       [](float x, float y) { return fmaxf(x, y); });
         inv_s[d] = a > 0.0f ? kFp8Max / a : 0.0f;
         if (chunk == 0) v_scale[(int64_t)bh * D + d] = a / kFp8Max;
     }
@@ -913,6 +1006,32 @@ static int resident_blocks(const void* kernel) {
     return n;
 }
 
+// Single-read head barrier: microseconds a block waits for the other chunks
+// of its head before it computes the head's statistic itself.
+static std::atomic<int> g_wait_us{2000};
+
+void set_quant_wait_us(int us) { g_wait_us.store(us, std::memory_order_relaxed); }
+
+static HeadSync head_sync(uint64_t* sync, int64_t BH, int nchunk) {
+    static std::atomic<uint64_t> nonce{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count()};
+    static std::mutex mu;
+    static std::map<int, int> khz;   // wall-clock rate per device
+    int dev = 0, rate = 0;
+    (void)hipGetDevice(&dev);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = khz.find(dev);
+        if (it == khz.end()) {
+            if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate <= 0)
+                rate = 100000;
+            it = khz.emplace(dev, rate).first;
+        }
+        rate = it->second;
+    }
+    return {sync, sync + BH * nchunk, nonce.fetch_add(1, std::memory_order_relaxed),
+            (int64_t)g_wait_us.load(std::memory_order_relaxed) * rate / 1000};
+}
+
 // The single-read path: the grid fits on the device at once, token rows do not
 // overlap (sL >= D, so rows past L fall outside the buffer resource) and byte
 // offsets within one head fit in 32 bits.
@@ -953,7 +1072,7 @@ hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int
         auto fused = D == 128 ? (k.bf16 ? k_quant_qk_fused<128, true> : k_quant_qk_fused<128, false>)
                               : (k.bf16 ? k_quant_qk_fused<64, true> : k_quant_qk_fused<64, false>);
         if (single_read_ok(k, Lk, D, BH * nchunk, (const void*)fused) && single_read_ok(q, Lq, D, 0, nullptr)) {
-            const HeadSync hs = {sync, sync + (int64_t)BH * nchunk};
+            const HeadSync hs = head_sync(sync, BH, nchunk);
             fused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nchunk, mean_partial, hs,
                                                              mu_out, q_out, q_scale, k_out, k_scale);
             return hipGetLastError();
@@ -977,7 +1096,7 @@ hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float*
     auto vfused = D == 128 ? (v.bf16 ? k_quant_v_fused<128, true> : k_quant_v_fused<128, false>)
                            : (v.bf16 ? k_quant_v_fused<64, true> : k_quant_v_fused<64, false>);
     if (single_read_ok(v, Lk, D, BH * nchunk, (const void*)vfused)) {
-        const HeadSync hs = {sync, sync + (int64_t)BH * nchunk};
+        const HeadSync hs = head_sync(sync, BH, nchunk);
         vfused<<<dim3(BH, nchunk), kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, hs, v_out, v_scale);
         return hipGetLastError();
     }

@@ -53,6 +53,11 @@ hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int
 hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float* amax_partial,
                           uint64_t* sync, uint8_t* v_out, float* v_scale, hipStream_t stream);
 
+// Microseconds a block of the single-read quantizers waits for the other
+// blocks of its head before computing the head's statistic itself (default
+// 2000; the outputs are the same either way).
+void set_quant_wait_us(int us);
+
 // Words of the quantizers' head-synchronization scratch (arrival flags and
 // epochs; needs no initialization).
 inline int64_t quant_sync_words(int64_t BH, int Lk) { return BH * mean_chunks(Lk) + BH; }

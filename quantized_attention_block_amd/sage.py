@@ -101,10 +101,12 @@ def lib():
         L.sage_hadamard_destroy.argtypes = [_P]
         L.sage_debug_qk_tile.argtypes = [_T, _T, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _T, _P]
+        L.sage_set_quant_wait_us.argtypes = [ctypes.c_int32]
         for name in ("sage_quantize_qk_workspace_size", "sage_quantize_qk",
                      "sage_quantize_v_workspace_size", "sage_quantize_v", "sage_attn_fwd",
                      "sage_paged_decode_workspace_size", "sage_paged_decode",
-                     "sage_hadamard_create", "sage_hadamard_destroy", "sage_debug_qk_tile"):
+                     "sage_hadamard_create", "sage_hadamard_destroy", "sage_debug_qk_tile",
+                     "sage_set_quant_wait_us"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -237,6 +239,13 @@ def sage_quantize_qk_workspace_size(q: torch.Tensor, k: torch.Tensor, *, mode: i
     _check(lib().sage_quantize_qk_workspace_size(ctypes.byref(desc(q)), ctypes.byref(desc(k)),
                                                  ctypes.byref(prm), ctypes.byref(nbytes)))
     return int(nbytes.value)
+
+
+def sage_set_quant_wait_us(us: int) -> None:
+    """Microseconds a block of the single-read quantizers waits for the rest
+    of its head before computing the head's statistic itself (process-wide;
+    the outputs are the same either way)."""
+    _check(lib().sage_set_quant_wait_us(int(us)))
 
 
 def sage_quantize_v_workspace_size(v: torch.Tensor) -> int:

@@ -33,7 +33,15 @@ def test_exports_every_declared_symbol(S):
     assert len(names) >= 13
     for n in names:
         assert hasattr(S.lib(), n), n
-    assert S.lib().sage_version() == 2   # 0.2: adds sage_attn_kv_tile
+    assert S.lib().sage_version() == 3   # 0.3: adds sage_set_quant_wait_us
+
+
+def test_quant_wait_bound_is_checked(S):
+    with pytest.raises(S.SageError):
+        S.sage_set_quant_wait_us(-1)
+    with pytest.raises(S.SageError):
+        S.sage_set_quant_wait_us(1000001)
+    S.sage_set_quant_wait_us(2000)   # the default; host-only, no device touched
 
 
 def test_attn_kv_tile_is_the_one_parity_tests_emulate(S):

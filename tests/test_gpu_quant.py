@@ -153,6 +153,65 @@ def test_single_read_sync_words(dev):
         assert torch.equal(got_v[1], ref_v[1])
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("llm_prefill", dict(Lq=2100, Lk=2100, B=1, H=3)),   # 9 chunks, bf16, D 128
+    ("tiny", dict(Lq=1000, Lk=1000, B=2, H=2)),          # 4 chunks, fp16, D 64
+    ("video_dit", dict(Lq=700, Lk=700, H=2)),            # stacked strided views
+])
+def test_single_read_wait_bound(dev, name, kw):
+    """With a zero wait bound a single-read block that does not find every
+    chunk of its head at its first look withdraws its arrival and computes the
+    head's statistic from the inputs itself: outputs bit-identical to the
+    default, over calls in a row on one workspace, after which the default
+    bound works on that workspace again; and in replays of a captured step
+    (which share one launch number)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    say("quantizer wait bound 0", f"{name} {kw}")
+    ref_qk = sage.sage_quantize_qk(inp.q, inp.k)
+    ref_v = sage.sage_quantize_v(inp.v)
+    wq = torch.empty(sage.sage_quantize_qk_workspace_size(inp.q, inp.k), dtype=torch.uint8, device=dev)
+    wv = torch.empty(sage.sage_quantize_v_workspace_size(inp.v), dtype=torch.uint8, device=dev)
+
+    def check(qk, v):
+        _same_qk(qk, ref_qk)
+        assert torch.equal(v[0].view(torch.uint8), ref_v[0].view(torch.uint8))
+        assert torch.equal(v[1], ref_v[1])
+
+    try:
+        sage.sage_set_quant_wait_us(0)
+        for _ in range(3):
+            got = sage.sage_quantize_qk(inp.q, inp.k, workspace=wq)
+            got_v = sage.sage_quantize_v(inp.v, workspace=wv)
+            torch.cuda.synchronize()
+            check(got, got_v)
+        qk = sage.sage_quantize_qk(inp.q, inp.k, workspace=wq)
+        vq, vs = sage.sage_quantize_v(inp.v, workspace=wv)
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                sage.sage_quantize_qk(inp.q, inp.k, workspace=wq, into=qk)
+                sage.sage_quantize_v(inp.v, workspace=wv, into=(vq, vs))
+        torch.cuda.synchronize()
+    finally:
+        sage.sage_set_quant_wait_us(2000)
+    for _ in range(3):
+        for t in (qk.q, qk.q_scale, qk.k, qk.k_scale, qk.k_mean, vq.view(torch.uint8), vs):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check(qk, (vq, vs))
+    got = sage.sage_quantize_qk(inp.q, inp.k, workspace=wq)
+    got_v = sage.sage_quantize_v(inp.v, workspace=wv)
+    torch.cuda.synchronize()
+    check(got, got_v)
+    with pytest.raises(sage.SageError):
+        sage.sage_set_quant_wait_us(-1)
+
+
 def test_two_pass_path_bit_exact(dev, orc):
     """More chunks than the device holds at once (9 heads x 258 chunks of 256
     tokens): the quantizers take the two-pass kernels, whose results must be
