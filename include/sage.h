@@ -209,7 +209,9 @@ int32_t sage_attn_kv_tile(void);
  * With window W > 0 query position p sees keys [p - W + 1, p]; otherwise
  * [0, p].  The work is split into 256-token tiles aligned to absolute
  * positions, one split per tile (page: "each tile is its own task"); splits
- * write (m, l, O) partials to the workspace and a merge step combines them.
+ * write (m, l, O) partials to the workspace and a merge step combines them
+ * (O is kept normalized, O / l, in fp16 scaled into [-448, 448]: the merge's
+ * inputs carry a relative rounding of 2^-11, below the bf16 output's 2^-9).
  * Q rows are quantized to e4m3 with a per-(token, head) scale; scores use FP8
  * MFMA; P is requantized per tile with the tile's largest per-token V scale.
  * D must be 128; the page size must be a multiple of 32 that divides 256 or

@@ -473,7 +473,7 @@ sage_status decode_query(const sage_tensor* q, const sage_tensor* page_table,
     return SAGE_OK;
 }
 size_t decode_ws(const DecShape& s, int Hkv) {
-    return align256((size_t)s.B * Hkv * s.splits * s.rows_pad * (128 + 4) * sizeof(float));
+    return align256((size_t)s.B * Hkv * s.splits * s.rows_pad * (2 * 128 + 16));
 }
 }  // namespace
 

@@ -38,7 +38,12 @@ constexpr int kThreads = 256;
 constexpr int kRows = 64;            // query rows per KV head (padded): 16 per wave
 constexpr int kTile = kDecodeTile;   // 256 keys per split
 constexpr int kD = 128;
-constexpr int kPartStride = kD + 4;  // floats per partial row: O[D], m, l, pad
+// Partial row of one (sequence, KV head, split, query row): h[D] as fp16,
+// then m, l and vmax as fp32, then 4 pad bytes.  h = O8 / (448 l) with O8 =
+// sum P8 V8 (e4m3 codes): P8 <= 448 p and |V8| <= 448 give |h| <= 448, so the
+// fp16 rounding is relative (2^-11) whatever the cache's scales; the split's
+// output is h vmax.
+constexpr int kPartBytes = 2 * kD + 16;
 
 // Keeps the first n bytes of v (all for n >= 16, none for n <= 0), zeroes the rest.
 __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
@@ -54,6 +59,16 @@ __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// two fp32 -> fp16 (round to nearest even), x in the low half
+__device__ __forceinline__ uint32_t pack_h2(float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y) << 16);
+}
+__device__ __forceinline__ float2 unpack_h2(uint32_t w) {
+    return make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)),
+                       (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)));
 }
 
 // LDS K tile [256 keys][128 B]: chunk c of key k is stored at chunk
@@ -334,21 +349,19 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         }
     }
     if (r < R) {
-        const float back = vmax / kFp8Max;
-        float* prow = a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartStride;
+        const float hs = ls > 0.0f ? 1.0f / (kFp8Max * ls) : 0.0f;
+        uint8_t* prow = (uint8_t*)a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartBytes;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-            *(float4*)(prow + 16 * db + 4 * q4) =
-                make_float4(O[db][0] * back, O[db][1] * back, O[db][2] * back, O[db][3] * back);
-        if (q4 == 0) {
-            prow[kD] = rmax;
-            prow[kD + 1] = ls;
-        }
+            *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
+                make_uint2(pack_h2(O[db][0] * hs, O[db][1] * hs), pack_h2(O[db][2] * hs, O[db][3] * hs));
+        if (q4 == 0) *(float4*)(prow + 2 * kD) = make_float4(rmax, ls, vmax, 0.0f);
     }
 }
 
 // Merge of the split partials of one (sequence, KV head, row): m* = max m_s,
-// out = sum 2^(m_s - m*) O_s / sum 2^(m_s - m*) l_s (fp32, split order), bf16.
+// out = sum 2^(m_s - m*) l_s (h_s vmax_s) / sum 2^(m_s - m*) l_s (fp32, split
+// order), bf16; l_s h_s vmax_s is the split's O_s.
 // One wave per row; the weights are broadcast and every lane merges two
 // output channels over all splits with coalesced loads.
 constexpr int kMergeRowsPerBlock = 4;
@@ -365,8 +378,8 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     const int G = a.Hq / a.Hkv;
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
-    const float* base = a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartStride;
-    const int64_t sstride = (int64_t)kRows * kPartStride;
+    const uint8_t* base = (const uint8_t*)a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartBytes;
+    const int64_t sstride = (int64_t)kRows * kPartBytes;
     // Splits are taken kMergeBatch at a time with every load of a batch in
     // flight at once: lane s holds split s's (m, l), every lane two output
     // channels of each split.  With at most kMergeBatch splits (windowed
@@ -375,12 +388,11 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int s0 = 0; s0 < nsp; s0 += kMergeBatch) {
         const int n = min(kMergeBatch, nsp - s0);
-        float2 ml = make_float2(-INFINITY, 0.0f);
-        if (lane < n) ml = *(const float2*)(base + (s0 + lane) * sstride + kD);
-        float2 o[kMergeBatch];
+        float4 ml = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);   // m, l, vmax
+        if (lane < n) ml = *(const float4*)(base + (s0 + lane) * sstride + 2 * kD);
+        uint32_t o[kMergeBatch];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
-            o[u] = u < n ? *(const float2*)(base + (s0 + u) * sstride + 2 * lane) : make_float2(0.0f, 0.0f);
+        for (int u = 0; u < kMergeBatch; ++u) o[u] = u < n ? *(const uint32_t*)(base + (s0 + u) * sstride + 4 * lane) : 0u;
         const float Mn = fmaxf(M, wave_max(ml.x));
         if (Mn == -INFINITY) continue;               // no visible key so far
         if (M != -INFINITY && M != Mn) {
@@ -392,13 +404,15 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
         M = Mn;
         const float w = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
         const float lw = w * ml.y;
+        const float ow = lw * ml.z;
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             if (u < n) {
-                const float wj = __shfl(w, u);
+                const float wj = __shfl(ow, u);
+                const float2 h = unpack_h2(o[u]);
                 L = L + __shfl(lw, u);
-                o0 = o0 + wj * o[u].x;
-                o1 = o1 + wj * o[u].y;
+                o0 = o0 + wj * h.x;
+                o1 = o1 + wj * h.y;
             }
         }
     }

@@ -106,7 +106,7 @@ struct DecodeArgs {
     int B, MTP, Hq, Hkv, D, page, num_pages, max_pages;
     int window, v_transposed, num_splits;
     float sm_scale;
-    float* partials;          // [B, Hkv, num_splits, rows, D + 2]
+    float* partials;          // [B, Hkv, num_splits, rows] rows of fp16 h[D], fp32 m, l, vmax, pad
 };
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
