@@ -99,6 +99,11 @@ template <int PW>
 __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float alpha) {
     constexpr int kNpb = kTile / PW;                 // page-blocks per tile
     constexpr int kLgn = PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
+    // Every kernel argument the block uses is read at entry, in one batch:
+    // left to itself the compiler loads the pointers only after the context
+    // length has arrived, one more round trip before the tile copies start.
+    asm volatile("" ::"s"(a.q), "s"(a.q_sB), "s"(a.q_sM), "s"(a.q_sH), "s"(a.k_cache), "s"(a.v_cache),
+                 "s"(a.k_scale), "s"(a.v_scale), "s"(a.partials));
     const int s = blockIdx.x, bk = blockIdx.y;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
     // A page table of at most 64 pages per sequence is read whole, one entry
@@ -110,24 +115,14 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         const int l = (int)(threadIdx.x & 63);
         prow = a.page_table[(int64_t)b * a.pt_stride + (l < a.max_pages ? l : 0)];
     }
-    // context lengths beyond what the page table covers are clamped to it
-    const int ctx = min(scalar_ptr(a.ctx_lens)[b], a.max_pages * a.page);
-    if (ctx <= 0) return;
     const int G = a.Hq / a.Hkv, R = a.MTP * G;
-    const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
-    const int T = lo_b / kTile + s;
-    if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
-    const int t0 = T * kTile, last = ctx - 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, q4 = lane >> 4;
 
-    __shared__ __attribute__((aligned(16))) uint8_t kt_s[kTile * kD];
-    __shared__ __attribute__((aligned(16))) uint8_t vt_s[kTile * kD];
-    __shared__ __attribute__((aligned(16))) float kss[kTile], vss[kTile];
-
-    // ---- 1. this lane's Q slice: row r = 16 wave + c16, channels [32 q4, +32)
-    // (rows past R read row 0 of the head, in bounds, and are zeroed below)
+    // ---- 1. this lane's Q slice: row r = 16 wave + c16, channels [32 q4, +32),
+    // also in flight with the context length (rows past R read row 0 of the
+    // head, in bounds, and are zeroed below)
     const int r = 16 * wave + c16;
     const int mt = (r < R ? r : 0) / G, gq = (r < R ? r : 0) % G;
     uint4 qraw[4];
@@ -137,6 +132,24 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
         for (int i = 0; i < 4; ++i) qraw[i] = *(const uint4*)(qp + 8 * i);
     }
+    // The context length is loaded next and both are awaited here, so the Q
+    // loads cannot be moved below the early exits (after the length arrives).
+    const int ctx_raw = scalar_ptr(a.ctx_lens)[b];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        asm volatile("" : "+v"(qraw[i].x), "+v"(qraw[i].y), "+v"(qraw[i].z), "+v"(qraw[i].w) : "s"(ctx_raw));
+
+    // context lengths beyond what the page table covers are clamped to it
+    const int ctx = min(ctx_raw, a.max_pages * a.page);
+    if (ctx <= 0) return;
+    const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
+    const int T = lo_b / kTile + s;
+    if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
+    const int t0 = T * kTile, last = ctx - 1;
+
+    __shared__ __attribute__((aligned(16))) uint8_t kt_s[kTile * kD];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_s[kTile * kD];
+    __shared__ __attribute__((aligned(16))) float kss[kTile], vss[kTile];
 
     // ---- 2. page ids of the tile's page-blocks (scalar loads, all in flight
     // at once).  Page-block i is page t0 / page + i; a block that starts past
