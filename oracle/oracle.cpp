@@ -413,9 +413,12 @@ int64_t orc_qk_int8_exact(const int8_t* q8, const int8_t* k8, int D) {
 // Pins: with quantization off (ORC_QK_FLOAT, quant_pv = 0: x = fp32(S alpha),
 // p = exp2(x - m), out = O / l) it equals exact attention within 1e-6 and is
 // invariant to BN; with V = 1 the output is the row sum of P8 / l, which lies
-// within the e4m3 rounding bound of 1.  The quantized result itself has no
-// independent pin beyond those bounds (parity unpinned except against the HIP
-// path, by design of the method).
+// within the e4m3 rounding bound of 1; on inputs where every rounding step is
+// exact (integer scores in log2 units within 15 of the row max, power-of-two
+// or unit scales, codes equal to the values, K mean exactly 0) the quantized
+// INT8 and MXFP4 results equal base-2 attention on those scores, computed
+// independently in float64 (a dropped rescale, 448 factor, scale, mask or V
+// index each break it).
 
 namespace {
 
@@ -629,8 +632,12 @@ int orc_attn_exact(const float* q, const float* k, const float* v,
 // (fp32, split order); l == 0 -> 0.
 // Pins: float mode equals exact attention of the last MTP rows; page
 // permutation and split length do not change the float result; the split
-// count formula reproduces the page's 18 / 25 / 34.  Quant mode: parity
-// unpinned beyond those structural checks.
+// count formula reproduces the page's 18 / 25 / 34.  Quant mode: on inputs
+// where every rounding is exact (integer scores, power-of-two token scales,
+// e4m3-exact Q rows with a 448 and cache values) it equals base-2 attention
+// over each query's window with the per-token V scale applied, computed
+// independently in float64 (a wrong window bound, fold, score scale, merge
+// weight or query position each break it).
 
 int orc_decode_num_splits(int window, int mtp, int tile) {
     // Largest number of tile-aligned windows that W + MTP - 1 consecutive keys
