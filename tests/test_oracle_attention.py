@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+from tests._util import base2_attention, dyadic_prefill
+
 
 def _rand(shape, seed, scale=1.0):
     return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
@@ -190,45 +192,8 @@ def test_mxfp4_pipeline_against_exact(orc):
 
 
 # ---- quantized emulation on inputs where every rounding is exact -----------
-# With integer scores x (in log2 units), 448 * 2^(x - m) is an e4m3 value for
-# x - m >= -15, the rescale factors are powers of two, INT8 / MXFP4 / e4m3
-# codes of the chosen values are the values themselves (up to a power-of-two
-# or fixed scale), and the K mean is exactly 0.  The quantized pipeline must
-# then reproduce base-2 attention on the integer scores, written out below in
-# float64: a dropped or misplaced rescale, scale, mask or 448 factor changes
-# some weight by a power of two.
-
-def _base2_attention(x, v, causal):
-    """sum_j 2^x_ij v_j / sum_j 2^x_ij over visible j (j <= i when causal)."""
-    x = x.astype(np.float64)
-    if causal:
-        Lq, Lk = x.shape[-2:]
-        x = np.where(np.tril(np.ones((Lq, Lk), bool)), x, -np.inf)
-    w = 2.0 ** (x - x.max(-1, keepdims=True))
-    return (w @ v.astype(np.float64)) / w.sum(-1, keepdims=True)
-
-
-def _paired(rng, vals, shape):
-    """Draws from vals for the first half of the tokens (axis 2) and negates
-    them for the second half, so every channel sums to exactly 0."""
-    B, H, L, D = shape
-    half = rng.choice(vals, (B, H, L // 2, D))
-    return np.concatenate([half, -half], axis=2)
-
-
-def _dyadic_inputs(seed, L, D, q_vals, k_vals, q_amax_val, k_amax_val, n_score=3):
-    rng = np.random.default_rng(seed)
-    B, H = 1, 2
-    q = np.zeros((B, H, L, D), np.float32)
-    k = np.zeros((B, H, L, D), np.float32)
-    q[..., :n_score] = rng.choice(q_vals, (B, H, L, n_score))
-    k[..., :n_score] = _paired(rng, k_vals, (B, H, L, n_score))
-    q[..., n_score] = q_amax_val                       # Q's block amax; K is 0 there
-    k[..., n_score + 1] = k_amax_val * (1 - 2 * (np.arange(L) % 2))   # +-, mean 0; Q is 0 there
-    v = rng.choice(np.array([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0], np.float32), (B, H, L, D))
-    v[..., 0, :] = 4.0                                  # every channel's amax is 4
-    return q, k, v.astype(np.float32)
-
+# (tests._util.dyadic_prefill): a dropped or misplaced rescale, scale, mask or
+# 448 factor changes some weight by a power of two.
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("BN", [32, 64])
@@ -239,13 +204,13 @@ def test_int8_pipeline_exact_on_dyadic_inputs(orc, causal, BN):
     in {0, +-2, +-4} and k in {0, +-1}: integers in [-6, 6].  V in
     {0, +-1, +-2, +-4} with amax 4 (codes 112 v, v_scale 4 / 448)."""
     L, D = 200, 64
-    q, k, v = _dyadic_inputs(81, L, D, [0.0, 2.0, -2.0, 4.0, -4.0], [0.0, 1.0, -1.0], 254.0, 127.0)
+    q, k, v = dyadic_prefill(81, L, D, [0.0, 2.0, -2.0, 4.0, -4.0], [0.0, 1.0, -1.0], 254.0, 127.0)
     out, it = _tiny_int8(orc, q, k, v, causal, np.log(2.0) / 2, BN)
     assert np.all(it["mu"] == 0.0)
     assert np.all(it["q_scale"] == 2.0) and np.all(it["k_scale"] == 1.0)
     x = np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64)) / 2
     assert np.array_equal(x, np.round(x)) and np.abs(x).max() <= 6
-    ref = _base2_attention(x, v, causal)
+    ref = base2_attention(x, v, causal)
     assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max()
 
 
@@ -256,12 +221,12 @@ def test_mxfp4_pipeline_exact_on_dyadic_inputs(orc, causal):
     x = S alpha with alpha = 0.5 and S = q.k with q in {0, +-2}, k in
     {0, +-1, +-2}: integers in [-6, 6]."""
     L, D = 160, 64
-    q, k, v = _dyadic_inputs(82, L, D, [0.0, 2.0, -2.0], [0.0, 1.0, -1.0, 2.0, -2.0], 4.0, 4.0)
+    q, k, v = dyadic_prefill(82, L, D, [0.0, 2.0, -2.0], [0.0, 1.0, -1.0, 2.0, -2.0], 4.0, 4.0)
     out, it = orc.prefill_mxfp4_pipeline(q, k, v, causal=causal, sm_scale=np.log(2.0) / 2, BN=32,
                                          rotate_qk=False)
     assert np.all(it["mu"] == 0.0)
     assert np.all(it["q_e8"][..., 0] == 127) and np.all(it["k_e8"][..., 0] == 127)
     x = np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64)) / 2
     assert np.array_equal(x, np.round(x)) and np.abs(x).max() <= 6
-    ref = _base2_attention(x, v, causal)
+    ref = base2_attention(x, v, causal)
     assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max()

@@ -7,6 +7,8 @@ import os
 import numpy as np
 import pytest
 
+from tests._util import base2_decode, dyadic_decode
+
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -115,49 +117,17 @@ def test_quant_mode_close_to_exact(orc):
 
 @pytest.mark.parametrize("window,tile", [(0, 32), (20, 32), (0, 256)])
 def test_quant_mode_exact_on_dyadic_inputs(orc, window, tile):
-    """Quantized decode on inputs where every rounding is exact: each Q row has
-    a 448 (q_scale 1, codes = Q) in a channel where K is 0, scores use
-    channels where q is in {0, +-2} and k in {0, +-1}, k_scale in {1, 2} and
-    alpha = fp32(ln2 / 2 * log2 e) = 0.5, so x = q.k k_scale / 2 is an integer
-    in [-4, 4]; V codes are e4m3 values and v_scale in {1/2, 1, 2}, so the
-    folded P8 = e4m3(448 p v_scale / vmax) is exact.  The result must be
-    base-2 attention of those integer scores over each query's window, with
-    the per-token V scale applied: a wrong mask, fold, split or merge changes
-    some weight by a power of two."""
-    rng = np.random.default_rng(91)
-    B, MTP, Hq, Hkv, D, PS, max_pages = 2, 4, 4, 2, 32, 16, 8
-    P = B * max_pages
-    G = Hq // Hkv
+    """Quantized decode on inputs where every rounding is exact
+    (tests._util.dyadic_decode): the result must be base-2 attention of the
+    integer scores over each query's window with the per-token V scale
+    applied; a wrong mask, fold, split or merge changes some weight by a
+    power of two."""
+    MTP, Hq, Hkv = 4, 4, 2
     ctx = np.array([100, 57], np.int32)
-    q = np.zeros((B, MTP, Hq, D), np.float32)
-    q[..., :2] = rng.choice([0.0, 2.0, -2.0], (B, MTP, Hq, 2))
-    q[..., 2] = 448.0
-    kf = rng.choice(np.array([0.0, 1.0, -1.0, 0.5, 3.0], np.float32), (P, Hkv, PS, D))
-    kf[..., :2] = rng.choice([0.0, 1.0, -1.0], (P, Hkv, PS, 2))
-    kf[..., 2] = 0.0
-    vf = rng.choice(np.array([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -0.5], np.float32), (P, Hkv, PS, D))
-    ks = rng.choice(np.array([1.0, 2.0], np.float32), (P, Hkv, PS))
-    vs = rng.choice(np.array([0.5, 1.0, 2.0], np.float32), (P, Hkv, PS))
+    q, kf, vf, ks, vs, table = dyadic_decode(91, B=2, MTP=MTP, Hq=Hq, Hkv=Hkv, D=32, PS=16, max_pages=8)
     kc, vc = orc.e4m3_encode_array(kf), orc.e4m3_encode_array(vf)
     assert np.array_equal(orc.e4m3_decode_array(kc), kf) and np.array_equal(orc.e4m3_decode_array(vc), vf)
-    table = rng.permutation(P).astype(np.int32).reshape(B, max_pages)
     out = orc.paged_decode(q, kc, vc, ks, vs, table, ctx, window=window, sm_scale=np.log(2.0) / 2,
                            tile=tile)
-    ref = np.zeros_like(out, dtype=np.float64)
-    for b in range(B):
-        pages = table[b]
-        kt = kf[pages].transpose(1, 0, 2, 3).reshape(Hkv, -1, D)    # [Hkv, tokens, D]
-        vt = vf[pages].transpose(1, 0, 2, 3).reshape(Hkv, -1, D)
-        kst = ks[pages].transpose(1, 0, 2).reshape(Hkv, -1)
-        vst = vs[pages].transpose(1, 0, 2).reshape(Hkv, -1)
-        for m in range(MTP):
-            pos = ctx[b] - MTP + m
-            lo = max(0, pos - window + 1) if window > 0 else 0
-            for hq in range(Hq):
-                hk = hq // G
-                t = np.arange(lo, pos + 1)
-                x = (kt[hk, t].astype(np.float64) @ q[b, m, hq].astype(np.float64)) * kst[hk, t] / 2
-                assert np.array_equal(x, np.round(x)) and np.abs(x).max() <= 4
-                w = 2.0 ** (x - x.max())
-                ref[b, m, hq] = (w * vst[hk, t]) @ vt[hk, t].astype(np.float64) / w.sum()
+    ref = base2_decode(q, kf, vf, ks, vs, table, ctx, window, Hkv)
     assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max()
