@@ -106,6 +106,8 @@ def _declare(L):
     L.orc_decode_num_splits.argtypes = [i32, i32, i32]; L.orc_decode_num_splits.restype = i32
     L.orc_paged_decode.argtypes = [ctypes.POINTER(DecodeParams), _P, _P, _P, _P, _P, _P, _P, _P]
     L.orc_paged_decode.restype = i32
+    L.orc_paged_decode_mx.argtypes = [ctypes.POINTER(DecodeParams), _P, _P, _P, _P, _P, _P, _P, _P]
+    L.orc_paged_decode_mx.restype = i32
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -318,6 +320,26 @@ def paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *,
                                 _ptr(vs), _ptr(pt), _ptr(cl), _ptr(out))
     if rc != 0:
         raise ValueError(f"orc_paged_decode failed ({rc})")
+    return out
+
+
+def paged_decode_mx(q, k_codes, k_e8, v_codes, v_e8, page_table, ctx_lens, *, window, sm_scale,
+                    tile=256, nthreads=0) -> np.ndarray:
+    """MXFP4 KV cache, one E2M1 code per byte: k_codes [P, Hkv, page, D],
+    k_e8 [P, Hkv, page, D/32]; V transposed: v_codes [P, Hkv, D, page],
+    v_e8 [P, Hkv, D, page/32]; q [B, MTP, Hq, D] float32."""
+    q = _c(q, np.float32)
+    B, MTP, Hq, D = q.shape
+    P, Hkv, PS, _ = k_codes.shape
+    kc, ke, vc, ve = (_c(a, np.uint8) for a in (k_codes, k_e8, v_codes, v_e8))
+    pt, cl = _c(page_table, np.int32), _c(ctx_lens, np.int32)
+    prm = DecodeParams(B, MTP, Hq, Hkv, D, PS, pt.shape[1], P, window, tile, float(sm_scale), 1,
+                       nthreads)
+    out = np.empty((B, MTP, Hq, D), dtype=np.float32)
+    rc = lib().orc_paged_decode_mx(ctypes.byref(prm), _ptr(q), _ptr(kc), _ptr(ke), _ptr(vc), _ptr(ve),
+                                   _ptr(pt), _ptr(cl), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"orc_paged_decode_mx failed ({rc})")
     return out
 
 

@@ -768,4 +768,126 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
     return bad ? -2 : 0;
 }
 
+// Paged decode over an MXFP4 KV cache ([aiter #7388] names pa_decode_mxfp4:
+// E2M1 KV with E8M0 scales, e4m3 queries and P, FP8_MAX of E4M3).
+// READING (the page fixes no layout): K keeps one E8M0 scale per 32 channels
+// of each token (the QK reduction axis); V is stored transposed with one
+// scale per 32 consecutive keys of each channel (the PV reduction axis), so
+// each block scale multiplies a whole 32-term partial sum.  Per split and
+// query row, with the fp8 path's window, split and merge:
+//   Q -> e4m3 per (token, head) row as in orc_paged_decode;
+//   dot = sum over 32-channel blocks of 2^(e_k - 127) * sum dec(Q8) e2m1(K)
+//         (exact), x = fp32(fp32(fp32(dot) * q_scale) * alpha);
+//   m_s = max x, p = exp2(x - m_s), l_s = sum p (fp32, key order);
+//   P8 = e4m3(fp32(448 p));
+//   O_s[d] = fp32(fp32(sum_t dec(P8_t) e2m1(V[d, t]) 2^(e_v[d, t/32] - 127))
+//            * fp32(1/448)) with the split's sum exact.
+// Pin: on caches whose dequantized values are e4m3 values, with unit
+// per-token scales, it equals orc_paged_decode's quantized mode bit for bit.
+int orc_paged_decode_mx(const orc_decode_params* p, const float* q,
+                        const uint8_t* k_codes, const uint8_t* k_e8,
+                        const uint8_t* v_codes, const uint8_t* v_e8,
+                        const int32_t* page_table, const int32_t* ctx_lens, float* out) {
+    if (!p || p->Hkv <= 0 || p->Hq % p->Hkv || p->tile <= 0 || p->D % 32 || p->page_size % 32) return -1;
+    const int D = p->D, PS = p->page_size;
+    const float alpha = (float)(p->sm_scale * kLog2e);
+    const float inv448 = 1.0f / 448.0f;
+    const int group = p->Hq / p->Hkv;
+    const int64_t nrows = (int64_t)p->B * p->MTP * p->Hq;
+    float dec[256];
+    for (int c = 0; c < 256; ++c) dec[c] = orc_e4m3_decode((uint8_t)c);
+    std::atomic<int> bad{0};
+    parallel_for(nrows, p->nthreads, [&](int64_t r) {
+        const int hq = (int)(r % p->Hq);
+        const int m = (int)((r / p->Hq) % p->MTP);
+        const int b = (int)(r / ((int64_t)p->Hq * p->MTP));
+        const int hk = hq / group;
+        const int ctx = ctx_lens[b];
+        const int pos = ctx - p->MTP + m;
+        const int lo_row = p->window > 0 ? std::max(0, pos - p->window + 1) : 0;
+        const int lo_b = p->window > 0 ? std::max(0, ctx - p->MTP - p->window + 1) : 0;
+        const float* qr = q + r * D;
+        float* o = out + r * D;
+
+        // (page, KV head) of key t, or -1 for an invalid page id
+        auto page_of = [&](int t) -> int64_t {
+            int pg = page_table[(int64_t)b * p->max_pages + t / PS];
+            if (pg < 0 || pg >= p->num_pages) return -1;
+            return (int64_t)pg * p->Hkv + hk;
+        };
+
+        std::vector<uint8_t> q8(D);
+        float q_s = 0.0f;
+        {
+            float amax = 0.0f;
+            for (int d = 0; d < D; ++d) amax = std::max(amax, std::fabs(qr[d]));
+            float inv = 0.0f;
+            if (amax > 0.0f) { inv = 448.0f / amax; q_s = amax / 448.0f; }
+            for (int d = 0; d < D; ++d) q8[d] = orc_e4m3_encode(qr[d] * inv);
+        }
+
+        std::vector<float> ms, ls;
+        std::vector<std::vector<float>> Os;
+        if (ctx > 0) {
+            const int t_first = lo_b / p->tile, t_last = (ctx - 1) / p->tile;
+            for (int T = t_first; T <= t_last; ++T) {
+                const int k0 = std::max(T * p->tile, lo_b), k1 = std::min((T + 1) * p->tile, ctx);
+                const int r0 = std::max(k0, lo_row), r1 = std::min(k1, pos + 1);
+                std::vector<float> Osp(D, 0.0f);
+                if (r0 >= r1) { ms.push_back(-INFINITY); ls.push_back(0.0f); Os.push_back(Osp); continue; }
+                std::vector<float> x(r1 - r0), pr(r1 - r0);
+                float mx = -INFINITY;
+                for (int t = r0; t < r1; ++t) {
+                    const int64_t ph = page_of(t);
+                    if (ph < 0) { bad = 1; return; }
+                    const int64_t row = ph * PS + t % PS;
+                    const uint8_t* kr = k_codes + row * D;
+                    const uint8_t* ke = k_e8 + row * (D / 32);
+                    double dot = 0.0;
+                    for (int bl = 0; bl < D / 32; ++bl) {
+                        double part = 0.0;
+                        for (int d = 32 * bl; d < 32 * bl + 32; ++d)
+                            part += (double)dec[q8[d]] * (double)orc_e2m1_decode(kr[d]);
+                        dot += std::ldexp(part, (int)ke[bl] - 127);
+                    }
+                    const float xv = ((float)dot * q_s) * alpha;
+                    x[t - r0] = xv;
+                    mx = std::max(mx, xv);
+                }
+                float l = 0.0f;
+                for (int t = r0; t < r1; ++t) {
+                    pr[t - r0] = exp2_f32(x[t - r0] - mx);
+                    l = l + pr[t - r0];
+                }
+                std::vector<double> acc(D, 0.0);
+                for (int t = r0; t < r1; ++t) {
+                    const double pv = dec[orc_e4m3_encode(448.0f * pr[t - r0])];
+                    if (pv == 0.0) continue;
+                    const int64_t ph = page_of(t);
+                    const int s = t % PS;
+                    for (int d = 0; d < D; ++d) {
+                        const int64_t vrow = ph * D + d;
+                        const double v = std::ldexp((double)orc_e2m1_decode(v_codes[vrow * PS + s]),
+                                                    (int)v_e8[vrow * (PS / 32) + s / 32] - 127);
+                        acc[d] += pv * v;
+                    }
+                }
+                for (int d = 0; d < D; ++d) Osp[d] = (float)acc[d] * inv448;
+                ms.push_back(mx); ls.push_back(l); Os.push_back(Osp);
+            }
+        }
+        float mstar = -INFINITY;
+        for (float v : ms) mstar = std::max(mstar, v);
+        float L = 0.0f;
+        std::vector<float> acc(D, 0.0f);
+        for (size_t s = 0; s < ms.size(); ++s) {
+            float w = (ms[s] == -INFINITY) ? 0.0f : exp2_f32(ms[s] - mstar);
+            L = L + w * ls[s];
+            for (int d = 0; d < D; ++d) acc[d] = acc[d] + w * Os[s][d];
+        }
+        for (int d = 0; d < D; ++d) o[d] = L > 0.0f ? acc[d] / L : 0.0f;
+    });
+    return bad ? -2 : 0;
+}
+
 }  // extern "C"

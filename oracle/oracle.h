@@ -107,6 +107,14 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
                      const void* k_cache, const void* v_cache,
                      const float* k_scale, const float* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* out);
+/* MXFP4 KV cache (E2M1 codes, one per byte, and E8M0 block scales):
+ * k_codes [P, Hkv, page, D], k_e8 [P, Hkv, page, D/32] (blocks along D);
+ * v_codes [P, Hkv, D, page], v_e8 [P, Hkv, D, page/32] (V transposed, blocks
+ * along the keys).  p->quant is ignored (Q and P are always e4m3). */
+int orc_paged_decode_mx(const orc_decode_params* p, const float* q,
+                        const uint8_t* k_codes, const uint8_t* k_e8,
+                        const uint8_t* v_codes, const uint8_t* v_e8,
+                        const int32_t* page_table, const int32_t* ctx_lens, float* out);
 
 #ifdef __cplusplus
 }

@@ -131,3 +131,41 @@ def test_quant_mode_exact_on_dyadic_inputs(orc, window, tile):
                            tile=tile)
     ref = base2_decode(q, kf, vf, ks, vs, table, ctx, window, Hkv)
     assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def _mx_cache(seed, P, Hkv, PS, D):
+    """Random MXFP4 KV cache (one E2M1 code per byte) with exponents in
+    [124, 130], and its dequantized K [P, Hkv, PS, D] and V [P, Hkv, PS, D]."""
+    from oracle import e2m1_decode
+    rng = np.random.default_rng(seed)
+    vals = np.array([e2m1_decode(c) for c in range(16)], np.float64)
+    kc = rng.integers(0, 16, (P, Hkv, PS, D)).astype(np.uint8)
+    ke = rng.integers(124, 131, (P, Hkv, PS, D // 32)).astype(np.uint8)
+    vc = rng.integers(0, 16, (P, Hkv, D, PS)).astype(np.uint8)          # V transposed
+    ve = rng.integers(124, 131, (P, Hkv, D, PS // 32)).astype(np.uint8)
+    kf = vals[kc] * np.repeat(2.0 ** (ke.astype(np.float64) - 127), 32, axis=-1)
+    vf = (vals[vc] * np.repeat(2.0 ** (ve.astype(np.float64) - 127), 32, axis=-1)).transpose(0, 1, 3, 2)
+    return kc, ke, vc, ve, kf.astype(np.float32), np.ascontiguousarray(vf).astype(np.float32)
+
+
+@pytest.mark.parametrize("D,PS,window,tile", [(128, 64, 0, 256), (128, 32, 40, 64), (64, 64, 0, 32)])
+def test_mx_decode_equals_fp8_decode_on_shared_values(orc, D, PS, window, tile):
+    """E2M1 values times 2^(e - 127) for e in [124, 130] are e4m3 values, so
+    an MXFP4 cache has an exact e4m3 twin with unit per-token scales; on it
+    the FP8 path computes the same scores, P8 and products (its vmax is 1),
+    and the two oracles must agree bit for bit."""
+    B, MTP, Hq, Hkv, max_pages = 2, 4, 4, 2, 6
+    P = B * max_pages
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((B, MTP, Hq, D)).astype(np.float32)
+    kc, ke, vc, ve, kf, vf = _mx_cache(8, P, Hkv, PS, D)
+    k8, v8 = orc.e4m3_encode_array(kf), orc.e4m3_encode_array(vf)
+    assert np.array_equal(orc.e4m3_decode_array(k8), kf) and np.array_equal(orc.e4m3_decode_array(v8), vf)
+    table = rng.permutation(P).astype(np.int32).reshape(B, max_pages)
+    ctx = np.array([max_pages * PS - 5, 3 * PS + 7], np.int32)
+    ones = np.ones((P, Hkv, PS), np.float32)
+    common = dict(window=window, sm_scale=D ** -0.5, tile=tile)
+    a = orc.paged_decode_mx(q, kc, ke, vc, ve, table, ctx, **common)
+    b = orc.paged_decode(q, k8, v8, ones, ones, table, ctx, **common)
+    assert np.array_equal(a, b)
+    assert np.abs(a).max() > 0
