@@ -154,7 +154,9 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
                           "traffic": _traffic(f"attn_fwd_{wname}", src)})
 
 
-def decode_bench(steps, warmup, dev, pools=32):
+def decode_bench(steps, warmup, dev, pools=32, mx=False):
+    """mx: the same decode over an MXFP4 cache (E2M1 + E8M0, the next step the
+    aiter page names), timed the same way."""
     from quantized_attention_block_amd import sage
     from quantized_attention_block_amd import workloads as wl
     w = wl.WORKLOADS["paged_decode"]
@@ -162,6 +164,15 @@ def decode_bench(steps, warmup, dev, pools=32):
     # come from HBM, not the MALL
     sets = []
     for i in range(pools):
+        if mx:
+            inp = wl.make_decode_mx(w, pool_seed=i)
+            k4, v4 = inp.packed()
+            sets.append(dict(
+                q=inp.q.to(dev), k=k4.to(dev).view(torch.float4_e2m1fn_x2),
+                v=v4.to(dev).view(torch.float4_e2m1fn_x2), ks=inp.k_e8.to(dev).view(torch.float8_e8m0fnu),
+                vs=inp.v_e8.to(dev).view(torch.float8_e8m0fnu), pt=inp.page_table.to(dev),
+                ctx=inp.ctx_lens.to(dev)))
+            continue
         inp = wl.make_decode(w, pool_seed=i)
         sets.append(dict(
             q=inp.q.to(dev), k=inp.k_cache.to(dev).view(torch.float8_e4m3fn),
@@ -197,16 +208,22 @@ def decode_bench(steps, warmup, dev, pools=32):
     t = min(_events_time(graph.replay, max(10, steps), stream) for _ in range(5)) / pools
     t_eager = _events_time(call, 200, stream)
     keys = min(w.ctx, w.window + w.mtp - 1)
-    alg_bytes = w.batch * w.hkv * keys * (2 * w.D + 8) + 2 * (w.batch * w.mtp * w.hq * w.D * 2)
+    # bytes per key and KV head: K and V codes plus their scales (e4m3: D + D
+    # bytes and two fp32; MXFP4: D/2 + D/2 bytes and D/32 + D/32 E8M0 bytes)
+    per_key = (w.D + w.D // 16) if mx else (2 * w.D + 8)
+    alg_bytes = w.batch * w.hkv * keys * per_key + 2 * (w.batch * w.mtp * w.hq * w.D * 2)
     gbs = alg_bytes / t / 1e9
-    return {"metric": "paged FP8 decode HBM GB/s (decode + merge)", "value": round(gbs, 1),
+    fmt = "MXFP4 (E2M1 + E8M0)" if mx else "FP8"
+    return {"metric": f"paged {fmt} decode HBM GB/s (decode + merge)", "value": round(gbs, 1),
             "unit": "GB/s", "us_per_call": round(t * 1e6, 3),
             "us_per_call_eager_launch": round(t_eager * 1e6, 2), "algorithmic_bytes": alg_bytes,
-            "workload": "batch16 MTP4 GQA16 D128 page128 ctx8192 window4096 fp8-e4m3 per-token",
+            "workload": "batch16 MTP4 GQA16 D128 page128 ctx8192 window4096 " +
+                        ("mxfp4 E8M0 per 32 (K: channels, V: keys)" if mx else "fp8-e4m3 per-token"),
             "kv_pools_rotated": pools,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": _traffic("paged_decode", ["decode.hip", "sage_device.hpp"])}}
+                         "traffic": _traffic("paged_decode_mxfp4" if mx else "paged_decode",
+                                             ["decode.hip", "sage_device.hpp"])}}
 
 
 def cpu_baseline(wname, target_s=15.0):
@@ -275,6 +292,7 @@ def main():
              "ms_per_step_hip_graph": round(r["t_step_graph"] * 1e3, 4)}
     if not args.no_decode:
         extra["paged_decode"] = decode_bench(args.steps, args.warmup, dev)
+        extra["paged_decode_mxfp4"] = decode_bench(args.steps, args.warmup, dev, mx=True)
     if args.all:
         for wn in ("video_dit", "video_dit_mxfp4"):
             rr = prefill_bench(wn, max(3, args.steps // 4), 2, dev)

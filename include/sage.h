@@ -220,6 +220,17 @@ int32_t sage_attn_kv_tile(void);
  * params.max_ctx; device data is not validated, but a page id outside
  * [0, P) reads page 0 and a length beyond the page table's coverage is
  * clamped to it, so bad device data gives wrong numbers, never a fault.
+ * MXFP4 cache ([aiter #7388] names pa_decode_mxfp4: E2M1 KV, E8M0 scales;
+ * the layout is this library's reading), chosen by k_cache's dtype:
+ *   k_cache FP4X2_E2M1 [P, Hkv, page, D/2], k_scale E8M0 [P, Hkv, page, D/32]
+ *           (one scale per 32 channels of a token: the QK reduction axis)
+ *   v_cache FP4X2_E2M1 [P, Hkv, D, page/2] (transposed; key 2i in the low
+ *           nibble), v_scale E8M0 [P, Hkv, D, page/32] (one scale per 32 keys
+ *           of a channel: the PV reduction axis)
+ * QK and PV run on the block-scaled MFMA with these scales, P8 =
+ * e4m3(448 p); the page size must be a multiple of 64, and the V scale of
+ * every 32-key block that holds a key below ctx_lens[b] must be set (blocks
+ * wholly past it are ignored).
  */
 typedef struct {
     float sm_scale;        /* <= 0: 1/sqrt(D)                  */

@@ -500,11 +500,12 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     sage_status st = decode_query(q, page_table, p, &s);
     if (st) return st;
     if ((st = check_basic(k_cache, "k_cache", 4))) return st;
-    if ((st = check_fp8(k_cache, "k_cache"))) return st;
+    const bool mx = k_cache->dtype == SAGE_FP4X2_E2M1;   // MXFP4 cache: E2M1 codes + E8M0 scales
+    if (!mx && (st = check_fp8(k_cache, "k_cache"))) return st;
     if ((st = check_basic(v_cache, "v_cache", 4))) return st;
-    if ((st = check_fp8(v_cache, "v_cache"))) return st;
+    if (!mx && (st = check_fp8(v_cache, "v_cache"))) return st;
     const int P = (int)k_cache->shape[0], Hkv = (int)k_cache->shape[1], page = (int)k_cache->shape[2];
-    if (k_cache->shape[3] != s.D) return fail(SAGE_ERR_SHAPE, "k_cache head dim differs from q");
+    if (k_cache->shape[3] != (mx ? s.D / 2 : s.D)) return fail(SAGE_ERR_SHAPE, "k_cache head dim differs from q");
     if (s.D != 128) return fail(SAGE_ERR_UNSUPPORTED, "decode head dim must be 128");
     if (Hkv < 1 || s.Hq % Hkv) return fail(SAGE_ERR_SHAPE, "query heads %d not a multiple of KV heads %d", s.Hq, Hkv);
     const int G = s.Hq / Hkv;
@@ -513,11 +514,21 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
         return fail(SAGE_ERR_UNSUPPORTED, "page size %d: need a multiple of 32 that divides 256 or is a multiple of 256", page);
     if (P < 1) return fail(SAGE_ERR_SHAPE, "empty KV pool");
     if (!p->v_transposed) return fail(SAGE_ERR_UNSUPPORTED, "only the transposed V cache [P, Hkv, D, page] is implemented");
-    const int64_t ks[4] = {P, Hkv, page, s.D}, vt[4] = {P, Hkv, s.D, page}, ss[3] = {P, Hkv, page};
-    if ((st = check_exact(k_cache, "k_cache", SAGE_FP8_E4M3FN, 4, ks))) return st;
-    if ((st = check_exact(v_cache, "v_cache", SAGE_FP8_E4M3FN, 4, vt))) return st;
-    if ((st = check_exact(k_scale, "k_scale", SAGE_F32, 3, ss))) return st;
-    if ((st = check_exact(v_scale, "v_scale", SAGE_F32, 3, ss))) return st;
+    if (mx) {
+        if (page % 64) return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 cache: page size %d is not a multiple of 64", page);
+        const int64_t ks[4] = {P, Hkv, page, s.D / 2}, vt[4] = {P, Hkv, s.D, page / 2};
+        const int64_t kse[4] = {P, Hkv, page, s.D / 32}, vse[4] = {P, Hkv, s.D, page / 32};
+        if ((st = check_exact(k_cache, "k_cache", SAGE_FP4X2_E2M1, 4, ks))) return st;
+        if ((st = check_exact(v_cache, "v_cache", SAGE_FP4X2_E2M1, 4, vt))) return st;
+        if ((st = check_exact(k_scale, "k_scale", SAGE_E8M0, 4, kse))) return st;
+        if ((st = check_exact(v_scale, "v_scale", SAGE_E8M0, 4, vse))) return st;
+    } else {
+        const int64_t ks[4] = {P, Hkv, page, s.D}, vt[4] = {P, Hkv, s.D, page}, ss[3] = {P, Hkv, page};
+        if ((st = check_exact(k_cache, "k_cache", SAGE_FP8_E4M3FN, 4, ks))) return st;
+        if ((st = check_exact(v_cache, "v_cache", SAGE_FP8_E4M3FN, 4, vt))) return st;
+        if ((st = check_exact(k_scale, "k_scale", SAGE_F32, 3, ss))) return st;
+        if ((st = check_exact(v_scale, "v_scale", SAGE_F32, 3, ss))) return st;
+    }
     if (page_table->shape[1] > 1 && page_table->stride[1] != 1)
         return fail(SAGE_ERR_LAYOUT, "page_table rows must be contiguous");
     if ((int64_t)page_table->shape[1] * page < p->max_ctx)
@@ -568,6 +579,7 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     a.window = p->window;
     a.v_transposed = p->v_transposed;
     a.num_splits = s.splits;
+    a.mx = mx ? 1 : 0;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)s.D));
     a.partials = (float*)workspace;
     return launch_status(sage::launch_paged_decode(a, (hipStream_t)stream), "paged decode");

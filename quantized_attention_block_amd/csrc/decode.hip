@@ -77,6 +77,25 @@ __device__ __forceinline__ float2 unpack_h2(uint32_t w) {
 // chunks, so the pass touches 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int dk_swz(int key) { return ((key >> 5) & 3) | (((key >> 1) & 1) << 2); }
 
+// MX K tile [256 keys][64 B]: one read pass fetches keys {16 a + 4 m + b}
+// (a, b in 0..3, see kx) at one of the 4 chunks; 4 rows share a bank sweep,
+// and the XOR with key bits 4-5 (= a) separates the 4 sweeps.
+__device__ __forceinline__ int dk_swz_mx(int key) { return (key >> 4) & 3; }
+
+// Key (within a 128-key group) of element i of S^T MFMA m in lane group q4,
+// which is also byte 4 m + i of that lane group's PV B operand.  e4m3:
+// 32 q4 + 4 m + i.  MX: the block-scaled MFMA pairs nibble j of an E2M1
+// operand's lane group G with byte b of an e4m3 operand's lane group G' where
+// 32 G' + b = 64 (G & 1) + 32 (j / 16) + 16 (G >> 1) + j % 16 (measured on
+// gfx950); for the E2M1 lane group q4 to hold the 32 consecutive keys (or
+// channels) [32 q4, +32) of one MX block, e4m3 byte b of lane group q4 must
+// hold 16 q4 + b (b < 16) or 64 + 16 q4 + b - 16 (b >= 16).
+template <bool MX>
+__device__ __forceinline__ int kx(int q4, int m, int i) {
+    if constexpr (MX) return (m < 4 ? 16 * q4 + 4 * m : 64 + 16 * q4 + 4 * (m - 4)) + i;
+    else return 32 * q4 + 4 * m + i;
+}
+
 // LDS V^T tile [page-block][128 d][PW keys], PW = min(page, 256), n = PW / 16
 // chunks per row (n = 2^LGN): chunk c of row d is stored at c ^ dv_swz(d).
 // One read pass fetches 16 consecutive rows at one chunk; 16 / n rows share a
@@ -95,10 +114,16 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* scalar_ptr
 
 // PW: keys per page-block, min(page, 256) (a page of at most 256 keys divides
 // 256; a larger page holds the whole tile at offset t0 % page).
-template <int PW>
+// MX: MXFP4 cache (E2M1 codes two per byte, E8M0 scales per 32 channels of
+// each K row and per 32 keys of each V^T row), QK and PV on the block-scaled
+// MFMA with the cache's scales; otherwise e4m3 with per-token fp32 scales.
+template <int PW, bool MX>
 __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float alpha) {
+    static_assert(!MX || PW >= 64, "MXFP4 pages of 64 keys or more");
     constexpr int kNpb = kTile / PW;                 // page-blocks per tile
     constexpr int kLgn = PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
+    constexpr int kRowB = MX ? kD / 2 : kD;          // bytes of one K row / of 256 keys of a V^T row
+    constexpr int kVLgn = MX ? kLgn - 1 : kLgn;      // log2 of 16-byte chunks per V^T row of a page-block
     // Every kernel argument the block uses is read at entry, in one batch:
     // left to itself the compiler loads the pointers only after the context
     // length has arrived, one more round trip before the tile copies start.
@@ -127,10 +152,15 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     const int mt = (r < R ? r : 0) / G, gq = (r < R ? r : 0) % G;
     uint4 qraw[4];
     {
+        // channels [32 q4, +32); MX: [16 q4, +16) and [64 + 16 q4, +16) (the
+        // e4m3 operand's byte order that meets the E2M1 operand's, see kx)
         const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM +
-                             (int64_t)(hk * G + gq) * a.q_sH + 32 * q4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qraw[i] = *(const uint4*)(qp + 8 * i);
+                             (int64_t)(hk * G + gq) * a.q_sH;
+        const int c0 = MX ? 16 * q4 : 32 * q4, c1 = MX ? 64 + 16 * q4 : 32 * q4 + 16;
+        qraw[0] = *(const uint4*)(qp + c0);
+        qraw[1] = *(const uint4*)(qp + c0 + 8);
+        qraw[2] = *(const uint4*)(qp + c1);
+        qraw[3] = *(const uint4*)(qp + c1 + 8);
     }
     // The context length is loaded next and both are awaited here, so the Q
     // loads cannot be moved below the early exits (after the length arrives).
@@ -147,8 +177,11 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
     const int t0 = T * kTile, last = ctx - 1;
 
+    // (sized for e4m3; MX uses the first half of each.  A size that depends
+    // on the template arguments leaves the host-side launch stub undefined.)
     __shared__ __attribute__((aligned(16))) uint8_t kt_s[kTile * kD];
     __shared__ __attribute__((aligned(16))) uint8_t vt_s[kTile * kD];
+    // per-token fp32 scales; MX: the E8M0 bytes ([key][D/32] and [page-block][d][PW/32])
     __shared__ __attribute__((aligned(16))) float kss[kTile], vss[kTile];
 
     // ---- 2. page ids of the tile's page-blocks (scalar loads, all in flight
@@ -166,23 +199,54 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
     for (int i = 0; i < kNpb; ++i) pid[i] = (unsigned)pid[i] < (unsigned)a.num_pages ? pid[i] : 0;
 
-    // per-token scales of key t0 + tid (issued before the copies)
+    // per-token scales of key t0 + tid (issued before the copies); MX: the
+    // four E8M0 bytes of K row t0 + tid, and dword tid of the tile's V^T
+    // scale bytes laid out [page-block][d][PW / 32]
     float ks, vs;
     {
         const int pbs = tid / PW;
         int pg = pid[0];
 #pragma unroll
         for (int i = 1; i < kNpb; ++i) pg = pbs == i ? pid[i] : pg;
-        const int64_t o = ((int64_t)pg * a.Hkv + hk) * a.page + (koff + tid % PW);
-        ks = a.k_scale[o];
-        vs = a.v_scale[o];
+        const int64_t ph = (int64_t)pg * a.Hkv + hk;
+        const int64_t o = ph * a.page + (koff + tid % PW);
+        if constexpr (MX) {
+            ks = __builtin_bit_cast(float, ((const uint32_t*)a.k_scale)[o]);
+            const int wb = 4 * (tid % PW);                     // byte of the page-block's [d][PW / 32]
+            const int d = wb / (PW / 32), col = wb % (PW / 32);
+            const uint8_t* vsb = (const uint8_t*)a.v_scale + ph * kD * (a.page / 32);
+            vs = __builtin_bit_cast(float, *(const uint32_t*)(vsb + d * (a.page / 32) + koff / 32 + col));
+        } else {
+            ks = a.k_scale[o];
+            vs = a.v_scale[o];
+        }
     }
 
-    // ---- 3. tile copies: 8 K and 8 V^T instructions per wave, 1 KB each.
-    // Instruction i = wave + 4 j fills LDS chunks [64 i, +64) of each tile;
-    // both tiles hold 128 n chunks per page-block (n = PW / 16), so it lies in
-    // page-block (wave + 4 j) / (2 n) = j >> (log2 n - 1), a constant.
-    const int kpage = a.page * kD;                   // bytes of one page of one KV head
+    // ---- 3. tile copies: 8 K and 8 V^T instructions per wave, 1 KB each
+    // (MX: 4 and 4).  Instruction i = wave + 4 j fills LDS chunks [64 i, +64)
+    // of each tile; both tiles hold 128 n chunks per page-block (n = PW / 16
+    // chunks per V^T row; MX: PW / 32), so it lies in page-block
+    // (wave + 4 j) / (2 n), a constant.
+    const int kpage = a.page * kRowB;                // bytes of one page of one KV head
+    if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = wave + 4 * j;
+            const int pg = pid[j >> (kLgn - 2)];   // page-block 16 i / PW (PW >= 64)
+            // K: keys [16 i, +16) of the tile, 4 chunks each
+            const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+            const int key = 16 * i + (lane >> 2);
+            const int kc = (lane & 3) ^ dk_swz_mx(key);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + 1024 * i, 16,
+                                                     (koff + key % PW) * kRowB + 16 * kc, 0, 0, 0);
+            // V^T: rows d of page-block (i >> (log2 n + 1)), chunks c
+            const int within = ((64 * i) & ((128 << kVLgn) - 1)) + lane;
+            const int d = within >> kVLgn, c = (within & ((1 << kVLgn) - 1)) ^ dv_swz<kVLgn>(d);
+            const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16, d * (a.page / 2) + koff / 2 + 16 * c,
+                                                     0, 0, 0);
+        }
+    } else
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int i = wave + 4 * j;
@@ -234,13 +298,32 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     }
 
     const int kpos_s = t0 + tid;
-    kss[tid] = kpos_s < ctx ? ks : 0.0f;
-    vss[tid] = kpos_s < ctx ? vs : 0.0f;
+    if constexpr (MX) {   // E8M0 bytes as loaded (K rows past ctx are masked later)
+        kss[tid] = ks;
+        vss[tid] = vs;
+    } else {
+        kss[tid] = kpos_s < ctx ? ks : 0.0f;
+        vss[tid] = kpos_s < ctx ? vs : 0.0f;
+    }
     __syncthreads();   // every wave's copies have landed (vmcnt(0)) and the scales are in LDS
 
-    // the tile's largest V scale over keys inside [lo_b, ctx)
+    // the tile's largest V scale over keys inside [lo_b, ctx); MX: the largest
+    // V^T block exponent em of blocks that start before ctx (it bounds |V|)
     float vmax;
-    {
+    int em = 0;
+    if constexpr (MX) {
+        const uint4 w4 = *(const uint4*)((const uint8_t*)vss + 16 * lane);
+        const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int bi = 16 * lane + i;                       // byte of [page-block][d][PW / 32]
+            const int pb = bi / (kD * (PW / 32)), col = bi % (PW / 32);
+            const int e = (int)((wv[i / 4] >> (8 * (i % 4))) & 0xFFu);
+            em = t0 + pb * PW + 32 * col < ctx ? max(em, e) : em;
+        }
+        em = (int)wave_max((float)em);
+        vmax = __builtin_ldexpf(1.0f, em - 127);
+    } else {
         const float4 v4 = *(const float4*)&vss[4 * lane];
         const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
         float vm = 0.0f;
@@ -259,13 +342,22 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const int key = 128 * g + 32 * (c16 >> 2) + 4 * m + (c16 & 3);   // A row c16
-            const int sw = dk_swz(key);
-            const uint8_t* krow = kt_s + key * kD;
-            const v4i lo = *(const v4i*)(krow + 16 * ((2 * q4) ^ sw));
-            const v4i hi = *(const v4i*)(krow + 16 * ((2 * q4 + 1) ^ sw));
-            S[g][m] = mfma_f8_16x16x128(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf,
-                                        v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            const int key = 128 * g + kx<MX>(c16 >> 2, m, c16 & 3);   // A row c16
+            if constexpr (MX) {
+                // channels [32 q4, +32) of K row key: 16 bytes of E2M1 and the
+                // row's E8M0 byte for that block
+                const v4i k4 = *(const v4i*)(kt_s + key * kRowB + 16 * (q4 ^ dk_swz_mx(key)));
+                const int sk = (int)((const uint8_t*)kss)[4 * key + q4];
+                S[g][m] = mfma_f4f8_16x16x128(__builtin_shufflevector(k4, k4, 0, 1, 2, 3, -1, -1, -1, -1), qf,
+                                              v4f{0.0f, 0.0f, 0.0f, 0.0f}, sk);
+            } else {
+                const int sw = dk_swz(key);
+                const uint8_t* krow = kt_s + key * kD;
+                const v4i lo = *(const v4i*)(krow + 16 * ((2 * q4) ^ sw));
+                const v4i hi = *(const v4i*)(krow + 16 * ((2 * q4 + 1) ^ sw));
+                S[g][m] = mfma_f8_16x16x128(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf,
+                                            v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            }
         }
 
     // ---- 6. masked scores, row max and sum over the 4 lanes of the row -------
@@ -280,18 +372,21 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         constexpr bool ALL = decltype(all_tag)::value;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const int kl0 = 128 * g + 32 * q4;         // tile-relative key of element (m, i) = kl0 + 4 m + i
+            const int kl0 = 128 * g + 32 * q4;         // e4m3: key of element (m, i) = kl0 + 4 m + i
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const float4 k4 = *(const float4*)&kss[kl0 + 4 * m];
-                const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+                float kk[4] = {1.0f, 1.0f, 1.0f, 1.0f};   // MX: the K scale is inside S
+                if constexpr (!MX) {
+                    const float4 k4 = *(const float4*)&kss[kl0 + 4 * m];
+                    kk[0] = k4.x, kk[1] = k4.y, kk[2] = k4.z, kk[3] = k4.w;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float xv = ((S[g][m][i] * qs) * kk[i]) * alpha;
+                    const float xv = MX ? (S[g][m][i] * qs) * alpha : ((S[g][m][i] * qs) * kk[i]) * alpha;
                     if constexpr (ALL) {
                         S[g][m][i] = xv;
                     } else {
-                        const int key = t0 + kl0 + 4 * m + i;
+                        const int key = t0 + 128 * g + kx<MX>(q4, m, i);
                         const bool ok = r < R && key < ctx && key <= pos && key >= lo;
                         S[g][m][i] = ok ? xv : -INFINITY;
                     }
@@ -317,14 +412,17 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         const int kl0 = 128 * g + 32 * q4;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const float4 v4 = *(const float4*)&vss[kl0 + 4 * m];
-            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            float vv[4] = {1.0f, 1.0f, 1.0f, 1.0f};   // MX: P8 = e4m3(448 p), V's scales are in the MFMA
+            if constexpr (!MX) {
+                const float4 v4 = *(const float4*)&vss[kl0 + 4 * m];
+                vv[0] = v4.x, vv[1] = v4.y, vv[2] = v4.z, vv[3] = v4.w;
+            }
             float pp[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = __builtin_amdgcn_exp2f(S[g][m][i] - Mb);
                 ls += p;
-                pp[i] = (p * vv[i]) * pinv;
+                pp[i] = MX ? p * kFp8Max : (p * vv[i]) * pinv;
             }
             const uint32_t c0 = cvt_pk_fp8<false>(pp[0], pp[1], 0);
             pf[g][m] = (int)cvt_pk_fp8<true>(pp[2], pp[3], c0);
@@ -345,6 +443,20 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int k0 = 128 * g + 32 * q4;           // tile-relative first key of this lane's 32
+            if constexpr (MX) {
+                // 16 bytes of V^T row d (keys [k0, +32), E2M1; any finite
+                // value past ctx meets P = 0) and that block's E8M0 byte; a
+                // block wholly past ctx may hold an unwritten scale (E8M0 255
+                // is NaN), so it gets 2^0
+                const int pb = k0 / PW, c = (k0 % PW) / 32;
+                const uint8_t* vrow = vt_s + (pb * 128 + d) * (PW / 2);
+                const v4i v4 = *(const v4i*)(vrow + 16 * (c ^ dv_swz<kVLgn>(d)));
+                int sv = (int)((const uint8_t*)vss)[(pb * 128 + d) * (PW / 32) + c];
+                if (!all_in && t0 + k0 >= ctx) sv = 127;
+                O[db] = mfma_f4f8_16x16x128(__builtin_shufflevector(v4, v4, 0, 1, 2, 3, -1, -1, -1, -1), pf[g],
+                                            O[db], sv);
+                continue;
+            }
             const int pb = k0 / PW, c = (k0 % PW) / 16;
             const uint8_t* vrow = vt_s + (pb * 128 + d) * PW;
             // keys at or beyond ctx may hold any bytes (e4m3 NaN codes
@@ -361,13 +473,21 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             O[db] = mfma_f8_16x16x128(av, pf[g], O[db]);
         }
     }
+    // An MFMA reads its operands from every lane, whatever the exec mask: the
+    // PV products (and the P packing and V reads feeding them) must not be
+    // moved into the r < R branch below, where the padding rows' lanes would
+    // feed stale registers into the valid rows' channels.
+#pragma unroll
+    for (int db = 0; db < 8; ++db) asm volatile("" : "+v"(O[db]));
     if (r < R) {
         const float hs = ls > 0.0f ? 1.0f / (kFp8Max * ls) : 0.0f;
         uint8_t* prow = (uint8_t*)a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartBytes;
+        // MX: h = O / (448 l vmax) with vmax = 2^(em - 127) (|h| <= 6)
+        auto hv = [&](float o) { return MX ? __builtin_ldexpf(o * hs, 127 - em) : o * hs; };
 #pragma unroll
         for (int db = 0; db < 8; ++db)
             *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
-                make_uint2(pack_h2(O[db][0] * hs, O[db][1] * hs), pack_h2(O[db][2] * hs, O[db][3] * hs));
+                make_uint2(pack_h2(hv(O[db][0]), hv(O[db][1])), pack_h2(hv(O[db][2]), hv(O[db][3])));
         if (q4 == 0) *(float4*)(prow + 2 * kD) = make_float4(rmax, ls, vmax, 0.0f);
     }
 }
@@ -441,11 +561,19 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid(a.num_splits, a.B * a.Hkv);
-    switch (a.page < kTile ? a.page : kTile) {
-        case 32: k_paged_decode<32><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-        case 64: k_paged_decode<64><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-        case 128: k_paged_decode<128><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-        default: k_paged_decode<256><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+    if (a.mx) {
+        switch (a.page < kTile ? a.page : kTile) {
+            case 64: k_paged_decode<64, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            case 128: k_paged_decode<128, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            default: k_paged_decode<256, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        }
+    } else {
+        switch (a.page < kTile ? a.page : kTile) {
+            case 32: k_paged_decode<32, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            case 64: k_paged_decode<64, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            case 128: k_paged_decode<128, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            default: k_paged_decode<256, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        }
     }
     const int rows = a.B * a.Hkv * kRows;
     k_decode_merge<<<(rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock, 64 * kMergeRowsPerBlock, 0,

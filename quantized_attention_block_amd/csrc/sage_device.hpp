@@ -44,6 +44,11 @@ __device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b, v4f c) {
 }
 // E2M1 x E2M1 with per-lane E8M0 scales (byte 0 of sa / sb); only the first
 // four dwords of a and b are read.
+// A: E2M1 (low four dwords) with E8M0 block scale sa; B: e4m3, scale 2^0.
+__device__ __forceinline__ v4f mfma_f4f8_16x16x128(v8i a, v8i b, v4f c, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, 127);
+}
+
 __device__ __forceinline__ v16f mfma_f4_32x32x64(v8i a, v8i b, v16f c, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }

@@ -34,6 +34,11 @@ _TORCH_DTYPES = {
     torch.int32: I32, torch.uint8: U8, torch.float8_e4m3fn: FP8_E4M3FN,
     torch.float8_e4m3fnuz: FP8_E4M3FNUZ,
 }
+# E2M1 pairs and E8M0 scales as torch dtypes (uint8 tensors carry them too,
+# with the dtype passed explicitly to desc)
+for _name, _code in (("float4_e2m1fn_x2", FP4X2_E2M1), ("float8_e8m0fnu", E8M0)):
+    if hasattr(torch, _name):
+        _TORCH_DTYPES[getattr(torch, _name)] = _code
 
 
 class SageError(RuntimeError):
@@ -322,8 +327,10 @@ def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_len
                       out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """q bf16 [B, MTP, Hq, D]; caches e4m3 [P, Hkv, page, D] (V transposed:
-    [P, Hkv, D, page]); scales fp32 [P, Hkv, page]; page_table int32 [B, pages];
-    ctx_lens int32 [B]."""
+    [P, Hkv, D, page]) with fp32 scales [P, Hkv, page], or MXFP4 caches
+    (torch.float4_e2m1fn_x2) K [P, Hkv, page, D/2], V [P, Hkv, D, page/2]
+    with E8M0 scales (torch.float8_e8m0fnu) K [P, Hkv, page, D/32] and
+    V [P, Hkv, D, page/32]; page_table int32 [B, pages]; ctx_lens int32 [B]."""
     if out is None:
         out = torch.empty_like(q)
     prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx))

@@ -212,6 +212,62 @@ def _per_token_e4m3(x: np.ndarray):
     return codes.contiguous(), scale.squeeze(-1).contiguous()
 
 
+@dataclass
+class DecodeInputsMX:
+    """MXFP4 KV cache, one E2M1 code (0-15, sign in bit 3) per byte; V
+    transposed.  `packed()` gives the two-codes-per-byte tensors the library
+    takes (element 2i in the low nibble)."""
+    q: torch.Tensor            # [batch, mtp, hq, D] bf16
+    k_codes: torch.Tensor      # [num_pages, hkv, page, D] uint8
+    k_e8: torch.Tensor         # [num_pages, hkv, page, D / 32] uint8 (E8M0)
+    v_codes: torch.Tensor      # [num_pages, hkv, D, page] uint8
+    v_e8: torch.Tensor         # [num_pages, hkv, D, page / 32] uint8 (E8M0)
+    page_table: torch.Tensor   # [batch, pages_per_seq] int32
+    ctx_lens: torch.Tensor     # [batch] int32
+
+    def packed(self):
+        pk = lambda c: (c[..., 0::2] | (c[..., 1::2] << 4)).contiguous()
+        return pk(self.k_codes), pk(self.v_codes)
+
+
+# magnitude index 0..7 of E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6) drawn with these
+# weights, a uniform sign, and block exponents around 2^-1: roughly the codes
+# of N(0, 1) values in blocks of 32 (synthetic codes, no quantization here)
+_E2M1_WEIGHTS = np.array([0.10, 0.20, 0.20, 0.16, 0.14, 0.12, 0.06, 0.02])
+
+
+def _mx_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    mag = rng.choice(8, size=shape, p=_E2M1_WEIGHTS / _E2M1_WEIGHTS.sum())
+    sign = rng.integers(0, 2, size=shape)
+    return (mag | (sign << 3)).astype(np.uint8)
+
+
+def _mx_exponents(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.choice(np.array([125, 126, 127], np.uint8), size=shape, p=[0.1, 0.8, 0.1])
+
+
+def make_decode_mx(w: DecodeWorkload, batch: Optional[int] = None, ctx: Optional[int] = None,
+                   pool_seed: int = 0) -> DecodeInputsMX:
+    """Draws a paged decode problem over an MXFP4 cache of the same shape as
+    make_decode's (same queries, page table and lengths)."""
+    batch = w.batch if batch is None else batch
+    ctx = w.ctx if ctx is None else ctx
+    pps = (ctx + w.page_size - 1) // w.page_size
+    npages = batch * pps
+    cid = w.config_id if pool_seed == 0 else 1000 + pool_seed
+    q = _normal(w.config_id, T_Q, (batch, w.mtp, w.hq, w.D))
+    rk, rv = _rng(cid, T_K), _rng(cid, T_V)
+    kc = _mx_codes(rk, (npages, w.hkv, w.page_size, w.D))
+    ke = _mx_exponents(rk, (npages, w.hkv, w.page_size, w.D // 32))
+    vc = _mx_codes(rv, (npages, w.hkv, w.D, w.page_size))
+    ve = _mx_exponents(rv, (npages, w.hkv, w.D, w.page_size // 32))
+    perm = _rng(cid, T_PAGES).permutation(npages).astype(np.int32)
+    table = torch.from_numpy(perm.reshape(batch, pps).copy())
+    ctx_lens = torch.full((batch,), ctx, dtype=torch.int32)
+    t = torch.from_numpy
+    return DecodeInputsMX(_to_dtype(q, w.q_dtype), t(kc), t(ke), t(vc), t(ve), table, ctx_lens)
+
+
 def make_decode(w: DecodeWorkload, batch: Optional[int] = None, ctx: Optional[int] = None,
                 pool_seed: int = 0) -> DecodeInputs:
     """Draws a paged decode problem.  ``pool_seed`` > 0 draws an independent KV

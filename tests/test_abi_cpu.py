@@ -198,6 +198,38 @@ def test_paged_decode_refusals(S):
     assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, 3, page, D)), vc_=T(S.FP8_E4M3FN, (P_, 3, D, page))) == S.ERR_SHAPE
 
 
+def test_paged_decode_mx_refusals(S):
+    """The MXFP4 cache (chosen by k_cache's FP4X2 dtype) is validated field by
+    field before any HIP call."""
+    B, MTP, Hq, D, P_, Hkv, page = 2, 4, 16, 128, 8, 1, 128
+    r = ctypes.byref
+    q = T(S.BF16, (B, MTP, Hq, D))
+    kc = T(S.FP4X2_E2M1, (P_, Hkv, page, D // 2))
+    vc = T(S.FP4X2_E2M1, (P_, Hkv, D, page // 2))
+    ke = T(S.E8M0, (P_, Hkv, page, D // 32))
+    ve = T(S.E8M0, (P_, Hkv, D, page // 32))
+    pt = T(S.I32, (B, 4))
+    cl = T(S.I32, (B,))
+    out = T(S.BF16, (B, MTP, Hq, D))
+    prm = S.DecodeParams(0.0, 256, 1, 512)
+
+    def call(kc_=kc, vc_=vc, ke_=ke, ve_=ve, prm_=prm):
+        return S.lib().sage_paged_decode(r(q), r(kc_), r(vc_), r(ke_), r(ve_), r(pt), r(cl), r(prm_),
+                                         r(out), ctypes.c_void_p(FAKE), 1 << 30, None)
+
+    assert call(kc_=T(S.FP4X2_E2M1, (P_, Hkv, page, D))) == S.ERR_SHAPE          # D / 2 bytes per row
+    assert call(vc_=T(S.FP4X2_E2M1, (P_, Hkv, D, page))) == S.ERR_SHAPE          # page / 2 bytes per row
+    assert call(vc_=T(S.FP8_E4M3FN, (P_, Hkv, D, page))) == S.ERR_DTYPE          # mixed cache formats
+    assert call(ke_=T(S.F32, (P_, Hkv, page, D // 32))) == S.ERR_DTYPE            # E8M0 bytes, not fp32
+    assert call(ve_=T(S.E8M0, (P_, Hkv, D, page // 16))) == S.ERR_SHAPE          # one per 32 keys
+    assert call(prm_=S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED
+    p32 = 32
+    assert call(kc_=T(S.FP4X2_E2M1, (P_, Hkv, p32, D // 2)), vc_=T(S.FP4X2_E2M1, (P_, Hkv, D, p32 // 2)),
+                ke_=T(S.E8M0, (P_, Hkv, p32, D // 32)), ve_=T(S.E8M0, (P_, Hkv, D, 1)),
+                prm_=S.DecodeParams(0.0, 64, 1, 128)) == S.ERR_UNSUPPORTED    # pages of 32 keys
+    assert "multiple of 64" in S.lib().sage_last_error().decode()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from quantized_attention_block_amd import sage
     monkeypatch.setattr(sage, "_lib", None)

@@ -69,7 +69,7 @@ def test_paged_decode_windows_and_contexts(dev, orc, window, ctx):
 
 
 @pytest.mark.parametrize("mtp,hq,hkv,page", [(1, 16, 1, 128), (4, 16, 2, 128), (2, 8, 1, 64),
-                                             (4, 16, 1, 256)])
+                                             (4, 16, 1, 256), (1, 8, 1, 128)])   # 8 rows: half a wave
 def test_paged_decode_shapes(dev, orc, mtp, hq, hkv, page):
     base = wl.WORKLOADS["paged_decode"]
     w = wl.DecodeWorkload("v", 9, 4, mtp, hq, hkv, 128, page, 1200, 512)
