@@ -202,7 +202,8 @@ int32_t sage_attn_kv_tile(void);
  *   k_cache    FP8_E4M3FN [P, Hkv, page, D] contiguous
  *   v_cache    FP8_E4M3FN [P, Hkv, D, page] contiguous when v_transposed = 1,
  *              [P, Hkv, page, D] otherwise
- *   k_scale, v_scale  F32 [P, Hkv, page] (per-token scales)
+ *   k_scale, v_scale  F32 [P, Hkv, page] (per-token scales), or F32 [1] each
+ *              (one scale per cache tensor)
  *   page_table I32 [B, max_pages]: page of token t is page_table[b][t / page]
  *   ctx_lens   I32 [B]
  *   out        BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides)

@@ -514,6 +514,7 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
         return fail(SAGE_ERR_UNSUPPORTED, "page size %d: need a multiple of 32 that divides 256 or is a multiple of 256", page);
     if (P < 1) return fail(SAGE_ERR_SHAPE, "empty KV pool");
     if (!p->v_transposed) return fail(SAGE_ERR_UNSUPPORTED, "only the transposed V cache [P, Hkv, D, page] is implemented");
+    bool per_tensor = false;
     if (mx) {
         if (page % 64) return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 cache: page size %d is not a multiple of 64", page);
         const int64_t ks[4] = {P, Hkv, page, s.D / 2}, vt[4] = {P, Hkv, s.D, page / 2};
@@ -524,10 +525,13 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
         if ((st = check_exact(v_scale, "v_scale", SAGE_E8M0, 4, vse))) return st;
     } else {
         const int64_t ks[4] = {P, Hkv, page, s.D}, vt[4] = {P, Hkv, s.D, page}, ss[3] = {P, Hkv, page};
+        const int64_t one[1] = {1};
         if ((st = check_exact(k_cache, "k_cache", SAGE_FP8_E4M3FN, 4, ks))) return st;
         if ((st = check_exact(v_cache, "v_cache", SAGE_FP8_E4M3FN, 4, vt))) return st;
-        if ((st = check_exact(k_scale, "k_scale", SAGE_F32, 3, ss))) return st;
-        if ((st = check_exact(v_scale, "v_scale", SAGE_F32, 3, ss))) return st;
+        // per-token scales [P, Hkv, page], or one per tensor [1] (both K and V)
+        per_tensor = k_scale && k_scale->ndim == 1;
+        if ((st = check_exact(k_scale, "k_scale", SAGE_F32, per_tensor ? 1 : 3, per_tensor ? one : ss))) return st;
+        if ((st = check_exact(v_scale, "v_scale", SAGE_F32, per_tensor ? 1 : 3, per_tensor ? one : ss))) return st;
     }
     if (page_table->shape[1] > 1 && page_table->stride[1] != 1)
         return fail(SAGE_ERR_LAYOUT, "page_table rows must be contiguous");
@@ -580,6 +584,7 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     a.v_transposed = p->v_transposed;
     a.num_splits = s.splits;
     a.mx = mx ? 1 : 0;
+    a.scale_per_tensor = per_tensor ? 1 : 0;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)s.D));
     a.partials = (float*)workspace;
     return launch_status(sage::launch_paged_decode(a, (hipStream_t)stream), "paged decode");

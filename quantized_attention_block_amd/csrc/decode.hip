@@ -217,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             const uint8_t* vsb = (const uint8_t*)a.v_scale + ph * kD * (a.page / 32);
             vs = __builtin_bit_cast(float, *(const uint32_t*)(vsb + d * (a.page / 32) + koff / 32 + col));
         } else {
-            ks = a.k_scale[o];
-            vs = a.v_scale[o];
+            ks = a.k_scale[a.scale_per_tensor ? 0 : o];   // one scale for the whole cache, or per token
+            vs = a.v_scale[a.scale_per_tensor ? 0 : o];
         }
     }
 

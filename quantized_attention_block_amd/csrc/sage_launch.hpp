@@ -106,6 +106,7 @@ struct DecodeArgs {
     int B, MTP, Hq, Hkv, D, page, num_pages, max_pages;
     int window, v_transposed, num_splits;
     int mx;                   // 1: MXFP4 cache (E2M1 codes, E8M0 scales) as documented in sage.h
+    int scale_per_tensor;     // e4m3 cache: k_scale / v_scale hold one value each
     float sm_scale;
     float* partials;          // [B, Hkv, num_splits, rows] rows of fp16 h[D], fp32 m, l, vmax, pad
 };

@@ -196,6 +196,13 @@ def test_paged_decode_refusals(S):
     assert call(S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED  # plain V layout
     assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
     assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, 3, page, D)), vc_=T(S.FP8_E4M3FN, (P_, 3, D, page))) == S.ERR_SHAPE
+    # one scale per tensor is F32 [1] for both K and V
+    bad = S.lib().sage_paged_decode(r(q), r(kc), r(vc), r(T(S.F32, (2,))), r(T(S.F32, (1,))), r(pt), r(cl),
+                                    r(prm), r(out), ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert bad == S.ERR_SHAPE
+    mixed = S.lib().sage_paged_decode(r(q), r(kc), r(vc), r(T(S.F32, (1,))), r(vsc), r(pt), r(cl),
+                                      r(prm), r(out), ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert mixed == S.ERR_SHAPE
 
 
 def test_paged_decode_mx_refusals(S):

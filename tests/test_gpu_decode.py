@@ -103,3 +103,31 @@ def test_paged_decode_long_page_tables(dev, orc, page, ctx, window):
     say("paged decode long table", page, ctx, window)
     g = _run(inp, dev, w.window, w.ctx, base.sm_scale)
     _check(g, _oracle(orc, inp, w.window, base.sm_scale), _oracle(orc, inp, w.window, base.sm_scale, False))
+
+
+def test_paged_decode_per_tensor_scales(dev, orc):
+    """One fp32 scale per cache tensor (F32 [1]) instead of per token: the
+    same cache values re-encoded with a single scale, against the oracle
+    given that scale for every token."""
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=3, ctx=900)
+    say("paged decode, per-tensor scales", "batch 3 ctx 900 window 256")
+    kf = orc.e4m3_decode_array(inp.k_cache.numpy()) * inp.k_scale.numpy()[..., None]
+    vf = orc.e4m3_decode_array(inp.v_cache.numpy()) * inp.v_scale.numpy()[..., None]
+    sk, sv = np.float32(np.abs(kf).max() / 448.0), np.float32(np.abs(vf).max() / 448.0)
+    k8 = torch.from_numpy(orc.e4m3_encode_array((kf / sk).astype(np.float32)))
+    v8 = torch.from_numpy(orc.e4m3_encode_array((vf / sv).astype(np.float32)))
+    q = inp.q.to(dev)
+    out = sage.sage_paged_decode(q, k8.to(dev).view(torch.float8_e4m3fn),
+                                 v8.transpose(2, 3).contiguous().to(dev).view(torch.float8_e4m3fn),
+                                 torch.tensor([sk], device=dev), torch.tensor([sv], device=dev),
+                                 inp.page_table.to(dev), inp.ctx_lens.to(dev), max_ctx=900, window=256,
+                                 sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    full = lambda x: np.full(inp.k_scale.shape, x, np.float32)
+    o = orc.paged_decode(inp.q.float().numpy(), k8.numpy(), v8.numpy(), full(sk), full(sv),
+                         inp.page_table.numpy(), inp.ctx_lens.numpy(), window=256, sm_scale=w.sm_scale)
+    e = orc.paged_decode(inp.q.float().numpy(), kf, vf, full(1.0), full(1.0), inp.page_table.numpy(),
+                         inp.ctx_lens.numpy(), window=256, sm_scale=w.sm_scale, quant=False)
+    _check(g, o, e)
