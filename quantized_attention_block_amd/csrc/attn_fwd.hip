@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     using G = Geo<D, MX>;
     using SAcc = SAccT<D, MX>;
     constexpr int kDB = D / 32;         // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * G::kStageBytes];
+    // the KV ring, then this KV head's V scales (fp32 [D], D <= 128)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * G::kStageBytes + 512];
+    static_assert(D * 4 <= 512, "V scales fit their LDS slot");
 
     const int Lqp = pad128(a.Lq), Lkp = pad128(a.Lk);
     const int nqb = Lqp / kBM;
@@ -351,6 +353,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // more, for the K scales; counting without it only waits longer)
     constexpr int kDma = Dma::kKRegions / 4 + Dma::kVRegions / 4;
 
+    // The V scales go to LDS ahead of tile 0 (wave 0, one instruction; they
+    // have landed once step 0's barrier is passed), so that the epilogue reads
+    // them without a global load: that would wait in the vector memory
+    // counter, which on this architecture also counts the output stores.
+    uint8_t* const vs_lds = smem + kStages * G::kStageBytes;
+    if (wave == 0 && lane < D / 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.v_scale + (int64_t)bhk * D, D * 4), vs_lds, 16,
+                                                 16 * lane, 0, 0, 0);
     // tiles 0 and 1 in flight before the loop; tile j + 2 is issued in step j
     Dma::issue(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane);
     if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const float lt = l + __shfl_xor(l, 32);
     const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;   // one division per row
     if (qrow < a.Lq) {
-        const float* vs = a.v_scale + (int64_t)bhk * D;
+        const float* vs = (const float*)vs_lds;
         const int64_t ooff = (int64_t)b * a.out.sB + (int64_t)qrow * a.out.sL + (int64_t)h * a.out.sH;
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
