@@ -510,8 +510,8 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     if (Hkv < 1 || s.Hq % Hkv) return fail(SAGE_ERR_SHAPE, "query heads %d not a multiple of KV heads %d", s.Hq, Hkv);
     const int G = s.Hq / Hkv;
     if (G > 64 || s.MTP * G > 64) return fail(SAGE_ERR_UNSUPPORTED, "MTP x (Hq / Hkv) must be <= 64");
-    if (page < 32 || page % 32 || !(256 % page == 0 || page % 256 == 0))
-        return fail(SAGE_ERR_UNSUPPORTED, "page size %d: need a multiple of 32 that divides 256 or is a multiple of 256", page);
+    if (page < 16 || page % 16 || !(256 % page == 0 || page % 256 == 0))
+        return fail(SAGE_ERR_UNSUPPORTED, "page size %d: need a multiple of 16 that divides 256 or is a multiple of 256", page);
     if (P < 1) return fail(SAGE_ERR_SHAPE, "empty KV pool");
     if (!p->v_transposed) return fail(SAGE_ERR_UNSUPPORTED, "only the transposed V cache [P, Hkv, D, page] is implemented");
     bool per_tensor = false;

@@ -121,7 +121,7 @@ template <int PW, bool MX>
 __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float alpha) {
     static_assert(!MX || PW >= 64, "MXFP4 pages of 64 keys or more");
     constexpr int kNpb = kTile / PW;                 // page-blocks per tile
-    constexpr int kLgn = PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
+    constexpr int kLgn = PW == 16 ? 0 : PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
     constexpr int kRowB = MX ? kD / 2 : kD;          // bytes of one K row / of 256 keys of a V^T row
     constexpr int kVLgn = MX ? kLgn - 1 : kLgn;      // log2 of 16-byte chunks per V^T row of a page-block
     // Every kernel argument the block uses is read at entry, in one batch:
@@ -226,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     // (MX: 4 and 4).  Instruction i = wave + 4 j fills LDS chunks [64 i, +64)
     // of each tile; both tiles hold 128 n chunks per page-block (n = PW / 16
     // chunks per V^T row; MX: PW / 32), so it lies in page-block
-    // (wave + 4 j) / (2 n), a constant.
+    // (wave + 4 j) / (2 n): a constant for n >= 2, and 2 j + wave / 2 for
+    // 16-key pages (a wave-uniform choice between two page ids).
     const int kpage = a.page * kRowB;                // bytes of one page of one KV head
     if constexpr (MX) {
 #pragma unroll
@@ -250,8 +251,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int i = wave + 4 * j;
-        constexpr int kShift = kLgn - 1;
-        const int pg = pid[j >> kShift];
+        int pg;
+        if constexpr (PW == 16) pg = (wave & 2) ? pid[2 * j + 1] : pid[2 * j];
+        else pg = pid[j >> (kLgn - 1)];
         // K: keys [8 i, +8) of the tile
         const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
         const int key = 8 * i + (lane >> 3);
@@ -459,10 +461,14 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             }
             const int pb = k0 / PW, c = (k0 % PW) / 16;
             const uint8_t* vrow = vt_s + (pb * 128 + d) * PW;
+            // keys [k0 + 16, +16): the next chunk of the row, or with 16-key
+            // pages the row of the next page-block
+            const uint8_t* vrow_hi = PW == 16 ? vrow + 128 * PW : vrow;
+            const int c_hi = PW == 16 ? 0 : c + 1;
             // keys at or beyond ctx may hold any bytes (e4m3 NaN codes
             // included) and 0 * NaN would poison the product: zero them
             uint4 lo4 = *(const uint4*)(vrow + 16 * (c ^ sw));
-            uint4 hi4 = *(const uint4*)(vrow + 16 * ((c + 1) ^ sw));
+            uint4 hi4 = *(const uint4*)(vrow_hi + 16 * (c_hi ^ sw));
             if (!all_in) {
                 const int nv = ctx - (t0 + k0);
                 lo4 = keep_bytes(lo4, nv);
@@ -569,6 +575,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
         }
     } else {
         switch (a.page < kTile ? a.page : kTile) {
+            case 16: k_paged_decode<16, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
             case 32: k_paged_decode<32, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
             case 64: k_paged_decode<64, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
             case 128: k_paged_decode<128, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;

@@ -195,6 +195,10 @@ def test_paged_decode_refusals(S):
     assert call(S.DecodeParams(0.0, 256, 1, 4096)) == S.ERR_SHAPE       # table too short
     assert call(S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED  # plain V layout
     assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
+    # pages of 8 or 48 keys: not a multiple of 16 dividing 256
+    for pg in (8, 48):
+        assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, Hkv, pg, D)), vc_=T(S.FP8_E4M3FN, (P_, Hkv, D, pg)),
+                    pt_=T(S.I32, (B, 64))) == S.ERR_UNSUPPORTED
     assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, 3, page, D)), vc_=T(S.FP8_E4M3FN, (P_, 3, D, page))) == S.ERR_SHAPE
     # one scale per tensor is F32 [1] for both K and V
     bad = S.lib().sage_paged_decode(r(q), r(kc), r(vc), r(T(S.F32, (2,))), r(T(S.F32, (1,))), r(pt), r(cl),

@@ -69,7 +69,8 @@ def test_paged_decode_windows_and_contexts(dev, orc, window, ctx):
 
 
 @pytest.mark.parametrize("mtp,hq,hkv,page", [(1, 16, 1, 128), (4, 16, 2, 128), (2, 8, 1, 64),
-                                             (4, 16, 1, 256), (1, 8, 1, 128)])   # 8 rows: half a wave
+                                             (4, 16, 1, 256), (1, 8, 1, 128),    # 8 rows: half a wave
+                                             (4, 16, 1, 16), (2, 8, 2, 16)])     # 16-key pages
 def test_paged_decode_shapes(dev, orc, mtp, hq, hkv, page):
     base = wl.WORKLOADS["paged_decode"]
     w = wl.DecodeWorkload("v", 9, 4, mtp, hq, hkv, 128, page, 1200, 512)
@@ -92,10 +93,10 @@ def test_page_placement_invariance(dev):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("page,ctx,window", [(32, 3000, 1024), (32, 4500, 0)])
+@pytest.mark.parametrize("page,ctx,window", [(32, 3000, 1024), (32, 4500, 0), (16, 2500, 700)])
 def test_paged_decode_long_page_tables(dev, orc, page, ctx, window):
     """More than 64 pages per sequence: the page ids are read after the
-    context length instead of whole in lanes (94 and 141 pages here)."""
+    context length instead of whole in lanes (94, 141 and 157 pages here)."""
     base = wl.WORKLOADS["paged_decode"]
     w = wl.DecodeWorkload("v", 9, 3, 4, 16, 1, 128, page, ctx, window)
     inp = wl.make_decode(w)
