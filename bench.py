@@ -71,16 +71,21 @@ def _events_time(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e-3   # seconds per call
 
 
-def prefill_bench(wname, steps, warmup, dev, mode=None):
+def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
+    """fused_q (INT8): Q is quantized in the attention kernel's prologue
+    (sage_quantize_qk(None, k) + sage_attn_fwd(q=...)), which gives the
+    unfused step's output bit for bit; the unfused step is timed beside it."""
     from quantized_attention_block_amd import sage
     from quantized_attention_block_amd import workloads as wl
     w = wl.WORKLOADS[wname]
     mode = (sage.QK_MXFP4 if w.qk_mode == "mxfp4" else sage.QK_INT8) if mode is None else mode
+    fused_q = fused_q and mode == sage.QK_INT8
     inp = wl.make_prefill(w, device=dev)
     had = sage.Hadamard(dev.index or 0) if mode == sage.QK_MXFP4 else None
     stream = torch.cuda.current_stream(dev)
     # preallocated outputs and workspaces: the timed step only launches kernels
-    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, want_mean=False)
+    qk_in = None if fused_q else inp.q
+    qk = sage.sage_quantize_qk(qk_in, inp.k, mode=mode, hadamard=had, want_mean=False)
     v_q, v_s = sage.sage_quantize_v(inp.v)
     out = torch.empty((w.B, w.Lq, w.H, w.D), dtype=torch.bfloat16, device=dev)
     ws_qk = torch.empty(max(16, sage.sage_quantize_qk_workspace_size(inp.q, inp.k, mode=mode)),
@@ -88,11 +93,12 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
     ws_v = torch.empty(sage.sage_quantize_v_workspace_size(inp.v), dtype=torch.uint8, device=dev)
 
     def quant():
-        sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, workspace=ws_qk, into=qk)
+        sage.sage_quantize_qk(qk_in, inp.k, mode=mode, hadamard=had, workspace=ws_qk, into=qk)
         sage.sage_quantize_v(inp.v, workspace=ws_v, into=(v_q, v_s))
 
     def attn():
-        sage.sage_attn_fwd(qk, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out)
+        sage.sage_attn_fwd(qk, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out,
+                           q=inp.q if fused_q else None)
 
     def step():
         quant()
@@ -136,6 +142,25 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
         graph.replay()
     torch.cuda.synchronize()
     t_step_graph = (time.perf_counter() - t0) / steps
+    t_step_unfused = None
+    if fused_q:   # the unfused step (Q's INT8 copy written and read), same inputs
+        qk_u = sage.sage_quantize_qk(inp.q, inp.k, want_mean=False)
+        out_u = torch.empty_like(out)
+
+        def step_u():
+            sage.sage_quantize_qk(inp.q, inp.k, workspace=ws_qk, into=qk_u)
+            sage.sage_quantize_v(inp.v, workspace=ws_v, into=(v_q, v_s))
+            sage.sage_attn_fwd(qk_u, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out_u)
+        for _ in range(warmup + 1):
+            step_u()
+        torch.cuda.synchronize()
+        if not torch.equal(out_u, out):
+            raise RuntimeError(f"{wname}: fused Q quantization differs from the unfused step")
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step_u()
+        torch.cuda.synchronize()
+        t_step_unfused = (time.perf_counter() - t0) / steps
     # attention kernel alone, HIP events on its stream
     attn()
     t_attn = min(_events_time(attn, max(steps, 10), stream) for _ in range(3))
@@ -146,7 +171,8 @@ def prefill_bench(wname, steps, warmup, dev, mode=None):
     peak = PEAK_MXFP4_MIX_TOPS if mode == sage.QK_MXFP4 else PEAK_MFMA_TOPS
     achieved = ops_alg / t_attn / 1e12
     src = ["attn_fwd.hip", "sage_device.hpp"]
-    return dict(w=w, t_step=t_step, t_step_graph=t_step_graph, t_attn=t_attn,
+    return dict(w=w, t_step=t_step, t_step_graph=t_step_graph, t_attn=t_attn, fused_q=fused_q,
+                t_step_unfused=t_step_unfused,
                 value=literal / t_step / 1e12,
                 attn_literal_tops=literal / t_attn / 1e12,
                 roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
@@ -290,6 +316,9 @@ def main():
              "attn_kernel_tops_literal": round(r["attn_literal_tops"], 1),
              "quantize_us": round((r["t_step"] - r["t_attn"]) * 1e6, 1),
              "ms_per_step_hip_graph": round(r["t_step_graph"] * 1e3, 4)}
+    if r["t_step_unfused"] is not None:
+        extra["ms_per_step_unfused_q"] = round(r["t_step_unfused"] * 1e3, 4)
+        extra["tops_unfused_q"] = round(r["value"] * r["t_step"] / r["t_step_unfused"], 2)
     if not args.no_decode:
         extra["paged_decode"] = decode_bench(args.steps, args.warmup, dev)
         extra["paged_decode_mxfp4"] = decode_bench(args.steps, args.warmup, dev, mx=True)
@@ -308,7 +337,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len_q": w.Lq,
                    "seq_len_k": w.Lk, "head_dim": w.D, "causal": w.causal,
                    "q_block": w.q_block, "k_block": w.k_block,
-                   "step": "quantize_qk + quantize_v + attn_fwd"},
+                   "step": ("quantize_qk (K) + quantize_v + attn_fwd (Q quantized in its prologue)"
+                            if r["fused_q"] else "quantize_qk + quantize_v + attn_fwd")},
         "roofline": r["roofline"],
         "extra": extra,
     }

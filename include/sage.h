@@ -120,6 +120,8 @@ typedef struct sage_hadamard sage_hadamard;
  *      q_out   FP4X2 [B, H, SAGE_PAD(Lq), D/2]   q_scale E8M0 [B, H, SAGE_PAD(Lq), D/32]
  *      k_out   FP4X2 [B, H, SAGE_PAD(Lk), D/2]   k_scale E8M0 [B, H, SAGE_PAD(Lk), D/32]
  *  q, k: F16 or BF16 logical [B, L, H, D], D in {64, 128}, any B/L/H strides.
+ *    q NULL (SAGE_QK_INT8 only): K alone, with q_out and q_scale NULL; Q is
+ *    then quantized inside sage_attn_fwd (q_scale NULL there).
  *  k_mean: optional F32 [B, H, D] output of mu (NULL: kept in the workspace).
  *  workspace: sage_quantize_qk_workspace_size bytes, 16-byte aligned.  Its
  *    contents need no initialization and may be anything between calls; the
@@ -172,6 +174,12 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
  * of OCP e4m3).  Causal masks keep key j <= query i (Lq == Lk);
  * fully masked tiles are skipped.
  *   q_q, q_scale, k_q, k_scale: sage_quantize_qk outputs (mode = qk_mode)
+ *   q_scale NULL (SAGE_QK_INT8 only): q_q is the F16/BF16 Q, logical
+ *     [B, Lq, H, D] with any B/L/H strides (token stride >= D, one head within
+ *     2^31 bytes), quantized per 128-query block in the kernel's prologue with
+ *     sage_quantize_qk's INT8 arithmetic: the codes and scales, hence the
+ *     output, are those of the unfused path bit for bit; Q's INT8 copy is
+ *     neither written nor read.
  *   v_q, v_scale: sage_quantize_v outputs
  *   out: F16, BF16 or F32 logical [B, Lq, H, D], any B/L/H strides
  * num_kv_heads: K/V heads (H % num_kv_heads == 0; query head h reads KV head

@@ -166,21 +166,23 @@ struct QkShape {
 sage_status qk_inputs(const sage_tensor* q, const sage_tensor* k, const sage_qk_params* p,
                       QkShape* s) {
     sage_status st;
-    if ((st = check_half_view(q, "q"))) return st;
+    if (q && (st = check_half_view(q, "q"))) return st;
     if ((st = check_half_view(k, "k"))) return st;
     if (!p) return fail(SAGE_ERR_INVALID_ARG, "params: null");
-    if (q->dtype != k->dtype) return fail(SAGE_ERR_DTYPE, "q and k dtypes differ");
-    if (q->shape[0] != k->shape[0] || q->shape[2] != k->shape[2] || q->shape[3] != k->shape[3])
+    if (q && q->dtype != k->dtype) return fail(SAGE_ERR_DTYPE, "q and k dtypes differ");
+    if (q && (q->shape[0] != k->shape[0] || q->shape[2] != k->shape[2] || q->shape[3] != k->shape[3]))
         return fail(SAGE_ERR_SHAPE, "q and k must agree on B, H and D");
-    s->B = (int)q->shape[0];
-    s->Lq = (int)q->shape[1];
-    s->H = (int)q->shape[2];
-    s->D = (int)q->shape[3];
+    s->B = (int)k->shape[0];
+    s->Lq = q ? (int)q->shape[1] : 0;   // q NULL: K only
+    s->H = (int)k->shape[2];
+    s->D = (int)k->shape[3];
     s->Lk = (int)k->shape[1];
-    if (s->B < 1 || s->H < 1 || s->Lq < 1 || s->Lk < 1)
+    if (s->B < 1 || s->H < 1 || (q && s->Lq < 1) || s->Lk < 1)
         return fail(SAGE_ERR_SHAPE, "empty q or k (B, H, L must be >= 1)");
     if (p->mode != SAGE_QK_INT8 && p->mode != SAGE_QK_MXFP4)
         return fail(SAGE_ERR_INVALID_ARG, "params.mode: unknown qk mode %d", p->mode);
+    if (!q && p->mode != SAGE_QK_INT8)
+        return fail(SAGE_ERR_UNSUPPORTED, "K-only quantization (q NULL) is INT8 only");
     if (p->smooth_k != 0 && p->smooth_k != 1)
         return fail(SAGE_ERR_INVALID_ARG, "params.smooth_k must be 0 or 1");
     if (p->mode == SAGE_QK_INT8) {
@@ -260,9 +262,13 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
         const int64_t qs[4] = {s.B, s.H, Lqp, s.D}, ks[4] = {s.B, s.H, Lkp, s.D};
         const int64_t qss[3] = {s.B, s.H, Lqp / params->q_block};
         const int64_t kss[3] = {s.B, s.H, Lkp / params->k_block};
-        if ((st = check_exact(q_out, "q_out", SAGE_I8, 4, qs))) return st;
+        if (!q) {
+            if (q_out || q_scale) return fail(SAGE_ERR_INVALID_ARG, "q is NULL: q_out and q_scale must be NULL");
+        } else {
+            if ((st = check_exact(q_out, "q_out", SAGE_I8, 4, qs))) return st;
+            if ((st = check_exact(q_scale, "q_scale", SAGE_F32, 3, qss))) return st;
+        }
         if ((st = check_exact(k_out, "k_out", SAGE_I8, 4, ks))) return st;
-        if ((st = check_exact(q_scale, "q_scale", SAGE_F32, 3, qss))) return st;
         if ((st = check_exact(k_scale, "k_scale", SAGE_F32, 3, kss))) return st;
         if (hadamard) return fail(SAGE_ERR_INVALID_ARG, "hadamard: only used by the MXFP4 mode");
     } else {
@@ -297,7 +303,8 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
 
     hipStream_t strm = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    const sage::HalfView qv = half_view(q), kv = half_view(k);
+    // K only: the K view stands in for Q with no Q rows (Lq = 0)
+    const sage::HalfView qv = half_view(q ? q : k), kv = half_view(k);
     float* mu = nullptr;
     double* partial = nullptr;
     uint64_t* sync = nullptr;
@@ -315,8 +322,9 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
     if (params->mode == SAGE_QK_INT8) {
         e = sage::launch_quant_qk_int8(qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, params->k_block,
                                        params->smooth_k != 0, partial, sync,
-                                       k_mean ? (float*)k_mean->data : nullptr, (int8_t*)q_out->data,
-                                       (float*)q_scale->data, (int8_t*)k_out->data,
+                                       k_mean ? (float*)k_mean->data : nullptr,
+                                       q ? (int8_t*)q_out->data : nullptr, q ? (float*)q_scale->data : nullptr,
+                                       (int8_t*)k_out->data,
                                        (float*)k_scale->data, strm);
     } else {
         if (partial) {
@@ -388,14 +396,27 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
     if (!std::isfinite(p->sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale is not finite");
     const int64_t Lqp = sage::pad128(Lq), Lkp = sage::pad128(Lk);
     sage_status st;
+    // q_scale NULL (INT8 only): q_q is the fp16/bf16 Q itself, quantized in
+    // the kernel's prologue
+    const bool q_fused = p->qk_mode == SAGE_QK_INT8 && q_scale == nullptr;
     if (p->qk_mode == SAGE_QK_INT8) {
         if (p->q_block != 128) return fail(SAGE_ERR_UNSUPPORTED, "q_block must be 128");
         if (p->k_block != 64 && p->k_block != 128) return fail(SAGE_ERR_UNSUPPORTED, "k_block must be 64 or 128");
         const int64_t qs[4] = {B, H, Lqp, D}, ks[4] = {B, Hkv, Lkp, D};
         const int64_t qss[3] = {B, H, Lqp / p->q_block}, kss[3] = {B, Hkv, Lkp / p->k_block};
-        if ((st = check_exact(q_q, "q_q", SAGE_I8, 4, qs))) return st;
+        if (q_fused) {
+            if ((st = check_half_view(q_q, "q_q"))) return st;
+            if (q_q->shape[0] != B || q_q->shape[1] != Lq || q_q->shape[2] != H || q_q->shape[3] != D)
+                return fail(SAGE_ERR_SHAPE, "q_q (fp16/bf16 Q) must be [B, Lq, H, D]");
+            if (Lq > 1 && q_q->stride[1] < D)
+                return fail(SAGE_ERR_LAYOUT, "q_q: rows of one head overlap (token stride < D)");
+            if (((int64_t)(Lq - 1) * q_q->stride[1] + D) * 2 > 0x7FFFFF00LL)
+                return fail(SAGE_ERR_UNSUPPORTED, "q_q: one head spans more than 2^31 bytes");
+        } else if ((st = check_exact(q_q, "q_q", SAGE_I8, 4, qs))) {
+            return st;
+        }
         if ((st = check_exact(k_q, "k_q", SAGE_I8, 4, ks))) return st;
-        if ((st = check_exact(q_scale, "q_scale", SAGE_F32, 3, qss))) return st;
+        if (!q_fused && (st = check_exact(q_scale, "q_scale", SAGE_F32, 3, qss))) return st;
         if ((st = check_exact(k_scale, "k_scale", SAGE_F32, 3, kss))) return st;
     } else {
         const int64_t qs[4] = {B, H, Lqp, D / 2}, ks[4] = {B, Hkv, Lkp, D / 2};
@@ -421,7 +442,9 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
 
     sage::AttnArgs a;
     a.q = q_q->data;
-    a.q_scale = q_scale->data;
+    a.q_scale = q_fused ? nullptr : q_scale->data;
+    a.q_fused = q_fused ? 1 : 0;
+    a.qh = q_fused ? half_view(q_q) : sage::HalfView{nullptr, 0, 0, 0, 0};
     a.k = k_q->data;
     a.k_scale = k_scale->data;
     a.v = (const uint8_t*)v_q->data;

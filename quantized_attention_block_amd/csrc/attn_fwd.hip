@@ -301,14 +301,90 @@ __device__ __forceinline__ void load_qfrag(QFrag<D, MX>& q, const uint8_t* qbase
     }
 }
 
-template <int D, bool MX>
+// Workgroup barrier once this wave's LDS accesses are done (vector memory
+// operations in flight are not waited for, unlike __syncthreads()).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Fused Q quantization.  Lane l of a wave loads the fp16/bf16 channels of its
+// Q fragment chunks, [16 (2 c + half), +16) for c < D/32, of query row qrow;
+// rows past Lq read as zeros (the buffer resource ends with row Lq - 1).
+template <int D>
+__device__ __forceinline__ void load_q_rows(uint4 (&raw)[D / 16], const HalfView& q, int b, int h, int Lq,
+                                            int qrow, int half) {
+    const uint16_t* head = (const uint16_t*)q.ptr + (int64_t)b * q.sB + (int64_t)h * q.sH;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, ((int64_t)(Lq - 1) * q.sL + D) * 2);
+    const int off = qrow < Lq ? (int)((int64_t)qrow * q.sL * 2) : 0x7FFFFF00;   // past the resource
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+        const int o = off + 32 * (2 * c + half);
+        raw[2 * c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+        raw[2 * c + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16, 0, 0));
+    }
+}
+
+// The 128 rows of the block are one INT8 quantization block of Q: amax over
+// the block (rows past Lq are zeros), codes clamp(rne(x * (127 / amax)),
+// -127, 127), scale amax / 127 (returned) -- the arithmetic of the Q blocks of
+// the quantize kernels, so the codes and the scale are theirs bit for bit.
+// The clamp comes before the rounding (the bounds are integers, and a NaN
+// product still gives -127), and the rounding is the addition of 1.5 * 2^23,
+// whose result has spacing 1 and holds the code in its low byte.
+// red: 4 floats of LDS for the waves' amax.
+template <int D, bool BF16>
+__device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&raw)[D / 16], float* red,
+                                             int wave) {
+    auto lo = [](uint32_t w) { return BF16 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu); };
+    auto hi = [](uint32_t w) { return BF16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16); };
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am = fmaxf(fmaxf(am, fabsf(lo(w[i]))), fabsf(hi(w[i])));
+    }
+    am = wave_max(am);
+    if ((threadIdx.x & 63) == 0) red[wave] = am;
+    lds_barrier();
+    float amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+    amax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax)));   // uniform
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    auto code = [&](float x) {   // float bits whose low byte is the code
+        return __float_as_uint(fminf(127.0f, fmaxf(-127.0f, x * inv)) + kSBiasF);
+    };
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4& u = raw[2 * c + k / 2];
+            const uint32_t a = (k & 1) ? u.z : u.x, b = (k & 1) ? u.w : u.y;
+            // bytes [code(a.lo), code(a.hi)] and [code(b.lo), code(b.hi)], then both
+            const uint32_t pa = __builtin_amdgcn_perm(code(hi(a)), code(lo(a)), 0x0C0C0400u);
+            const uint32_t pb = __builtin_amdgcn_perm(code(hi(b)), code(lo(b)), 0x0C0C0400u);
+            wd[k] = __builtin_amdgcn_perm(pb, pa, 0x05040100u);
+        }
+        qf.f[c] = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+    }
+    return amax > 0.0f ? amax / 127.0f : 0.0f;
+}
+
+// QF: Q quantized in the prologue from the fp16/bf16 view a.qh (INT8 only).
+template <int D, bool MX, bool QF = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_attn_fwd(
-    AttnArgs a, float alpha) {
+    AttnKernelArgs a, float alpha, HalfView qh) {
     using G = Geo<D, MX>;
     using SAcc = SAccT<D, MX>;
     constexpr int kDB = D / 32;         // 32-row blocks of O^T
-    // the KV ring, then this KV head's V scales (fp32 [D], D <= 128)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * G::kStageBytes + 512];
+    // the KV ring, this KV head's V scales (fp32 [D], D <= 128), the waves'
+    // Q amax (fused Q quantization)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * G::kStageBytes + 512 + 16];
     static_assert(D * 4 <= 512, "V scales fit their LDS slot");
 
     const int Lqp = pad128(a.Lq), Lkp = pad128(a.Lk);
@@ -358,6 +434,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // them without a global load: that would wait in the vector memory
     // counter, which on this architecture also counts the output stores.
     uint8_t* const vs_lds = smem + kStages * G::kStageBytes;
+    // fused Q: this lane's fp16/bf16 Q loads go out ahead of the copies, so
+    // that the Q block's amax does not wait for the first two KV tiles
+    uint4 qraw[QF ? D / 16 : 1];
+    if constexpr (QF) load_q_rows<D>(qraw, qh, b, h, a.Lq, qrow, half);
     if (wave == 0 && lane < D / 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.v_scale + (int64_t)bhk * D, D * 4), vs_lds, 16,
                                                  16 * lane, 0, 0, 0);
@@ -366,13 +446,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
 
     QFrag<D, MX> qf;
-    load_qfrag<D, MX>(qf, qbase, qsc, qrow, lane);
+    float q_s = 0.0f;
+    if constexpr (QF) {
+        q_s = qh.bf16 ? quant_qfrag<D, true>(qf, qraw, (float*)(vs_lds + 512), wave)
+                      : quant_qfrag<D, false>(qf, qraw, (float*)(vs_lds + 512), wave);
+        q_s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, q_s)));
+    } else {
+        load_qfrag<D, MX>(qf, qbase, qsc, qrow, lane);
+    }
     // Score scale of tile kt: c = fp32(fp32(q_s k_s) alpha) for INT8 (a 64-key
     // tile lies inside one K scale block), alpha for MXFP4.  (Read through the
     // constant address space: a scalar load, which does not queue behind the
     // LDS DMA in the vector memory counter.)
-    float q_s = 0.0f;
-    if constexpr (!MX) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
+    if (!MX && !QF) q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + qb * kBM / a.q_block];
     const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
     const __attribute__((address_space(4))) float* kscale_c =
         (const __attribute__((address_space(4))) float*)kscale_f;
@@ -579,12 +665,20 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     const int nqb = pad128(a.Lq) / kBM;
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid((unsigned)(nqb * a.B * a.H));
+    const AttnKernelArgs k{a.q, a.q_scale, a.k, a.k_scale, a.v, a.v_scale, a.out, a.B, a.H, a.Hkv,
+                           a.Lq, a.Lk, a.D, a.q_block, a.k_block, a.causal};
     if (a.mxfp4) {
-        k_attn_fwd<128, true><<<grid, kThreads, 0, stream>>>(a, alpha);
+        k_attn_fwd<128, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
     } else if (a.D == 128) {
-        k_attn_fwd<128, false><<<grid, kThreads, 0, stream>>>(a, alpha);
+        if (a.q_fused)
+            k_attn_fwd<128, false, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
+        else
+            k_attn_fwd<128, false><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
     } else {
-        k_attn_fwd<64, false><<<grid, kThreads, 0, stream>>>(a, alpha);
+        if (a.q_fused)
+            k_attn_fwd<64, false, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
+        else
+            k_attn_fwd<64, false><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
     }
     return hipGetLastError();
 }

@@ -84,6 +84,24 @@ struct AttnArgs {
     int causal;
     int mxfp4;
     float sm_scale;
+    // q_fused: Q is the caller's fp16/bf16 [B, Lq, H, D] view qh (q and
+    // q_scale unused), quantized to INT8 per 128-row block in the prologue
+    int q_fused;
+    HalfView qh;
+};
+// The part of AttnArgs the attention kernel itself takes (the fused-Q view
+// travels as a kernel argument of its own).
+struct AttnKernelArgs {
+    const void* q;
+    const void* q_scale;
+    const void* k;
+    const void* k_scale;
+    const uint8_t* v;
+    const float* v_scale;
+    OutView out;
+    int B, H, Hkv, Lq, Lk, D;
+    int q_block, k_block;
+    int causal;
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 

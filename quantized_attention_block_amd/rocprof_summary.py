@@ -27,7 +27,7 @@ CSRC = os.path.join(ROOT, "quantized_attention_block_amd", "csrc")
 
 # kernel-name fragment -> (traffic key, source files it is built from)
 KERNELS = {
-    "k_attn_fwd<128, false>": ("attn_fwd_llm_prefill", ["attn_fwd.hip", "sage_device.hpp"]),
+    "k_attn_fwd<128, false, true>": ("attn_fwd_llm_prefill", ["attn_fwd.hip", "sage_device.hpp"]),
     "k_paged_decode<128, false>": ("paged_decode", ["decode.hip", "sage_device.hpp"]),
     "k_paged_decode<128, true>": ("paged_decode_mxfp4", ["decode.hip", "sage_device.hpp"]),
     "k_decode_merge": ("decode_merge", ["decode.hip", "sage_device.hpp"]),

@@ -192,10 +192,11 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
                      workspace: Optional[torch.Tensor] = None,
                      into: Optional[QuantizedQK] = None) -> QuantizedQK:
     """q, k: logical [B, L, H, D] fp16/bf16 (any B/L/H strides).  `into`
-    reuses the output tensors of an earlier call with the same shapes."""
-    B, Lq, H, D = q.shape
-    Lk = k.shape[1]
-    dev = q.device
+    reuses the output tensors of an earlier call with the same shapes.  q None
+    (INT8 only): K alone; Q is then quantized inside sage_attn_fwd(q=...)."""
+    B, Lk, H, D = k.shape
+    Lq = q.shape[1] if q is not None else 0
+    dev = k.device
     if into is not None:
         q_out, q_sc, k_out, k_sc, mean = into.q, into.q_scale, into.k, into.k_scale, into.k_mean
         if mode == QK_INT8:
@@ -203,6 +204,11 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
         else:
             qd, kd = desc(q_out, FP4X2_E2M1), desc(k_out, FP4X2_E2M1)
             qsd, ksd = desc(q_sc, E8M0), desc(k_sc, E8M0)
+    elif mode == QK_INT8 and q is None:
+        q_out = q_sc = None
+        k_out = torch.empty((B, H, pad128(Lk), D), dtype=torch.int8, device=dev)
+        k_sc = torch.empty((B, H, pad128(Lk) // k_block), dtype=torch.float32, device=dev)
+        qd, kd, qsd, ksd = None, desc(k_out), None, desc(k_sc)
     elif mode == QK_INT8:
         q_out = torch.empty((B, H, pad128(Lq), D), dtype=torch.int8, device=dev)
         k_out = torch.empty((B, H, pad128(Lk), D), dtype=torch.int8, device=dev)
@@ -222,12 +228,12 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
     prm = QkParams(mode, q_block, k_block, int(smooth_k))
     qv, kv = desc(q), desc(k)
     nbytes = ctypes.c_size_t()
-    _check(lib().sage_quantize_qk_workspace_size(ctypes.byref(qv), ctypes.byref(kv),
+    _check(lib().sage_quantize_qk_workspace_size(_ref(qv), ctypes.byref(kv),
                                                  ctypes.byref(prm), ctypes.byref(nbytes)))
     if workspace is None:
         workspace = _workspace(nbytes.value, dev)
-    _check(lib().sage_quantize_qk(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(prm),
-                                  ctypes.byref(qd), ctypes.byref(qsd), ctypes.byref(kd),
+    _check(lib().sage_quantize_qk(_ref(qv), ctypes.byref(kv), ctypes.byref(prm),
+                                  _ref(qd), _ref(qsd), ctypes.byref(kd),
                                   ctypes.byref(ksd), _ref(desc(mean)),
                                   hadamard.handle if hadamard is not None else None,
                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
@@ -241,7 +247,7 @@ def sage_quantize_qk_workspace_size(q: torch.Tensor, k: torch.Tensor, *, mode: i
     """Bytes of device workspace sage_quantize_qk needs for these inputs."""
     prm = QkParams(mode, q_block, k_block, int(smooth_k))
     nbytes = ctypes.c_size_t()
-    _check(lib().sage_quantize_qk_workspace_size(ctypes.byref(desc(q)), ctypes.byref(desc(k)),
+    _check(lib().sage_quantize_qk_workspace_size(_ref(desc(q)), ctypes.byref(desc(k)),
                                                  ctypes.byref(prm), ctypes.byref(nbytes)))
     return int(nbytes.value)
 
@@ -283,34 +289,50 @@ def sage_quantize_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None, i
 
 def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, causal: bool = False,
                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                  out_dtype: torch.dtype = torch.bfloat16, num_kv_heads: int = 0) -> torch.Tensor:
+                  out_dtype: torch.dtype = torch.bfloat16, num_kv_heads: int = 0,
+                  q: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Quantized attention; `out` is a logical [B, Lq, H, D] fp16/bf16 tensor
-    with any B/L/H strides (allocated contiguous when None)."""
-    B, H, _, _ = qk.q.shape
+    with any B/L/H strides (allocated contiguous when None).  When qk holds K
+    alone (sage_quantize_qk(None, k)), `q` is the fp16/bf16 [B, Lq, H, D] Q,
+    quantized to INT8 in the kernel's prologue (the same codes and scales as
+    sage_quantize_qk's)."""
+    if (qk.q is None) != (q is not None):
+        raise ValueError("pass q exactly when qk was quantized without Q")
+    if q is not None:
+        B, Lq, H, _ = q.shape
+    else:
+        B, H, _, _ = qk.q.shape
+        Lq = qk.Lq
     D = v_q.shape[2]
+    dev = qk.k.device
     if out is None:
-        out = torch.empty((B, qk.Lq, H, D), dtype=out_dtype, device=qk.q.device)
-    prm = AttnParams(float(sm_scale), int(causal), qk.mode, B, H, qk.Lq, qk.Lk, D,
+        out = torch.empty((B, Lq, H, D), dtype=out_dtype, device=dev)
+    prm = AttnParams(float(sm_scale), int(causal), qk.mode, B, H, Lq, qk.Lk, D,
                      num_kv_heads, qk.q_block, qk.k_block)
-    if qk.mode == QK_INT8:
+    if q is not None:
+        qd, qsd, kd, ksd = desc(q), None, desc(qk.k), desc(qk.k_scale)
+    elif qk.mode == QK_INT8:
         qd, qsd, kd, ksd = desc(qk.q), desc(qk.q_scale), desc(qk.k), desc(qk.k_scale)
     else:
         qd, kd = desc(qk.q, FP4X2_E2M1), desc(qk.k, FP4X2_E2M1)
         qsd, ksd = desc(qk.q_scale, E8M0), desc(qk.k_scale, E8M0)
-    _check(lib().sage_attn_fwd(ctypes.byref(qd), ctypes.byref(qsd), ctypes.byref(kd),
+    _check(lib().sage_attn_fwd(ctypes.byref(qd), _ref(qsd), ctypes.byref(kd),
                                ctypes.byref(ksd), ctypes.byref(desc(v_q)),
                                ctypes.byref(desc(v_scale)), ctypes.byref(prm),
-                               ctypes.byref(desc(out)), None, 0, _stream(qk.q.device)))
+                               ctypes.byref(desc(out)), None, 0, _stream(dev)))
     return out
 
 
 def sage_attention(q, k, v, *, causal=False, sm_scale=0.0, mode=QK_INT8, k_block=64,
                    hadamard: Optional[Hadamard] = None, out=None):
-    """quantize_qk + quantize_v + attn_fwd on strided [B, L, H, D] inputs."""
-    qk = sage_quantize_qk(q, k, mode=mode, k_block=k_block, hadamard=hadamard, want_mean=False)
+    """quantize_qk + quantize_v + attn_fwd on strided [B, L, H, D] inputs (INT8:
+    Q quantized inside the attention kernel)."""
+    fuse = mode == QK_INT8
+    qk = sage_quantize_qk(None if fuse else q, k, mode=mode, k_block=k_block, hadamard=hadamard,
+                          want_mean=False)
     v_q, v_s = sage_quantize_v(v)
     return sage_attn_fwd(qk, v_q, v_s, causal=causal, sm_scale=sm_scale, out=out,
-                         out_dtype=q.dtype)
+                         out_dtype=q.dtype, q=q if fuse else None)
 
 
 def sage_attn_kv_tile() -> int:

@@ -247,3 +247,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sage, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         sage.lib()
+
+
+def test_fused_q_refusals(S):
+    """K-only quantization (q NULL) and Q quantized inside sage_attn_fwd
+    (q_scale NULL): argument checks, no device work."""
+    B, L, H, D = 1, 256, 2, 128
+    r = ctypes.byref
+    k = T(S.BF16, (B, L, H, D))
+    _, _, kq, ks = _int8_outs(S, B, H, L, L, D)
+    lib = S.lib()
+
+    def qk(prm, q_out=None, q_scale=None):
+        return lib.sage_quantize_qk(None, r(k), r(prm), q_out and r(q_out), q_scale and r(q_scale), r(kq), r(ks),
+                                    None, None, ctypes.c_void_p(FAKE), 1 << 30, None)
+
+    assert qk(S.QkParams(S.QK_MXFP4, 128, 64, 1)) == S.ERR_UNSUPPORTED     # INT8 only
+    assert qk(S.QkParams(S.QK_INT8, 128, 64, 1), q_out=T(S.I8, (B, H, L, D))) == S.ERR_INVALID_ARG
+    nbytes = ctypes.c_size_t()
+    assert lib.sage_quantize_qk_workspace_size(None, r(k), r(S.QkParams(S.QK_INT8, 128, 64, 1)),
+                                               r(nbytes)) == S.OK
+    vq, vs = T(S.FP8_E4M3FN, (B, H, D, 256)), T(S.F32, (B, H, D))
+    out = T(S.BF16, (B, L, H, D))
+    good = dict(sm_scale=0.0, causal=1, qk_mode=S.QK_INT8, batch=B, heads=H, seqlen_q=L,
+                seqlen_k=L, head_dim=D, num_kv_heads=0, q_block=128, k_block=64)
+
+    def attn(q, **kw):
+        return lib.sage_attn_fwd(r(q), None, r(kq), r(ks), r(vq), r(vs), r(S.AttnParams(**{**good, **kw})),
+                                 r(out), None, 0, None)
+
+    assert attn(T(S.I8, (B, H, L, D))) == S.ERR_DTYPE                      # needs the fp16/bf16 Q
+    assert attn(T(S.BF16, (B, L + 1, H, D))) == S.ERR_SHAPE
+    assert attn(T(S.BF16, (B, L, H, D), stride=(L * H * D, 64, D, 1))) == S.ERR_LAYOUT   # rows overlap
+    assert attn(T(S.BF16, (B, L, H, D)), qk_mode=S.QK_MXFP4) != S.OK         # MXFP4 keeps its q_scale

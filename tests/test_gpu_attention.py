@@ -265,3 +265,31 @@ def test_single_token_and_tiny_lengths(dev, orc):
             ref, _ = orc.prefill_int8_pipeline(q, k, v, causal=causal, sm_scale=w.sm_scale, BN=BN,
                                                mu=qk.k_mean.cpu().numpy())
             _check(canon(out), ref)
+
+
+@pytest.mark.parametrize("name,Lq,D,causal,dtype", [
+    ("llm_prefill", 333, 128, True, torch.bfloat16),     # ragged last Q block
+    ("llm_prefill", 4096, 128, True, torch.bfloat16),    # the benchmark's shape
+    ("video_dit", 1000, 128, False, torch.bfloat16),     # outlier-heavy Q blocks
+    ("llm_prefill", 200, 64, True, torch.float16),
+])
+def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
+    """Q quantized in the attention prologue (sage_quantize_qk(None, k) +
+    sage_attn_fwd(q=...)) gives the unfused path's output bit for bit: the
+    same INT8 codes and block scales, hence the same kernel arithmetic."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, Lq=Lq, Lk=Lq, device=dev)
+    q, k, v = inp.q, inp.k, inp.v
+    if D != q.shape[3] or dtype != q.dtype:
+        q, k, v = (x[..., :D].to(dtype) for x in (q, k, v))
+    say("fused Q quantization", name, Lq, D, causal, dtype)
+    qk = sage.sage_quantize_qk(q, k)
+    kq = sage.sage_quantize_qk(None, k)
+    v_q, v_s = sage.sage_quantize_v(v)
+    ref = sage.sage_attn_fwd(qk, v_q, v_s, causal=causal, sm_scale=w.sm_scale, out_dtype=torch.float32)
+    got = sage.sage_attn_fwd(kq, v_q, v_s, causal=causal, sm_scale=w.sm_scale, out_dtype=torch.float32, q=q)
+    torch.cuda.synchronize()
+    assert kq.q is None and torch.equal(kq.k, qk.k) and torch.equal(kq.k_scale, qk.k_scale)
+    assert torch.equal(got, ref)
+    bf = sage.sage_attention(q, k, v, causal=causal, sm_scale=w.sm_scale)   # the fused convenience path
+    assert torch.equal(bf, ref.to(dtype))
