@@ -223,7 +223,8 @@ int32_t sage_attn_kv_tile(void);
  * inputs carry a relative rounding of 2^-11, below the bf16 output's 2^-9).
  * Q rows are quantized to e4m3 with a per-(token, head) scale; scores use FP8
  * MFMA; P is requantized per tile with the tile's largest per-token V scale.
- * D must be 128; the page size must be a multiple of 16 that divides 256 or
+ * D must be 128, or 64 with an e4m3 cache; the page size must be a multiple
+ * of 16 that divides 256 or
  * is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
  * below ctx_lens[b] must be valid page indices, and ctx_lens[b] <=
  * params.max_ctx; device data is not validated, but a page id outside

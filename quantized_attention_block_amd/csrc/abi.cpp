@@ -529,7 +529,8 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     if (!mx && (st = check_fp8(v_cache, "v_cache"))) return st;
     const int P = (int)k_cache->shape[0], Hkv = (int)k_cache->shape[1], page = (int)k_cache->shape[2];
     if (k_cache->shape[3] != (mx ? s.D / 2 : s.D)) return fail(SAGE_ERR_SHAPE, "k_cache head dim differs from q");
-    if (s.D != 128) return fail(SAGE_ERR_UNSUPPORTED, "decode head dim must be 128");
+    if (s.D != 128 && (mx || s.D != 64))
+        return fail(SAGE_ERR_UNSUPPORTED, "decode head dim must be 128 (or 64 with an e4m3 cache)");
     if (Hkv < 1 || s.Hq % Hkv) return fail(SAGE_ERR_SHAPE, "query heads %d not a multiple of KV heads %d", s.Hq, Hkv);
     const int G = s.Hq / Hkv;
     if (G > 64 || s.MTP * G > 64) return fail(SAGE_ERR_UNSUPPORTED, "MTP x (Hq / Hkv) must be <= 64");

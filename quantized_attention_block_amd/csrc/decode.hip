@@ -157,10 +157,14 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM +
                              (int64_t)(hk * G + gq) * a.q_sH;
         const int c0 = MX ? 16 * q4 : 32 * q4, c1 = MX ? 64 + 16 * q4 : 32 * q4 + 16;
-        qraw[0] = *(const uint4*)(qp + c0);
-        qraw[1] = *(const uint4*)(qp + c0 + 8);
-        qraw[2] = *(const uint4*)(qp + c1);
-        qraw[3] = *(const uint4*)(qp + c1 + 8);
+        if (MX || c0 < a.D) {
+            qraw[0] = *(const uint4*)(qp + c0);
+            qraw[1] = *(const uint4*)(qp + c0 + 8);
+            qraw[2] = *(const uint4*)(qp + c1);
+            qraw[3] = *(const uint4*)(qp + c1 + 8);
+        } else {   // D = 64: channels [64, 128) are zero
+            qraw[0] = qraw[1] = qraw[2] = qraw[3] = make_uint4(0, 0, 0, 0);
+        }
     }
     // The context length is loaded next and both are awaited here, so the Q
     // loads cannot be moved below the early exits (after the length arrives).
@@ -228,7 +232,10 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     // chunks per V^T row; MX: PW / 32), so it lies in page-block
     // (wave + 4 j) / (2 n): a constant for n >= 2, and 2 j + wave / 2 for
     // 16-key pages (a wave-uniform choice between two page ids).
-    const int kpage = a.page * kRowB;                // bytes of one page of one KV head
+    // bytes of one page of one KV head; e4m3 rows of D = 64 channels sit in
+    // the tiles as 128-byte rows whose upper half (and V^T rows d >= 64) the
+    // copies fill with zeros: their offsets fall past the page's resource
+    const int kpage = a.page * (MX ? kRowB : a.D);
     if constexpr (MX) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -259,7 +266,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         const int key = 8 * i + (lane >> 3);
         const int kc = (lane & 7) ^ dk_swz(key);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + 1024 * i, 16,
-                                                 (koff + key % PW) * kD + 16 * kc, 0, 0, 0);
+                                                 16 * kc < a.D ? (koff + key % PW) * a.D + 16 * kc : kpage,
+                                                 0, 0, 0);
         // V^T: rows d of page-block (j >> kShift), chunks c
         const int within = ((64 * i) & ((128 << kLgn) - 1)) + lane;
         const int d = within >> kLgn, c = (within & ((1 << kLgn) - 1)) ^ dv_swz<kLgn>(d);
@@ -492,8 +500,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         auto hv = [&](float o) { return MX ? __builtin_ldexpf(o * hs, 127 - em) : o * hs; };
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-            *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
-                make_uint2(pack_h2(hv(O[db][0]), hv(O[db][1])), pack_h2(hv(O[db][2]), hv(O[db][3])));
+            if (16 * db < a.D)
+                *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
+                    make_uint2(pack_h2(hv(O[db][0]), hv(O[db][1])), pack_h2(hv(O[db][2]), hv(O[db][3])));
         if (q4 == 0) *(float4*)(prow + 2 * kD) = make_float4(rmax, ls, vmax, 0.0f);
     }
 }
@@ -559,7 +568,8 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     const int mt = r / G, g = r % G;
     uint16_t* op = (uint16_t*)a.out + (int64_t)b * a.o_sB + (int64_t)mt * a.o_sM +
                    (int64_t)(hk * G + g) * a.o_sH + 2 * lane;
-    *(uint32_t*)op = f32_to_bf16_bits(o0 * inv) | ((uint32_t)f32_to_bf16_bits(o1 * inv) << 16);
+    if (2 * lane < a.D)
+        *(uint32_t*)op = f32_to_bf16_bits(o0 * inv) | ((uint32_t)f32_to_bf16_bits(o1 * inv) << 16);
 }
 
 }  // namespace

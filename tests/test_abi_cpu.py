@@ -195,6 +195,11 @@ def test_paged_decode_refusals(S):
     assert call(S.DecodeParams(0.0, 256, 1, 4096)) == S.ERR_SHAPE       # table too short
     assert call(S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED  # plain V layout
     assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
+    # head dims other than 128, and 64 with e4m3 caches
+    q96, o96 = T(S.BF16, (B, MTP, Hq, 96)), T(S.BF16, (B, MTP, Hq, 96))
+    assert S.lib().sage_paged_decode(r(q96), r(T(S.FP8_E4M3FN, (P_, Hkv, page, 96))),
+                                     r(T(S.FP8_E4M3FN, (P_, Hkv, 96, page))), r(ksc), r(vsc), r(pt), r(cl),
+                                     r(prm), r(o96), ctypes.c_void_p(FAKE), 1 << 30, None) == S.ERR_UNSUPPORTED
     # pages of 8 or 48 keys: not a multiple of 16 dividing 256
     for pg in (8, 48):
         assert call(prm, kc_=T(S.FP8_E4M3FN, (P_, Hkv, pg, D)), vc_=T(S.FP8_E4M3FN, (P_, Hkv, D, pg)),

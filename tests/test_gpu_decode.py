@@ -132,3 +132,18 @@ def test_paged_decode_per_tensor_scales(dev, orc):
     e = orc.paged_decode(inp.q.float().numpy(), kf, vf, full(1.0), full(1.0), inp.page_table.numpy(),
                          inp.ctx_lens.numpy(), window=256, sm_scale=w.sm_scale, quant=False)
     _check(g, o, e)
+
+
+@pytest.mark.parametrize("mtp,hq,hkv,page,window", [(4, 16, 1, 128, 512), (1, 8, 1, 16, 0), (2, 16, 2, 64, 300)])
+def test_paged_decode_head_dim_64(dev, orc, mtp, hq, hkv, page, window):
+    """D = 64 (e4m3 cache): the tiles hold 128-byte K rows and 128 V^T rows
+    whose channels past 64 the copies fill with zeros."""
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("v", 9, 3, mtp, hq, hkv, 64, page, 1300, window)
+    inp = wl.make_decode(w)
+    inp.ctx_lens[1] = 700
+    say("paged decode D 64", mtp, hq, hkv, page, window)
+    sm = float(1.0 / np.sqrt(64))
+    g = _run(inp, dev, w.window, w.ctx, sm)
+    assert g.shape[-1] == 64
+    _check(g, _oracle(orc, inp, w.window, sm), _oracle(orc, inp, w.window, sm, False))

@@ -66,9 +66,9 @@ def test_mxfp4_pipeline_equals_base2_attention(dev, causal):
     assert np.abs(g - ref).max() <= REL * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("window,PS", [(0, 32), (20, 32), (20, 16)])
-def test_paged_decode_equals_base2_attention(dev, window, PS):
-    B, MTP, Hq, Hkv, D = 2, 4, 4, 1, 128
+@pytest.mark.parametrize("window,PS,D", [(0, 32, 128), (20, 32, 128), (20, 16, 128), (20, 32, 64)])
+def test_paged_decode_equals_base2_attention(dev, window, PS, D):
+    B, MTP, Hq, Hkv = 2, 4, 4, 1
     max_pages = 128 // PS
     ctx = np.array([100, 57], np.int32)
     q, kf, vf, ks, vs, table = dyadic_decode(93, B=B, MTP=MTP, Hq=Hq, Hkv=Hkv, D=D, PS=PS,
