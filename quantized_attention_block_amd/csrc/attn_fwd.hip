@@ -42,6 +42,11 @@
 //    max is taken on the integer scores (rounding is monotone, so
 //    max fp32(S c) = fp32(max S c)); the O/l rescale is skipped when no row of
 //    the wave changed its max; 448 is folded into the exp2 offset.
+//  - Q may arrive as the caller's fp16/bf16 tensor instead of INT8 codes: the
+//    block's 128 rows are exactly one Q scale block, so the prologue quantizes
+//    them with the quantize kernels' arithmetic (codes and scale bit-identical)
+//    and no INT8 copy of Q is written or read.  The V scales of the KV head
+//    are copied to LDS ahead of tile 0 for the epilogue.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
