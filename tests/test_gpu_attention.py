@@ -272,13 +272,15 @@ def test_single_token_and_tiny_lengths(dev, orc):
     ("llm_prefill", 4096, 128, True, torch.bfloat16),    # the benchmark's shape
     ("video_dit", 1000, 128, False, torch.bfloat16),     # outlier-heavy Q blocks
     ("llm_prefill", 200, 64, True, torch.float16),
+    ("video_dit", -700, 128, False, torch.bfloat16),     # Lq 700 against Lk 1500
 ])
 def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
     """Q quantized in the attention prologue (sage_quantize_qk(None, k) +
     sage_attn_fwd(q=...)) gives the unfused path's output bit for bit: the
     same INT8 codes and block scales, hence the same kernel arithmetic."""
     w = wl.WORKLOADS[name]
-    inp = wl.make_prefill(w, Lq=Lq, Lk=Lq, device=dev)
+    Lq, Lk = (-Lq, 1500) if Lq < 0 else (Lq, Lq)
+    inp = wl.make_prefill(w, Lq=Lq, Lk=Lk, device=dev)
     q, k, v = inp.q, inp.k, inp.v
     if D != q.shape[3] or dtype != q.dtype:
         q, k, v = (x[..., :D].to(dtype) for x in (q, k, v))
