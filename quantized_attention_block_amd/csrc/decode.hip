@@ -150,6 +150,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     // head, in bounds, and are zeroed below)
     const int r = 16 * wave + c16;
     const int mt = (r < R ? r : 0) / G, gq = (r < R ? r : 0) % G;
+    // the context length's scalar load goes out first: issued after the Q
+    // loads, it waited for them, two memory latencies in a row
+    const int ctx_raw = scalar_ptr(a.ctx_lens)[b];
     uint4 qraw[4];
     {
         // channels [32 q4, +32); MX: [16 q4, +16) and [64 + 16 q4, +16) (the
@@ -166,9 +169,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             qraw[0] = qraw[1] = qraw[2] = qraw[3] = make_uint4(0, 0, 0, 0);
         }
     }
-    // The context length is loaded next and both are awaited here, so the Q
-    // loads cannot be moved below the early exits (after the length arrives).
-    const int ctx_raw = scalar_ptr(a.ctx_lens)[b];
+    // Both are awaited here, so the Q loads cannot be moved below the early
+    // exits (after the length arrives).
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         asm volatile("" : "+v"(qraw[i].x), "+v"(qraw[i].y), "+v"(qraw[i].z), "+v"(qraw[i].w) : "s"(ctx_raw));
