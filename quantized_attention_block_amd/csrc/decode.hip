@@ -524,12 +524,23 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     const int bk = rowg / kRows, r = rowg % kRows;
     if (bk >= a.B * a.Hkv || r >= R) return;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
-    const int ctx = min(a.ctx_lens[b], a.max_pages * a.page);
+    const int ctx_raw = a.ctx_lens[b];
     const int G = a.Hq / a.Hkv;
-    const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
-    const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
     const uint8_t* base = (const uint8_t*)a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartBytes;
     const int64_t sstride = (int64_t)kRows * kPartBytes;
+    // The first batch's loads go out together with the context length's,
+    // for every allocated split (rows of splits this sequence does not have
+    // are read but never used), instead of waiting for the split count.
+    // (Split indexes are clamped to the allocated ones rather than guarded:
+    // guarded loads become branches that the compiler waits on one by one.)
+    const int na = min(kMergeBatch, a.num_splits);
+    const float4 ml_first = *(const float4*)(base + min(lane, na - 1) * sstride + 2 * kD);
+    uint32_t o_first[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) o_first[u] = *(const uint32_t*)(base + min(u, na - 1) * sstride + 4 * lane);
+    const int ctx = min(ctx_raw, a.max_pages * a.page);
+    const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
+    const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
     // Splits are taken kMergeBatch at a time with every load of a batch in
     // flight at once: lane s holds split s's (m, l), every lane two output
     // channels of each split.  With at most kMergeBatch splits (windowed
@@ -539,10 +550,17 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     for (int s0 = 0; s0 < nsp; s0 += kMergeBatch) {
         const int n = min(kMergeBatch, nsp - s0);
         float4 ml = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);   // m, l, vmax
-        if (lane < n) ml = *(const float4*)(base + (s0 + lane) * sstride + 2 * kD);
         uint32_t o[kMergeBatch];
+        if (s0 == 0) {
+            if (lane < n) ml = ml_first;
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) o[u] = u < n ? *(const uint32_t*)(base + (s0 + u) * sstride + 4 * lane) : 0u;
+            for (int u = 0; u < kMergeBatch; ++u) o[u] = o_first[u];
+        } else {
+            if (lane < n) ml = *(const float4*)(base + (s0 + lane) * sstride + 2 * kD);
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+                o[u] = u < n ? *(const uint32_t*)(base + (s0 + u) * sstride + 4 * lane) : 0u;
+        }
         const float Mn = fmaxf(M, wave_max(ml.x));
         if (Mn == -INFINITY) continue;               // no visible key so far
         if (M != -INFINITY && M != Mn) {
