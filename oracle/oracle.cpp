@@ -43,7 +43,6 @@
 namespace {
 
 const double kLog2e = 1.4426950408889634073599246810019;  // log2(e)
-const float kLog2Fp8Max = (float)8.8073549220576041074;   // fp32(log2(448))
 
 // ---------------------------------------------------------------------------
 // Rounding to a small binary floating-point format, from its definition.
@@ -74,6 +73,7 @@ double round_to_format(double x, int mant, int emin, double maxv, bool saturate)
 // finite value 448 (code 0x7E), 0x7F/0xFF are NaN, no infinities.
 const int kE4M3Mant = 3, kE4M3Emin = -6;
 const double kE4M3Max = 448.0;   // FP8_MAX of the OCP flavour [aiter #7388]
+const float kFp8Max = 448.0f;     // the same value, the static scale of P
 
 uint8_t e4m3_bits_of_value(double v) {   // v exactly representable, finite
     uint8_t s = std::signbit(v) ? 0x80 : 0x00;
@@ -394,29 +394,25 @@ int64_t orc_qk_int8_exact(const int8_t* q8, const int8_t* k8, int D) {
 //       masked keys get x = -inf;
 //   (c) m_new = max(m, max_j x_j); a = exp2(m - m_new) (0 while m = -inf);
 //       l = a * l; O = a * O (update_mdo);
-//   (d) the FP8_MAX-scaled probability 448 * 2^(x_j - m_new) is evaluated as
-//       q_j = exp2(fma(float(S_j), c, -m')) with m' = fp32(m_new - fp32(log2
-//       448)): one rounding for the exponent, FP8_MAX folded into it;
-//       l += q_j in key order (accumulate_d, from the fp32 values, before
-//       conversion; l therefore carries the factor 448);
-//   (e) P8_j = e4m3(q_j) (RS_32_to_8; 448 = FP8_MAX of [aiter #7388], valid
-//       because the unscaled probability is <= 1);
+//   (d) p_j = exp2(x_j - m_new); l += p_j in key order (accumulate_d, from the
+//       fp32 probabilities, before their conversion);
+//   (e) P8_j = e4m3(fp32(448 * p_j)) (RS_32_to_8: 448 = FP8_MAX, the largest
+//       e4m3 value, scales P as in [aiter #7388] Changes; valid because
+//       p_j <= 1);
 //   (f) O[d] += fp32(sum_j dec(P8_j) * dec(V8[j, d])) with the tile's sum exact.
-// Epilogue: out[d] = fp32(fp32(O[d] * v_scale[d]) / l) (the fused V scale; l
-// holds 448 sum p, i.e. the epilogue's 1/FP8_MAX); l == 0 -> 0.
+// Epilogue: out[d] = fp32(fp32(O[d] * v_scale[d]) / fp32(448 * l)) (the fused
+// V scale, and the epilogue's 1/FP8_MAX of [aiter #7388]); l == 0 -> 0.
 // READINGS: exp2 with log2(e) folded into alpha; exp2 is evaluated in binary64
-// and rounded once; the pages fix no rounding order for 448 * 2^(x - m), and
-// since it decides the e4m3 code of P, it is evaluated in the order the fused
-// kernel uses (the fma and the folded log2 448 above); the tile length BN and
-// the ascending order are part of the numeric definition (the running max
-// decides how P is rounded), so the caller passes the kernel's BN.
-// Pins: with quantization off (ORC_QK_FLOAT, quant_pv = 0: x = fp32(S alpha),
-// p = exp2(x - m), out = O / l) it equals exact attention within 1e-6 and is
-// invariant to BN; with V = 1 the output is the row sum of P8 / l, which lies
-// within the e4m3 rounding bound of 1; on inputs where every rounding step is
-// exact (integer scores in log2 units within 15 of the row max, power-of-two
-// or unit scales, codes equal to the values, K mean exactly 0) the quantized
-// INT8 and MXFP4 results equal base-2 attention on those scores, computed
+// and rounded once; the tile length BN and the ascending order are part of the
+// numeric definition (the running max decides how P is rounded), so the
+// caller passes the kernel's BN.
+// Pins: with quantization off (ORC_QK_FLOAT, quant_pv = 0: P and V stay fp32,
+// out = O / l) it equals exact attention within 1e-6 and is invariant to BN;
+// with V = 1 the output is the row sum of P8 / (448 l), which lies within the
+// e4m3 rounding bound of 1; on inputs where every rounding step is exact
+// (integer scores in log2 units within 15 of the row max, power-of-two or
+// unit scales, codes equal to the values, K mean exactly 0) the quantized INT8
+// and MXFP4 results equal base-2 attention on those scores, computed
 // independently in float64 (a dropped rescale, 448 factor, scale, mask or V
 // index each break it).
 
@@ -492,21 +488,13 @@ struct EmulRow {
             const float a = (m == -INFINITY) ? 0.0f : exp2_f32(m - m_new);
             l = a * l;
             for (int d = 0; d < D; ++d) O[d] = a * O[d];
-            if (p.quant_pv) {
-                const float mq = m_new - kLog2Fp8Max;
-                for (int t = 0; t < nt; ++t) {
-                    pr[t] = vis[t] ? exp2_f32(std::fma(Sf[t], cs[t], -mq)) : 0.0f;
-                    l = l + pr[t];
-                }
-            } else {
-                for (int t = 0; t < nt; ++t) {
-                    pr[t] = vis[t] ? exp2_f32(Sf[t] * cs[t] - m_new) : 0.0f;
-                    l = l + pr[t];
-                }
+            for (int t = 0; t < nt; ++t) {
+                pr[t] = vis[t] ? exp2_f32(Sf[t] * cs[t] - m_new) : 0.0f;
+                l = l + pr[t];
             }
             std::fill(acc.begin(), acc.end(), 0.0);
             if (p.quant_pv) {
-                for (int t = 0; t < nt; ++t) p8[t] = orc_e4m3_encode(pr[t]);
+                for (int t = 0; t < nt; ++t) p8[t] = orc_e4m3_encode(kFp8Max * pr[t]);
                 for (int t = 0; t < nt; ++t) {
                     double pv = dec[p8[t]];
                     if (pv == 0.0) continue;
@@ -528,7 +516,7 @@ struct EmulRow {
                 out[d] = 0.0f;
             } else if (p.quant_pv) {
                 float vs = in.v_scale[((int64_t)b * p.H + h) * D + d];
-                out[d] = (O[d] * vs) / l;
+                out[d] = (O[d] * vs) / (kFp8Max * l);
             } else {
                 out[d] = O[d] / l;
             }
