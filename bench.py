@@ -1,29 +1,33 @@
 """Benchmark of the quantized-attention hot path on one MI355X.
 
-One step = quantize Q/K (K channel mean + INT8 blocks) + quantize V (e4m3,
-per-channel scale, transposed) + fused quantized attention, on the
-LLM-prefill workload (B=2, H=32, Lq=Lk=4096, D=128, bf16, causal), inputs
-resident in HBM, launched eagerly; the same step replayed from a HIP graph
-(each replay first checked bit-equal to an eager step) is reported beside it.
-Prints one JSON line:
+One step = quantize K (channel mean + INT8 blocks) + quantize V (e4m3,
+per-channel scale, transposed) + quantized attention with Q quantized to INT8
+in the attention kernel's prologue, on the video-DiT workload (B=1, H=40,
+Lq=Lk=32760, D=128, bf16, non-causal, Q/K/V strided views of one stacked
+[B, L, 3, H, D] buffer) -- the largest configuration of the metric that fits
+one GPU.  Inputs are resident in HBM, outputs and workspaces preallocated,
+launches eager; the same step replayed from a HIP graph (each replay first
+checked bit-equal to an eager step) is reported beside it.  Prints one JSON
+line:
 
-  value        = 4 B H Lq Lk D / t_step  (the metric's own formula, TOPS)
-  roofline     = the attention kernel alone: algorithmic ops (unmasked causal
-                 pairs, 4 D per pair) / its average launch time, measured with
-                 HIP events on the stream it runs on, against the INT8/FP8 MFMA
-                 peak (5.0 POPS dense)
-  cpu_baseline = the CPU oracle (quantize + step-by-step emulation) on a
-                 bounded sample of query rows of the same workload
-  extra        = the paged FP8 decode workload (HBM GB/s) and, with --all,
-                 the video-DiT INT8 and MXFP4 workloads.
+  value        = 4 B H Lq Lk D / t_step  (the metric's formula, TOPS)
+  roofline     = the attention kernel alone: algorithmic ops (4 D per visible
+                 (query, key) pair) / its average launch time, measured with
+                 HIP events on the stream it runs on, against the INT8/FP8
+                 MFMA peak (5.0 POPS dense)
+  cpu_baseline = the CPU oracle, both the quantization-emulating and the exact
+                 fp64 one, on bounded seeded row samples of video-DiT and
+                 LLM-prefill: one warm-up and three timed runs each, median
+  extra        = the same measurements for LLM-prefill (causal) and the MXFP4
+                 video-DiT path, and the paged FP8 / MXFP4 decodes (HBM GB/s).
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -33,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_MFMA_TOPS = 5000.0      # INT8 and FP8 dense MFMA, MI355X
 PEAK_MXFP4_MIX_TOPS = 4.0 / (2.0 / 10100.0 + 2.0 / 5000.0)   # half FP4 QK, half FP8 PV
 PEAK_HBM_GBS = 8000.0
+HEADLINE = "video_dit"
 
 
 def _src_hash(*names):
@@ -49,8 +54,8 @@ def _traffic(kernel_key, src_names):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            t = json.load(f)[kernel_key]
-    except (OSError, KeyError, ValueError):
+            t = json.load(f)["kernels"][kernel_key]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if t.get("src_hash") != _src_hash(*src_names):
         return None
@@ -58,9 +63,8 @@ def _traffic(kernel_key, src_names):
 
 
 def _events_time(fn, reps, stream):
-    """Average duration of one call of fn (one kernel launch), each call
-    bracketed by its own pair of HIP events on `stream` (gaps between
-    launches are not counted)."""
+    """Average duration of one call of fn, each call bracketed by its own pair
+    of HIP events on `stream` (gaps between calls are not counted)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for a, b in ev:
@@ -71,19 +75,29 @@ def _events_time(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e-3   # seconds per call
 
 
-def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
-    """fused_q (INT8): Q is quantized in the attention kernel's prologue
-    (sage_quantize_qk(None, k) + sage_attn_fwd(q=...)), which gives the
-    unfused step's output bit for bit; the unfused step is timed beside it."""
+def _wall(fn, steps):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def prefill_bench(wname, steps, warmup, dev, time_unfused=False):
+    """INT8 workloads quantize Q in the attention kernel's prologue
+    (sage_quantize_qk(None, k) + sage_attn_fwd(q=...)); that step's output is
+    checked bit-equal to the unfused step's (Q quantized by sage_quantize_qk)
+    before timing."""
     from quantized_attention_block_amd import sage
     from quantized_attention_block_amd import workloads as wl
     w = wl.WORKLOADS[wname]
-    mode = (sage.QK_MXFP4 if w.qk_mode == "mxfp4" else sage.QK_INT8) if mode is None else mode
-    fused_q = fused_q and mode == sage.QK_INT8
+    mode = sage.QK_MXFP4 if w.qk_mode == "mxfp4" else sage.QK_INT8
+    fused_q = mode == sage.QK_INT8
+    print(f"bench: {wname}: drawing inputs", file=sys.stderr, flush=True)
     inp = wl.make_prefill(w, device=dev)
     had = sage.Hadamard(dev.index or 0) if mode == sage.QK_MXFP4 else None
     stream = torch.cuda.current_stream(dev)
-    # preallocated outputs and workspaces: the timed step only launches kernels
     qk_in = None if fused_q else inp.q
     qk = sage.sage_quantize_qk(qk_in, inp.k, mode=mode, hadamard=had, want_mean=False)
     v_q, v_s = sage.sage_quantize_v(inp.v)
@@ -92,8 +106,10 @@ def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
                         dtype=torch.uint8, device=dev)
     ws_v = torch.empty(sage.sage_quantize_v_workspace_size(inp.v), dtype=torch.uint8, device=dev)
 
-    def quant():
+    def quant_qk():
         sage.sage_quantize_qk(qk_in, inp.k, mode=mode, hadamard=had, workspace=ws_qk, into=qk)
+
+    def quant_v():
         sage.sage_quantize_v(inp.v, workspace=ws_v, into=(v_q, v_s))
 
     def attn():
@@ -101,9 +117,11 @@ def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
                            q=inp.q if fused_q else None)
 
     def step():
-        quant()
+        quant_qk()
+        quant_v()
         attn()
 
+    print(f"bench: {wname}: warm-up", file=sys.stderr, flush=True)
     # untimed pre-warm (~0.2 s of steps) so clocks have settled before the
     # W warm-up steps and the K timed ones
     t0 = time.perf_counter()
@@ -112,15 +130,29 @@ def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
+    t_step = _wall(step, steps)
+    # the unfused step (Q's INT8 copy written and read) gives the same bits
+    t_step_unfused = None
+    if fused_q:
+        qk_u = sage.sage_quantize_qk(inp.q, inp.k, want_mean=False)
+        out_u = torch.empty_like(out)
+
+        def step_u():
+            sage.sage_quantize_qk(inp.q, inp.k, workspace=ws_qk, into=qk_u)
+            quant_v()
+            sage.sage_attn_fwd(qk_u, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out_u)
         step()
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / steps
-    # The same step captured once in a HIP graph and replayed (context): each
-    # replay is first checked bit for bit against an eager step, with eager
-    # work in between.
+        step_u()
+        torch.cuda.synchronize()
+        if not torch.equal(out_u, out):
+            raise RuntimeError(f"{wname}: fused Q quantization differs from the unfused step")
+        if time_unfused:
+            for _ in range(warmup):
+                step_u()
+            t_step_unfused = _wall(step_u, steps)
+        del qk_u, out_u
+    # The same step captured once in a HIP graph and replayed: each replay is
+    # first checked bit for bit against an eager step, with eager work between.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
@@ -136,34 +168,13 @@ def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
             raise RuntimeError(f"{wname}: graph replay differs from the eager step")
     for _ in range(warmup):
         graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    t_step_graph = (time.perf_counter() - t0) / steps
-    t_step_unfused = None
-    if fused_q:   # the unfused step (Q's INT8 copy written and read), same inputs
-        qk_u = sage.sage_quantize_qk(inp.q, inp.k, want_mean=False)
-        out_u = torch.empty_like(out)
-
-        def step_u():
-            sage.sage_quantize_qk(inp.q, inp.k, workspace=ws_qk, into=qk_u)
-            sage.sage_quantize_v(inp.v, workspace=ws_v, into=(v_q, v_s))
-            sage.sage_attn_fwd(qk_u, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out_u)
-        for _ in range(warmup + 1):
-            step_u()
-        torch.cuda.synchronize()
-        if not torch.equal(out_u, out):
-            raise RuntimeError(f"{wname}: fused Q quantization differs from the unfused step")
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step_u()
-        torch.cuda.synchronize()
-        t_step_unfused = (time.perf_counter() - t0) / steps
-    # attention kernel alone, HIP events on its stream
-    attn()
-    t_attn = min(_events_time(attn, max(steps, 10), stream) for _ in range(3))
+    t_step_graph = _wall(graph.replay, steps)
+    del graph
+    # each part alone, HIP events on the stream it runs on
+    reps = max(steps, 10)
+    t_attn = min(_events_time(attn, reps, stream) for _ in range(3))
+    t_qk = min(_events_time(quant_qk, reps, stream) for _ in range(3))
+    t_v = min(_events_time(quant_v, reps, stream) for _ in range(3))
     L = w.Lq
     pairs = w.B * w.H * (L * (L + 1) // 2 if w.causal else w.Lq * w.Lk)
     ops_alg = 4.0 * pairs * w.D
@@ -171,21 +182,34 @@ def prefill_bench(wname, steps, warmup, dev, mode=None, fused_q=True):
     peak = PEAK_MXFP4_MIX_TOPS if mode == sage.QK_MXFP4 else PEAK_MFMA_TOPS
     achieved = ops_alg / t_attn / 1e12
     src = ["attn_fwd.hip", "sage_device.hpp"]
-    return dict(w=w, t_step=t_step, t_step_graph=t_step_graph, t_attn=t_attn, fused_q=fused_q,
-                t_step_unfused=t_step_unfused,
-                value=literal / t_step / 1e12,
-                attn_literal_tops=literal / t_attn / 1e12,
-                roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                          "traffic": _traffic(f"attn_fwd_{wname}", src)})
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": _traffic(f"attn_fwd_{wname}", src)}
+    res = {"value": round(literal / t_step / 1e12, 2), "unit": "TOPS",
+           "ms_per_step": round(t_step * 1e3, 4),
+           "ms_per_step_hip_graph": round(t_step_graph * 1e3, 4),
+           "attn_kernel_us": round(t_attn * 1e6, 2),
+           "attn_kernel_tops_literal": round(literal / t_attn / 1e12, 1),
+           "attn_algorithmic_ops": ops_alg,
+           "quantize_qk_us": round(t_qk * 1e6, 2), "quantize_v_us": round(t_v * 1e6, 2),
+           "step": ("quantize_qk (K) + quantize_v + attn_fwd (Q quantized in its prologue)"
+                    if fused_q else "quantize_qk (Hadamard + MXFP4) + quantize_v + attn_fwd"),
+           "roofline": roof}
+    if t_step_unfused is not None:
+        res["ms_per_step_unfused_q"] = round(t_step_unfused * 1e3, 4)
+    del inp, qk, v_q, v_s, out, ws_qk, ws_v
+    torch.cuda.empty_cache()
+    return w, res
 
 
 def decode_bench(steps, warmup, dev, pools=32, mx=False):
-    """mx: the same decode over an MXFP4 cache (E2M1 + E8M0, the next step the
-    aiter page names), timed the same way."""
+    """Paged decode (decode + merge) of the decode workload over an FP8 e4m3
+    cache, or (mx) over an MXFP4 cache (E2M1 + E8M0) of the same shape."""
     from quantized_attention_block_amd import sage
     from quantized_attention_block_amd import workloads as wl
     w = wl.WORKLOADS["paged_decode"]
+    print(f"bench: paged decode ({'mxfp4' if mx else 'fp8'}): drawing {pools} KV pools",
+          file=sys.stderr, flush=True)
     # rotate among independent KV pools (> 256 MB in total) so the timed reads
     # come from HBM, not the MALL
     sets = []
@@ -222,8 +246,8 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
     for _ in range(warmup * 10):
         call()
     torch.cuda.synchronize()
-    # one decode (decode + merge kernels) per pool, captured once and replayed:
-    # the device time per call without Python launch overhead
+    # one decode per pool, captured once and replayed: the device time per
+    # call without Python launch overhead
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(pools):
@@ -240,6 +264,8 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
     alg_bytes = w.batch * w.hkv * keys * per_key + 2 * (w.batch * w.mtp * w.hq * w.D * 2)
     gbs = alg_bytes / t / 1e9
     fmt = "MXFP4 (E2M1 + E8M0)" if mx else "FP8"
+    del sets, graph
+    torch.cuda.empty_cache()
     return {"metric": f"paged {fmt} decode HBM GB/s (decode + merge)", "value": round(gbs, 1),
             "unit": "GB/s", "us_per_call": round(t * 1e6, 3),
             "us_per_call_eager_launch": round(t_eager * 1e6, 2), "algorithmic_bytes": alg_bytes,
@@ -252,44 +278,68 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
                                              ["decode.hip", "sage_device.hpp"])}}
 
 
-def cpu_baseline(wname, target_s=15.0):
-    """The oracle as it stands, on a bounded sample: quantize one (b, h) head
-    of the workload and emulate a seeded sample of its query rows."""
+def cpu_baseline(target_run_s=1.5):
+    """The oracle as it stands, on bounded samples: for video-DiT and
+    LLM-prefill, one (b, h) head is quantized and a seeded sample of its query
+    rows is run through the quantization-emulating oracle, and the same rows
+    through the exact fp64 oracle.  The sample is sized to ~target_run_s per
+    run; one warm-up run, then three timed runs, median.  Throughput uses the
+    metric's formula per query row, 4 Lk D ops (LLM-prefill is causal, so
+    that counts each row's masked keys too, as the metric's formula does)."""
     import numpy as np
     sys.path.insert(0, ROOT)
     import oracle
     from quantized_attention_block_amd import workloads as wl
-    w = wl.WORKLOADS[wname]
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
-    inp = wl.make_prefill(w, B=1, H=1)
-    canon = lambda t: t.float().permute(0, 2, 1, 3).contiguous().numpy()
-    q, k, v = canon(inp.q), canon(inp.k), canon(inp.v)
-    rng = np.random.default_rng(11)
+    results = {}
+    for wname in (HEADLINE, "llm_prefill"):
+        w = wl.WORKLOADS[wname]
+        print(f"bench: cpu baseline on {wname} ({cores} threads)", file=sys.stderr, flush=True)
+        inp = wl.make_prefill(w, B=1, H=1)
+        canon = lambda t: t.float().permute(0, 2, 1, 3).contiguous().numpy()
+        q, k, v = canon(inp.q), canon(inp.k), canon(inp.v)
+        del inp
+        for kind in ("emulated", "exact"):
+            rng = np.random.default_rng(11)
 
-    def run(nrows):
-        ri = np.sort(rng.integers(0, w.Lq, nrows))
-        rows = np.stack([np.zeros_like(ri), np.zeros_like(ri), ri], 1)
-        t0 = time.perf_counter()
-        oracle.prefill_int8_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale, BN=64,
-                                     rows=rows, nthreads=cores)
-        return time.perf_counter() - t0
+            def rows_of(n):
+                ri = np.sort(rng.integers(0, w.Lq, n))
+                return np.stack([np.zeros_like(ri), np.zeros_like(ri), ri], 1)
 
-    # the per-run cost is one head's quantization plus a per-row emulation
-    # cost: two probes give both, then the sample is sized to ~target_s
-    t1, t2 = run(64), run(512)
-    per_row = max((t2 - t1) / 448.0, 1e-7)
-    nrows = int(max(512, min(2_000_000, (target_s - t1) / per_row)))
-    t = run(nrows)
-    literal = 4.0 * nrows * w.Lk * w.D      # same formula per query row as the GPU value
-    return {"value": round(literal / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
-            "seconds": round(t, 2),
-            "sample": f"{nrows} seeded query rows of one (b,h) head of {w.name} "
-                      f"(Lk={w.Lk}, D={w.D}, causal={w.causal}): K mean + INT8/e4m3 quantization "
-                      f"of that head + step-by-step emulation of those rows, C++ threads={cores}"}
+            def run(rows):
+                t0 = time.perf_counter()
+                if kind == "emulated":
+                    oracle.prefill_int8_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale,
+                                                 BN=64, rows=rows, nthreads=cores)
+                else:
+                    oracle.attn_exact(q, k, v, w.causal, w.sm_scale, rows=rows, nthreads=cores)
+                return time.perf_counter() - t0
+
+            # a fixed cost (the head's quantization) plus a per-row cost: two
+            # probes give both, then the sample is sized to ~target_run_s
+            t1, t2 = run(rows_of(4 * cores)), run(rows_of(36 * cores))
+            per_row = max((t2 - t1) / (32 * cores), 1e-7)
+            nrows = int(max(8 * cores, min(2_000_000, (target_run_s - min(t1, t2) / 2) / per_row)))
+            rows = rows_of(nrows)
+            run(rows)   # warm-up
+            ts = [run(rows) for _ in range(3)]
+            t = statistics.median(ts)
+            results[f"{wname}_{kind}"] = {
+                "value": round(4.0 * nrows * w.Lk * w.D / t / 1e12, 6), "unit": "TOPS",
+                "seconds_median": round(t, 3), "seconds_runs": [round(x, 3) for x in ts],
+                "rows": nrows}
+    head = results[f"{HEADLINE}_emulated"]
+    w = wl.WORKLOADS[HEADLINE]
+    return {"value": head["value"], "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": (f"{head['rows']} seeded query rows of one (b,h) head of {HEADLINE} "
+                       f"(Lk={w.Lk}, D={w.D}): K mean + INT8/e4m3 quantization of that head + "
+                       f"step-by-step emulation of those rows, C++ threads={cores}; median of 3 "
+                       f"timed runs after 1 warm-up; 4 Lk D ops per row"),
+            "runs": results}
 
 
 def main():
@@ -297,10 +347,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llm_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time the video-DiT workloads")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -310,40 +358,32 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    r = prefill_bench(args.workload, args.steps, args.warmup, dev)
-    w = r["w"]
-    extra = {"attn_kernel_us": round(r["t_attn"] * 1e6, 1),
-             "attn_kernel_tops_literal": round(r["attn_literal_tops"], 1),
-             "quantize_us": round((r["t_step"] - r["t_attn"]) * 1e6, 1),
-             "ms_per_step_hip_graph": round(r["t_step_graph"] * 1e3, 4)}
-    if r["t_step_unfused"] is not None:
-        extra["ms_per_step_unfused_q"] = round(r["t_step_unfused"] * 1e3, 4)
-        extra["tops_unfused_q"] = round(r["value"] * r["t_step"] / r["t_step_unfused"], 2)
-    if not args.no_decode:
+    w, r = prefill_bench(HEADLINE, args.steps, args.warmup, dev)
+    extra = {"attn_kernel_us": r["attn_kernel_us"],
+             "attn_kernel_tops_literal": r["attn_kernel_tops_literal"],
+             "quantize_qk_us": r["quantize_qk_us"], "quantize_v_us": r["quantize_v_us"],
+             "ms_per_step_hip_graph": r["ms_per_step_hip_graph"]}
+    if not args.no_extra:
+        for wn in ("video_dit_mxfp4", "llm_prefill"):
+            _, rr = prefill_bench(wn, args.steps, args.warmup, dev, time_unfused=wn == "llm_prefill")
+            extra[wn] = rr
         extra["paged_decode"] = decode_bench(args.steps, args.warmup, dev)
         extra["paged_decode_mxfp4"] = decode_bench(args.steps, args.warmup, dev, mx=True)
-    if args.all:
-        for wn in ("video_dit", "video_dit_mxfp4"):
-            rr = prefill_bench(wn, max(3, args.steps // 4), 2, dev)
-            extra[wn] = {"value": round(rr["value"], 1), "unit": "TOPS",
-                         "ms_per_step": round(rr["t_step"] * 1e3, 3),
-                         "attn_kernel_ms": round(rr["t_attn"] * 1e3, 3), "roofline": rr["roofline"]}
     line = {
         "metric": "quantized attn fwd TOPS (4BHLqLkD/t) + % gfx950 MFMA peak; decode HBM GB/s",
-        "value": round(r["value"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(r["t_step"] * 1e3, 4),
+        "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8 QK / fp8-e4m3 PV, fp32 softmax, bf16 in/out", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len_q": w.Lq,
                    "seq_len_k": w.Lk, "head_dim": w.D, "causal": w.causal,
-                   "q_block": w.q_block, "k_block": w.k_block,
-                   "step": ("quantize_qk (K) + quantize_v + attn_fwd (Q quantized in its prologue)"
-                            if r["fused_q"] else "quantize_qk + quantize_v + attn_fwd")},
+                   "inputs": "strided [B,L,H,D] views of one stacked [B,L,3,H,D] bf16 buffer",
+                   "q_block": w.q_block, "k_block": w.k_block, "step": r["step"]},
         "roofline": r["roofline"],
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload)
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 
 

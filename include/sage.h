@@ -217,7 +217,8 @@ int32_t sage_attn_kv_tile(void);
  *   out        BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides)
  * With window W > 0 query position p sees keys [p - W + 1, p]; otherwise
  * [0, p].  The work is split into 256-token tiles aligned to absolute
- * positions, one split per tile (page: "each tile is its own task"); splits
+ * positions, one split per tile ([aiter #7388], "Batch-first plan grid
+ * removal": one task per 256-token window tile); splits
  * write (m, l, O) partials to the workspace and a merge step combines them
  * (O is kept normalized, O / l, in fp16 scaled into [-448, 448]: the merge's
  * inputs carry a relative rounding of 2^-11, below the bf16 output's 2^-9).
@@ -228,8 +229,8 @@ int32_t sage_attn_kv_tile(void);
  * is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
  * below ctx_lens[b] must be valid page indices, and ctx_lens[b] <=
  * params.max_ctx; device data is not validated, but a page id outside
- * [0, P) reads page 0 and a length beyond the page table's coverage is
- * clamped to it, so bad device data gives wrong numbers, never a fault.
+ * [0, P) reads page 0 and a length above max_ctx is treated as max_ctx, so
+ * bad device data gives wrong numbers, never a fault.
  * MXFP4 cache ([aiter #7388] names pa_decode_mxfp4: E2M1 KV, E8M0 scales;
  * the layout is this library's reading), chosen by k_cache's dtype:
  *   k_cache FP4X2_E2M1 [P, Hkv, page, D/2], k_scale E8M0 [P, Hkv, page, D/32]
@@ -294,6 +295,18 @@ sage_status sage_set_quant_wait_us(int32_t us);
 sage_status sage_debug_qk_tile(const sage_tensor* q_q, const sage_tensor* k_q,
                                int32_t q0, int32_t nq, int32_t k0, int32_t nk,
                                const sage_tensor* out, void* stream);
+
+/* Test hook: fp32 S = Q K^T of MXFP4 codes, for query rows [q0, q0 + nq)
+ * and keys [k0, k0 + nk) of every (b, h), computed by sage_attn_fwd's own
+ * MXFP4 QK step (the block-scaled MFMA, same operand layout and order): per
+ * 32-channel block the E2M1 products scaled by 2^(e_q + e_k), summed in fp32
+ * ([xDiT #665]: the Sage v2 MXFP4 path).  Ranges as for sage_debug_qk_tile.
+ *   q_q FP4X2_E2M1 [B, H, Lqp, 64], q_scale E8M0 [B, H, Lqp, 4] (D = 128),
+ *   k_q, k_scale likewise with Lkp; out F32 [B, H, nq, nk] contiguous. */
+sage_status sage_debug_qk_tile_mx(const sage_tensor* q_q, const sage_tensor* q_scale,
+                                  const sage_tensor* k_q, const sage_tensor* k_scale, int32_t q0,
+                                  int32_t nq, int32_t k0, int32_t nk, const sage_tensor* out,
+                                  void* stream);
 
 /* Thread-local message of the last failure on this thread ("" if none). */
 const char* sage_last_error(void);

@@ -248,6 +248,27 @@ def qk_int8_tile(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
     return np.matmul(q8.astype(np.int64), np.swapaxes(k8.astype(np.int64), -1, -2))
 
 
+def qk_mxfp4_tile(q4: np.ndarray, q_e8: np.ndarray, k4: np.ndarray, k_e8: np.ndarray,
+                  partial_blocks: Optional[int] = None) -> np.ndarray:
+    """Exact S = Q K^T of MXFP4 operands (one E2M1 code per byte, [..., M, D]
+    and [..., N, D], E8M0 scales [..., M, D/32] and [..., N, D/32]) in float64:
+    per 32-channel block the integer sum of (2 e2m1_q)(2 e2m1_k) times
+    2^(e_q + e_k - 2), e = E8M0 code - 127.  partial_blocks: sum only the
+    first that many blocks.  Exact for every input of this library (block sums
+    < 2^13, exponents within binary64's range)."""
+    dec2 = np.array([int(round(2 * e2m1_decode(c))) for c in range(16)], np.int64)
+    qi, ki = dec2[np.asarray(q4)], dec2[np.asarray(k4)]
+    nb = qi.shape[-1] // 32 if partial_blocks is None else partial_blocks
+    S = 0.0
+    for b in range(nb):
+        sl = slice(32 * b, 32 * b + 32)
+        isum = np.matmul(qi[..., sl], np.swapaxes(ki[..., sl], -1, -2))
+        ex = (np.asarray(q_e8, np.int64)[..., b][..., :, None] - 127) + \
+             (np.asarray(k_e8, np.int64)[..., b][..., None, :] - 127) - 2
+        S = S + np.ldexp(isum.astype(np.float64), ex)
+    return S
+
+
 # ---- attention -------------------------------------------------------------
 def _rows_arg(rows):
     if rows is None:

@@ -600,7 +600,8 @@ int orc_attn_exact(const float* q, const float* k, const float* v,
 // lives in page page_table[b][t / page_size], slot t % page_size; query head
 // hq reads KV head hq / (Hq / Hkv).
 // Splits are `tile`-token windows aligned to absolute positions, one split per
-// tile the sequence's window union touches ("each tile is its own task").
+// tile the sequence's window union touches (one task per window tile, as the
+// "Batch-first plan grid removal" section describes the plan).
 // Per split and query row:
 //   quant: Q row -> e4m3 with a dynamic scale (READING: per (token, head) row,
 //          q_scale = fp32(amax / 448), codes e4m3(fp32(q * fp32(448 / amax)));

@@ -607,6 +607,7 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     a.window = p->window;
     a.v_transposed = p->v_transposed;
     a.num_splits = s.splits;
+    a.max_ctx = p->max_ctx;
     a.mx = mx ? 1 : 0;
     a.scale_per_tensor = per_tensor ? 1 : 0;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)s.D));
@@ -689,6 +690,37 @@ sage_status sage_debug_qk_tile(const sage_tensor* q_q, const sage_tensor* k_q, i
                                                (int)H, (int)Lqp, (int)Lkp, (int)D, q0, nq, k0, nk,
                                                (int32_t*)out->data, (hipStream_t)stream),
                          "debug qk tile");
+}
+
+sage_status sage_debug_qk_tile_mx(const sage_tensor* q_q, const sage_tensor* q_scale,
+                                  const sage_tensor* k_q, const sage_tensor* k_scale, int32_t q0,
+                                  int32_t nq, int32_t k0, int32_t nk, const sage_tensor* out,
+                                  void* stream) {
+    sage_status st = check_basic(q_q, "q_q", 4);
+    if (st) return st;
+    if ((st = check_basic(k_q, "k_q", 4))) return st;
+    const int64_t B = q_q->shape[0], H = q_q->shape[1], Lqp = q_q->shape[2], Lkp = k_q->shape[2];
+    const int64_t D = 2 * q_q->shape[3];
+    if (D != 128) return fail(SAGE_ERR_SHAPE, "MXFP4 score tiles need head dim 128 (q_q [B, H, Lqp, 64])");
+    const int64_t qs[4] = {B, H, Lqp, D / 2}, ks[4] = {B, H, Lkp, D / 2};
+    const int64_t qe[4] = {B, H, Lqp, D / 32}, ke[4] = {B, H, Lkp, D / 32};
+    if ((st = check_exact(q_q, "q_q", SAGE_FP4X2_E2M1, 4, qs))) return st;
+    if ((st = check_exact(k_q, "k_q", SAGE_FP4X2_E2M1, 4, ks))) return st;
+    if ((st = check_exact(q_scale, "q_scale", SAGE_E8M0, 4, qe))) return st;
+    if ((st = check_exact(k_scale, "k_scale", SAGE_E8M0, 4, ke))) return st;
+    if (Lqp % 128 || Lkp % 128) return fail(SAGE_ERR_SHAPE, "q_q / k_q lengths must be padded to 128");
+    if (q0 < 0 || nq < 32 || q0 % 32 || nq % 32 || q0 + nq > Lqp)
+        return fail(SAGE_ERR_SHAPE, "query range must be 32-aligned and inside q_q");
+    if (k0 < 0 || nk < 128 || k0 % 128 || nk % 128 || k0 + nk > Lkp)
+        return fail(SAGE_ERR_SHAPE, "key range must be 128-aligned and inside k_q");
+    const int64_t os[4] = {B, H, nq, nk};
+    if ((st = check_exact(out, "out", SAGE_F32, 4, os))) return st;
+    if ((st = check_device())) return st;
+    return launch_status(sage::launch_debug_qk_mx((const uint8_t*)q_q->data, (const uint8_t*)q_scale->data,
+                                                  (const uint8_t*)k_q->data, (const uint8_t*)k_scale->data,
+                                                  (int)B, (int)H, (int)Lqp, (int)Lkp, q0, nq, k0, nk,
+                                                  (float*)out->data, (hipStream_t)stream),
+                         "debug qk tile (MXFP4)");
 }
 
 }  // extern "C"

@@ -664,6 +664,40 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* 
     }
 }
 
+// Test hook: fp32 S = Q K^T of MXFP4 codes (E2M1 with E8M0 block scales),
+// through the same staging and qk_subtile_mx as the attention kernel.
+template <int D>
+__global__ __launch_bounds__(64) void k_debug_qk_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k,
+                                                    const uint8_t* ks, int Lqp, int Lkp, int q0, int k0,
+                                                    int nq, int nk, float* out) {
+    using G = Geo<D, true>;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[G::kStageBytes];
+    const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+    const int qg = blockIdx.x, kg = blockIdx.y, bh = blockIdx.z;
+    const uint8_t* qbase = q + (int64_t)bh * Lqp * G::kRowBytes;
+    const uint8_t* qsc = qs + (int64_t)bh * Lqp * (D / 32);
+    const uint8_t* kbase = k + ((int64_t)bh * Lkp + k0) * G::kRowBytes;
+    const uint8_t* ksc = ks + ((int64_t)bh * Lkp + k0) * (D / 32);
+    // stage K rows [k0 + kBN kg, +kBN) and their scales; the V part is not used
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)nk * G::kRowBytes);
+    const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ksc, (int64_t)nk * (D / 32));
+    TileDma<D, true, 1>::issue(stage, krs, ksrs, krs, 0, kg, 0, lane, false);
+    wait_dma();
+    __syncthreads();
+    QFrag<D, true> qf;
+    load_qfrag<D, true>(qf, qbase, qsc, q0 + 32 * qg + col, lane);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+        const v16f s = qk_subtile_mx<D>(stage, qf, t, lane);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = kBN * kg + 32 * t + 16 * half + e;   // relative to k0
+            const int qq = 32 * qg + col;                         // relative to q0
+            out[((int64_t)bh * nq + qq) * nk + key] = s[e];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
@@ -696,6 +730,14 @@ hipError_t launch_debug_qk(const int8_t* q, const int8_t* k, int B, int H, int L
         k_debug_qk<128><<<grid, 64, 0, stream>>>(q, k, Lqp, Lkp, q0, k0, nq, nk, out);
     else
         k_debug_qk<64><<<grid, 64, 0, stream>>>(q, k, Lqp, Lkp, q0, k0, nq, nk, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_qk_mx(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                              const uint8_t* k_scale, int B, int H, int Lqp, int Lkp, int q0, int nq,
+                              int k0, int nk, float* out, hipStream_t stream) {
+    dim3 grid(nq / 32, nk / kBN, B * H);
+    k_debug_qk_mx<128><<<grid, 64, 0, stream>>>(q, q_scale, k, k_scale, Lqp, Lkp, q0, k0, nq, nk, out);
     return hipGetLastError();
 }
 

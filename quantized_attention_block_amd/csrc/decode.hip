@@ -4,7 +4,7 @@
 // Source: ROCm/aiter pull request 7388 (FlyDSL pa_decode), sections Changes
 // and "Batch-first plan grid removal": paged attention decode with an FP8 KV
 // cache and per-token scales, MTP query tokens, GQA, sliding windows; the work
-// is cut into 256-token window tiles, "each tile is its own task"; a reduce
+// is cut into 256-token window tiles, one task per tile; a reduce
 // step merges the partitions and is timed together with the decode; Q and P
 // are quantized to the cache's FP8 format (FP8_MAX = 448 on gfx950's OCP e4m3).
 //
@@ -175,8 +175,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     for (int i = 0; i < 4; ++i)
         asm volatile("" : "+v"(qraw[i].x), "+v"(qraw[i].y), "+v"(qraw[i].z), "+v"(qraw[i].w) : "s"(ctx_raw));
 
-    // context lengths beyond what the page table covers are clamped to it
-    const int ctx = min(ctx_raw, a.max_pages * a.page);
+    // context lengths beyond max_ctx (which sizes the split plan) or beyond
+    // what the page table covers are clamped to them
+    const int ctx = min(min(ctx_raw, a.max_ctx), a.max_pages * a.page);
     if (ctx <= 0) return;
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int T = lo_b / kTile + s;
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     uint32_t o_first[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) o_first[u] = *(const uint32_t*)(base + min(u, na - 1) * sstride + 4 * lane);
-    const int ctx = min(ctx_raw, a.max_pages * a.page);
+    const int ctx = min(min(ctx_raw, a.max_ctx), a.max_pages * a.page);   // as in k_paged_decode
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
     // Splits are taken kMergeBatch at a time with every load of a batch in

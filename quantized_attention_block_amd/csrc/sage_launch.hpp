@@ -108,6 +108,10 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_debug_qk(const int8_t* q, const int8_t* k, int B, int H, int Lqp, int Lkp,
                            int D, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t stream);
+// MXFP4 codes [B,H,Lqp,64] / [B,H,Lkp,64] with E8M0 scales [.., 4]; D = 128
+hipError_t launch_debug_qk_mx(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                              const uint8_t* k_scale, int B, int H, int Lqp, int Lkp, int q0, int nq,
+                              int k0, int nk, float* out, hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;            // bf16
@@ -123,6 +127,7 @@ struct DecodeArgs {
     int64_t o_sB, o_sM, o_sH;
     int B, MTP, Hq, Hkv, D, page, num_pages, max_pages;
     int window, v_transposed, num_splits;
+    int max_ctx;              // context lengths are clamped to it (it sizes the split plan)
     int mx;                   // 1: MXFP4 cache (E2M1 codes, E8M0 scales) as documented in sage.h
     int scale_per_tensor;     // e4m3 cache: k_scale / v_scale hold one value each
     float sm_scale;

@@ -106,12 +106,14 @@ def lib():
         L.sage_hadamard_destroy.argtypes = [_P]
         L.sage_debug_qk_tile.argtypes = [_T, _T, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _T, _P]
+        L.sage_debug_qk_tile_mx.argtypes = [_T, _T, _T, _T, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, _T, _P]
         L.sage_set_quant_wait_us.argtypes = [ctypes.c_int32]
         for name in ("sage_quantize_qk_workspace_size", "sage_quantize_qk",
                      "sage_quantize_v_workspace_size", "sage_quantize_v", "sage_attn_fwd",
                      "sage_paged_decode_workspace_size", "sage_paged_decode",
                      "sage_hadamard_create", "sage_hadamard_destroy", "sage_debug_qk_tile",
-                     "sage_set_quant_wait_us"):
+                     "sage_debug_qk_tile_mx", "sage_set_quant_wait_us"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -387,6 +389,18 @@ def sage_debug_qk_tile(q_q: torch.Tensor, k_q: torch.Tensor, q0: int, nq: int, k
     out = torch.empty((B, H, nq, nk), dtype=torch.int32, device=q_q.device)
     _check(lib().sage_debug_qk_tile(ctypes.byref(desc(q_q)), ctypes.byref(desc(k_q)), q0, nq, k0,
                                     nk, ctypes.byref(desc(out)), _stream(q_q.device)))
+    return out
+
+
+def sage_debug_qk_tile_mx(qk: QuantizedQK, q0: int, nq: int, k0: int, nk: int) -> torch.Tensor:
+    """fp32 MXFP4 score tile of the attention kernel's QK step (test hook)."""
+    B, H = qk.q.shape[:2]
+    out = torch.empty((B, H, nq, nk), dtype=torch.float32, device=qk.q.device)
+    _check(lib().sage_debug_qk_tile_mx(ctypes.byref(desc(qk.q, FP4X2_E2M1)),
+                                       ctypes.byref(desc(qk.q_scale, E8M0)),
+                                       ctypes.byref(desc(qk.k, FP4X2_E2M1)),
+                                       ctypes.byref(desc(qk.k_scale, E8M0)), q0, nq, k0, nk,
+                                       ctypes.byref(desc(out)), _stream(qk.q.device)))
     return out
 
 

@@ -103,6 +103,47 @@ def test_qk_tiles_full_size_sampled(dev, orc):
         assert np.array_equal(S.astype(np.int64), ref), (q0, k0)
 
 
+def _ulp32(x):
+    return np.spacing(np.abs(x).astype(np.float32)).astype(np.float64)
+
+
+@pytest.mark.parametrize("kw,full", [(dict(Lq=1000, Lk=1000, H=2), True),
+                                     (dict(Lq=520, Lk=333, H=1), True),
+                                     (dict(), False)])          # full video-DiT length, sampled
+def test_mxfp4_qk_tiles_within_one_ulp(dev, orc, kw, full):
+    """fp32 MXFP4 score tiles of the attention kernel's QK step against the
+    exact block-scaled integer sum (float64): within one fp32 ulp of the
+    larger of the exact value and the first instruction's two-block partial
+    sum (the MFMA rounds its fp32 accumulator once per instruction), and
+    exact wherever the sums are representable."""
+    w = wl.WORKLOADS["video_dit_mxfp4"]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    had = sage.Hadamard(0)
+    say("mxfp4 qk tiles", kw)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4, hadamard=had)
+    torch.cuda.synchronize()
+    q4, qe = orc.unpack_fp4(qk.q.cpu().numpy()), qk.q_scale.cpu().numpy()
+    k4, ke = orc.unpack_fp4(qk.k.cpu().numpy()), qk.k_scale.cpu().numpy()
+    Lqp, Lkp = q4.shape[2], k4.shape[2]
+    if full:
+        picks = [(0, Lqp, 0, Lkp)]
+    else:
+        rng = np.random.default_rng(77)
+        picks = [(int(rng.integers(0, Lqp // 32)) * 32, 32, int(rng.integers(0, Lkp // 128)) * 128, 128)
+                 for _ in range(16)] + [(Lqp - 32, 32, Lkp - 128, 128)]
+    n_exact = n_all = 0
+    for q0, nq, k0, nk in picks:
+        S = sage.sage_debug_qk_tile_mx(qk, q0, nq, k0, nk).cpu().numpy().astype(np.float64)
+        a = (q4[:, :, q0:q0 + nq], qe[:, :, q0:q0 + nq], k4[:, :, k0:k0 + nk], ke[:, :, k0:k0 + nk])
+        ex = orc.qk_mxfp4_tile(*a)
+        p01 = orc.qk_mxfp4_tile(*a, partial_blocks=2)
+        err = np.abs(S - ex)
+        assert np.all(err <= _ulp32(np.maximum(np.abs(ex), np.abs(p01)))), (q0, k0, float(err.max()))
+        n_exact += int((err == 0).sum())
+        n_all += err.size
+    print(f"mxfp4 score tiles: {n_exact} of {n_all} exact")
+
+
 # ---- outputs, reduced sizes (every row) ---------------------------------------------
 @pytest.mark.parametrize("name,kw,causal", [
     ("tiny", dict(), False),
@@ -148,6 +189,26 @@ def test_gqa(dev, orc):
     _check(canon(out), ref, orc.attn_exact(q, kr, vr, True, w.sm_scale))
 
 
+def _mx_given_gpu_codes(orc, qk, v, w, causal, rows=None, sl=None):
+    """The oracle's attention stage fed the GPU's own E2M1 codes and E8M0
+    scales (so the last-bit differences of the rotation's fp32 sums, which
+    move a few codes, are taken out of the comparison), with V quantized by
+    the oracle.  sl: (b, h) to restrict the codes to one head; rows then
+    index that head."""
+    q4, qe, k4, ke = (t.cpu().numpy() for t in (qk.q, qk.q_scale, qk.k, qk.k_scale))
+    if sl is not None:
+        b, h = sl
+        q4, qe, k4, ke = (x[b:b + 1, h:h + 1] for x in (q4, qe, k4, ke))
+    Lq, Lk = qk.Lq, qk.Lk
+    q4, k4 = orc.unpack_fp4(q4)[:, :, :Lq], orc.unpack_fp4(k4)[:, :, :Lk]
+    qe, ke = qe[:, :, :Lq], ke[:, :, :Lk]
+    v8, vs = orc.quant_v_fp8(v)
+    B, H, _, D = q4.shape
+    return orc.attn_emulated(B=B, H=H, Lq=Lq, Lk=Lk, D=D, causal=causal, sm_scale=w.sm_scale, BN=BN,
+                             qk_mode=orc.QK_MXFP4, rows=rows, q4=q4, q_e8=qe, k4=k4, k_e8=ke, v8=v8,
+                             v_scale=vs)
+
+
 def test_mxfp4_attention_matches_oracle(dev, orc):
     w = wl.WORKLOADS["video_dit_mxfp4"]
     inp = wl.make_prefill(w, device=dev, Lq=1000, Lk=1000, H=2)
@@ -161,12 +222,13 @@ def test_mxfp4_attention_matches_oracle(dev, orc):
     _check(canon(out), ref)
     say("mxfp4 attention (hadamard)")
     out, qk = _gpu_out(inp, False, w.sm_scale, mode=sage.QK_MXFP4, hadamard=had)
-    ref, _ = orc.prefill_mxfp4_pipeline(q, k, v, causal=False, sm_scale=w.sm_scale, BN=BN, mu=mu)
-    c = cosine(canon(out), ref)
-    assert c >= COS_EMUL, c
     exact = orc.attn_exact(q, k, v, False, w.sm_scale)
-    print("mxfp4 (hadamard) cosine vs exact: gpu", cosine(canon(out), exact), "oracle",
-          cosine(ref, exact))
+    # element-wise against the oracle's attention stage given the GPU's codes
+    given = _mx_given_gpu_codes(orc, qk, v, w, False)
+    ref, _ = orc.prefill_mxfp4_pipeline(q, k, v, causal=False, sm_scale=w.sm_scale, BN=BN, mu=mu)
+    _check(canon(out), given, exact, orc_exact=cosine(ref, exact))
+    # and the whole oracle pipeline (its own rotation and codes): cosine
+    assert cosine(canon(out), ref) >= COS_EMUL
 
 
 # ---- full sizes, sampled rows ---------------------------------------------------------
@@ -215,15 +277,28 @@ def test_video_dit_full_size_sampled(dev, orc):
 
 
 def test_video_dit_mxfp4_full_size_sampled(dev, orc):
+    """Full size: 3 heads x 48 sampled rows element-wise against the oracle's
+    attention stage given the GPU's MXFP4 codes, and by cosine against the
+    whole oracle pipeline (its own rotation) and exact attention."""
     w = wl.WORKLOADS["video_dit_mxfp4"]
     inp = wl.make_prefill(w, device=dev)
     had = sage.Hadamard(0)
     say("video dit mxfp4 full size")
-    g, r, e = _sampled_full(orc, inp, w, False, [(0, 5)], 12, mode=sage.QK_MXFP4, hadamard=had)
-    # rotation sums differ from the oracle's in the last bit (fp32 MFMA
-    # accumulation), which moves a few E2M1 codes: cosine only
+    heads = [(0, 5), (0, 21), (0, 39)]
+    g, r, e = _sampled_full(orc, inp, w, False, heads, 48, mode=sage.QK_MXFP4, hadamard=had, seed=3)
+    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4, hadamard=had)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    given = []
+    for (b, h) in heads:
+        v = inp.v[b:b + 1, :, h:h + 1].float().cpu().permute(0, 2, 1, 3).contiguous().numpy()
+        L = v.shape[2]
+        rows_i = np.unique(np.concatenate([rng.integers(0, L, 48), [0, L - 1]]))
+        rows = np.stack([np.zeros_like(rows_i), np.zeros_like(rows_i), rows_i], 1)
+        given.append(_mx_given_gpu_codes(orc, qk, v, w, False, rows=rows, sl=(b, h)))
+    given = np.concatenate(given)
+    _check(g, given, e, bf16=True, orc_exact=cosine(r, e))
     assert cosine(g, r) >= COS_EMUL
-    print("mxfp4 full-size cosine vs exact: gpu", cosine(g, e), "oracle", cosine(r, e))
 
 
 # ---- layouts, output strides, determinism ------------------------------------------
@@ -253,18 +328,19 @@ def test_layouts_give_identical_results(dev):
     assert torch.equal(o32.half(), o16)
 
 
-def test_single_token_and_tiny_lengths(dev, orc):
-    """Edge cases: one key, one query, lengths 1 / 63 / 129 (one partial tile)."""
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 127, 128, 129, 192, 255, 256, 257])
+def test_boundary_lengths(dev, orc, L):
+    """One query or key, and lengths on either side of the 64-key tile and
+    the 128-query block: one to five KV tiles, full and ragged."""
     w = wl.WORKLOADS["llm_prefill"]
-    for L in (1, 63, 129):
-        inp = wl.make_prefill(w, device=dev, Lq=L, Lk=L, B=1, H=2)
-        say("tiny length", L)
-        for causal in (False, True):
-            out, qk = _gpu_out(inp, causal, w.sm_scale)
-            q, k, v = canon(inp.q), canon(inp.k), canon(inp.v)
-            ref, _ = orc.prefill_int8_pipeline(q, k, v, causal=causal, sm_scale=w.sm_scale, BN=BN,
-                                               mu=qk.k_mean.cpu().numpy())
-            _check(canon(out), ref)
+    inp = wl.make_prefill(w, device=dev, Lq=L, Lk=L, B=1, H=2)
+    for causal in (False, True):
+        say("boundary length", L, "causal" if causal else "non-causal")
+        out, qk = _gpu_out(inp, causal, w.sm_scale)
+        q, k, v = canon(inp.q), canon(inp.k), canon(inp.v)
+        ref, _ = orc.prefill_int8_pipeline(q, k, v, causal=causal, sm_scale=w.sm_scale, BN=BN,
+                                           mu=qk.k_mean.cpu().numpy())
+        _check(canon(out), ref, orc.attn_exact(q, k, v, causal, w.sm_scale) if L > 1 else None)
 
 
 @pytest.mark.parametrize("name,Lq,D,causal,dtype", [

@@ -147,3 +147,36 @@ def test_paged_decode_head_dim_64(dev, orc, mtp, hq, hkv, page, window):
     g = _run(inp, dev, w.window, w.ctx, sm)
     assert g.shape[-1] == 64
     _check(g, _oracle(orc, inp, w.window, sm), _oracle(orc, inp, w.window, sm, False))
+
+
+@pytest.mark.parametrize("window,ctx,mtp", [(0, 12000, 4), (8192, 12000, 4), (0, 8500, 1)])
+def test_paged_decode_more_than_32_splits(dev, orc, window, ctx, mtp):
+    """More splits than one merge batch (32): no window over 12000 tokens (47
+    splits), the aiter page's window 8192 with MTP 4 (34 splits), and 8500
+    tokens without a window (34 splits, one past the batch); the merge then
+    carries a running maximum across batches of splits."""
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("v", 9, 2, mtp, 16, 1, 128, 128, ctx, window)
+    inp = wl.make_decode(w)
+    inp.ctx_lens[1] = ctx - 1000
+    assert sage.sage_decode_num_splits(window, mtp, ctx) > 32
+    say("paged decode > 32 splits", window, ctx, mtp)
+    g = _run(inp, dev, window, ctx, base.sm_scale)
+    _check(g, _oracle(orc, inp, window, base.sm_scale), _oracle(orc, inp, window, base.sm_scale, False))
+
+
+def test_paged_decode_context_above_max_ctx(dev, orc):
+    """A context length above params.max_ctx (the page table still covering
+    it) is treated as max_ctx: the output is finite and equals the oracle's at
+    the clamped length."""
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("v", 9, 3, 4, 16, 1, 128, 128, 2048, 0)
+    inp = wl.make_decode(w)
+    max_ctx = 1000
+    inp.ctx_lens[:] = torch.tensor([1000, 1900, 600], dtype=torch.int32)
+    say("paged decode, ctx above max_ctx", inp.ctx_lens.tolist(), max_ctx)
+    g = _run(inp, dev, 0, max_ctx, base.sm_scale)
+    assert np.isfinite(g).all()
+    clamped = wl.DecodeInputs(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale, inp.page_table,
+                              torch.clamp(inp.ctx_lens, max=max_ctx))
+    _check(g, _oracle(orc, clamped, 0, base.sm_scale), _oracle(orc, clamped, 0, base.sm_scale, False))

@@ -123,3 +123,16 @@ def test_mx_decode_equals_base2_attention(dev, window):
     ref = base2_decode(q, kf, vf, ones, ones, table, ctx, window, Hkv)
     fp16_rows = 2.0 ** -12 * np.abs(vf).max()
     assert np.all(np.abs(g - ref) <= _half_ulp_bf16(ref) + fp16_rows + 1e-4 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("window,ctx", [(0, 12000), (8192, 12000)])
+def test_mx_decode_more_than_32_splits(dev, orc, window, ctx):
+    """47 and 34 splits per sequence: more than one merge batch of 32."""
+    base = wl.WORKLOADS["paged_decode"]
+    w = wl.DecodeWorkload("mx_long", 77, 2, 4, 16, 1, 128, 128, ctx, window)
+    inp = wl.make_decode_mx(w)
+    inp.ctx_lens[1] = ctx - 1000
+    assert sage.sage_decode_num_splits(window, 4, ctx) > 32
+    say("MXFP4 paged decode > 32 splits", f"window {window} ctx {ctx}")
+    g = _run(inp, dev, window, ctx, base.sm_scale)
+    _check(g, _oracle(orc, inp, window, base.sm_scale), _exact(orc, inp, window, base.sm_scale))
