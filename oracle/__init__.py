@@ -70,7 +70,8 @@ class DecodeParams(ctypes.Structure):
                 ("Hkv", ctypes.c_int), ("D", ctypes.c_int), ("page_size", ctypes.c_int),
                 ("max_pages", ctypes.c_int), ("num_pages", ctypes.c_int), ("window", ctypes.c_int),
                 ("tile", ctypes.c_int), ("sm_scale", ctypes.c_double), ("quant", ctypes.c_int),
-                ("nthreads", ctypes.c_int)]
+                ("nthreads", ctypes.c_int), ("q8", ctypes.c_void_p), ("q8_scale", ctypes.c_void_p),
+                ("q8_scale_per_tensor", ctypes.c_int)]
 
 
 def _declare(L):
@@ -323,10 +324,23 @@ def decode_num_splits(window: int, mtp: int, tile: int = 256) -> int:
     return int(lib().orc_decode_num_splits(window, mtp, tile))
 
 
+def _q8_fields(prm, q8, q8_scale, keep):
+    """Fills the pre-quantized query fields: q8 uint8 codes shaped like q,
+    q8_scale float32 [B, MTP, Hq] (per row) or [1] (per tensor)."""
+    if q8 is None:
+        return
+    c, s = _c(q8, np.uint8), _c(q8_scale, np.float32)
+    keep += [c, s]
+    prm.q8, prm.q8_scale = c.ctypes.data, s.ctypes.data
+    prm.q8_scale_per_tensor = int(s.size == 1)
+
+
 def paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *, window,
-                 sm_scale, tile=256, quant=True, nthreads=0) -> np.ndarray:
+                 sm_scale, tile=256, quant=True, nthreads=0, q8=None, q8_scale=None) -> np.ndarray:
     """q: [B, MTP, Hq, D] float32; caches [P, Hkv, page, D] (uint8 codes when
-    quant, else float32); scales [P, Hkv, page]; page_table [B, max_pages]."""
+    quant, else float32); scales [P, Hkv, page]; page_table [B, max_pages].
+    q8 / q8_scale: the query given in e4m3 (codes shaped like q, fp32 scales
+    [B, MTP, Hq] or [1]); q is then only read for its shape."""
     q = _c(q, np.float32)
     B, MTP, Hq, D = q.shape
     P, Hkv, PS, _ = k_cache.shape
@@ -336,6 +350,8 @@ def paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *,
     pt, cl = _c(page_table, np.int32), _c(ctx_lens, np.int32)
     prm = DecodeParams(B, MTP, Hq, Hkv, D, PS, pt.shape[1], P, window, tile, float(sm_scale),
                        int(quant), nthreads)
+    keep = []
+    _q8_fields(prm, q8, q8_scale, keep)
     out = np.empty((B, MTP, Hq, D), dtype=np.float32)
     rc = lib().orc_paged_decode(ctypes.byref(prm), _ptr(q), _ptr(kc), _ptr(vc), _ptr(ks),
                                 _ptr(vs), _ptr(pt), _ptr(cl), _ptr(out))
@@ -345,7 +361,7 @@ def paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *,
 
 
 def paged_decode_mx(q, k_codes, k_e8, v_codes, v_e8, page_table, ctx_lens, *, window, sm_scale,
-                    tile=256, nthreads=0) -> np.ndarray:
+                    tile=256, nthreads=0, q8=None, q8_scale=None) -> np.ndarray:
     """MXFP4 KV cache, one E2M1 code per byte: k_codes [P, Hkv, page, D],
     k_e8 [P, Hkv, page, D/32]; V transposed: v_codes [P, Hkv, D, page],
     v_e8 [P, Hkv, D, page/32]; q [B, MTP, Hq, D] float32."""
@@ -356,6 +372,8 @@ def paged_decode_mx(q, k_codes, k_e8, v_codes, v_e8, page_table, ctx_lens, *, wi
     pt, cl = _c(page_table, np.int32), _c(ctx_lens, np.int32)
     prm = DecodeParams(B, MTP, Hq, Hkv, D, PS, pt.shape[1], P, window, tile, float(sm_scale), 1,
                        nthreads)
+    keep = []
+    _q8_fields(prm, q8, q8_scale, keep)
     out = np.empty((B, MTP, Hq, D), dtype=np.float32)
     rc = lib().orc_paged_decode_mx(ctypes.byref(prm), _ptr(q), _ptr(kc), _ptr(ke), _ptr(vc), _ptr(ve),
                                    _ptr(pt), _ptr(cl), _ptr(out))

@@ -603,9 +603,9 @@ int orc_attn_exact(const float* q, const float* k, const float* v,
 // tile the sequence's window union touches (one task per window tile, as the
 // "Batch-first plan grid removal" section describes the plan).
 // Per split and query row:
-//   quant: Q row -> e4m3 with a dynamic scale (READING: per (token, head) row,
-//          q_scale = fp32(amax / 448), codes e4m3(fp32(q * fp32(448 / amax)));
-//          the page says Q is quantized to the cache's FP8 format);
+//   quant: Q row -> e4m3 with a dynamic scale (quant_query_row), or the
+//          e4m3 query as given (p->q8: codes and a per-row or per-tensor
+//          scale; the page lists e4m3 queries beside bf16 ones);
 //          x = fp32(fp32(fp32(dot * q_scale) * k_scale[t]) * alpha) where dot
 //          is the exact e4m3 dot product rounded once;
 //   float: x = fp32(sum_d q * k_cache * k_scale[t] in binary64 * sm_scale *
@@ -627,6 +627,27 @@ int orc_attn_exact(const float* q, const float* k, const float* v,
 // over each query's window with the per-token V scale applied, computed
 // independently in float64 (a wrong window bound, fold, score scale, merge
 // weight or query position each break it).
+
+namespace {
+// The e4m3 query row r: given codes and scale (p->q8), or the float row
+// quantized with a dynamic scale (READING: per (token, head) row, scale =
+// fp32(amax / 448), codes e4m3(fp32(q * fp32(448 / amax))); the page says Q
+// is quantized to the cache's FP8 format).
+void quant_query_row(const orc_decode_params* p, const float* qr, int64_t r, uint8_t* q8, float* q_s) {
+    const int D = p->D;
+    if (p->q8) {
+        for (int d = 0; d < D; ++d) q8[d] = p->q8[r * D + d];
+        *q_s = p->q8_scale[p->q8_scale_per_tensor ? 0 : r];
+        return;
+    }
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) amax = std::max(amax, std::fabs(qr[d]));
+    float inv = 0.0f;
+    *q_s = 0.0f;
+    if (amax > 0.0f) { inv = 448.0f / amax; *q_s = amax / 448.0f; }
+    for (int d = 0; d < D; ++d) q8[d] = orc_e4m3_encode(qr[d] * inv);
+}
+}  // namespace
 
 int orc_decode_num_splits(int window, int mtp, int tile) {
     // Largest number of tile-aligned windows that W + MTP - 1 consecutive keys
@@ -668,13 +689,7 @@ int orc_paged_decode(const orc_decode_params* p, const float* q,
 
         std::vector<uint8_t> q8(D);
         float q_s = 0.0f;
-        if (p->quant) {
-            float amax = 0.0f;
-            for (int d = 0; d < D; ++d) amax = std::max(amax, std::fabs(qr[d]));
-            float inv = 0.0f;
-            if (amax > 0.0f) { inv = 448.0f / amax; q_s = amax / 448.0f; }
-            for (int d = 0; d < D; ++d) q8[d] = orc_e4m3_encode(qr[d] * inv);
-        }
+        if (p->quant) quant_query_row(p, qr, r, q8.data(), &q_s);
 
         std::vector<float> ms, ls;
         std::vector<std::vector<float>> Os;
@@ -807,13 +822,7 @@ int orc_paged_decode_mx(const orc_decode_params* p, const float* q,
 
         std::vector<uint8_t> q8(D);
         float q_s = 0.0f;
-        {
-            float amax = 0.0f;
-            for (int d = 0; d < D; ++d) amax = std::max(amax, std::fabs(qr[d]));
-            float inv = 0.0f;
-            if (amax > 0.0f) { inv = 448.0f / amax; q_s = amax / 448.0f; }
-            for (int d = 0; d < D; ++d) q8[d] = orc_e4m3_encode(qr[d] * inv);
-        }
+        quant_query_row(p, qr, r, q8.data(), &q_s);
 
         std::vector<float> ms, ls;
         std::vector<std::vector<float>> Os;

@@ -100,6 +100,12 @@ typedef struct {
     double sm_scale;
     int quant;         /* 1: e4m3 caches + per-row e4m3 query + e4m3 P; 0: float */
     int nthreads;
+    /* Optional query given already in e4m3 (quant modes only): codes
+     * [B, MTP, Hq, D] and fp32 scales, one per (token, head) row or (per
+     * tensor) one for all; NULL: the float q is quantized per row. */
+    const uint8_t* q8;
+    const float* q8_scale;
+    int q8_scale_per_tensor;
 } orc_decode_params;
 
 int orc_decode_num_splits(int window, int mtp, int tile);

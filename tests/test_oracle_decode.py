@@ -169,3 +169,47 @@ def test_mx_decode_equals_fp8_decode_on_shared_values(orc, D, PS, window, tile):
     b = orc.paged_decode(q, k8, v8, ones, ones, table, ctx, **common)
     assert np.array_equal(a, b)
     assert np.abs(a).max() > 0
+
+
+@pytest.mark.parametrize("per_tensor", [True, False])
+def test_e4m3_query_exact_on_dyadic_inputs(orc, per_tensor):
+    """The query given already in e4m3 (codes + fp32 scale per tensor or per
+    (token, head) row) instead of bf16: on the exact inputs of
+    test_quant_mode_exact_on_dyadic_inputs, with codes q / s for power-of-two
+    scales s (every code exact), the result is base-2 attention again; a
+    dropped or misplaced query scale moves every score by a power of two."""
+    MTP, Hq, Hkv = 4, 4, 2
+    ctx = np.array([100, 57], np.int32)
+    q, kf, vf, ks, vs, table = dyadic_decode(91, B=2, MTP=MTP, Hq=Hq, Hkv=Hkv, D=32, PS=16, max_pages=8)
+    kc, vc = orc.e4m3_encode_array(kf), orc.e4m3_encode_array(vf)
+    rng = np.random.default_rng(3)
+    s = np.full((1,), 4.0, np.float32) if per_tensor else \
+        rng.choice(np.array([1.0, 2.0, 4.0], np.float32), q.shape[:3])
+    qs = (q / (s if per_tensor else s[..., None])).astype(np.float32)
+    q8 = orc.e4m3_encode_array(qs)
+    assert np.array_equal(orc.e4m3_decode_array(q8), qs)
+    junk = np.full_like(q, 123.0)            # only the codes and scales are read
+    out = orc.paged_decode(junk, kc, vc, ks, vs, table, ctx, window=20, sm_scale=np.log(2.0) / 2,
+                           tile=32, q8=q8, q8_scale=s)
+    ref = base2_decode(q, kf, vf, ks, vs, table, ctx, 20, Hkv)
+    assert np.abs(out - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_mx_decode_e4m3_query_equals_fp8_decode(orc):
+    """The given-e4m3-query path of the MXFP4 decode agrees bit for bit with
+    the FP8 decode's on an MXFP4 cache's exact e4m3 twin (as above)."""
+    B, MTP, Hq, Hkv, max_pages, D, PS = 2, 2, 8, 1, 4, 128, 64
+    P = B * max_pages
+    rng = np.random.default_rng(17)
+    kc, ke, vc, ve, kf, vf = _mx_cache(9, P, Hkv, PS, D)
+    k8, v8 = orc.e4m3_encode_array(kf), orc.e4m3_encode_array(vf)
+    q8 = orc.e4m3_encode_array(rng.standard_normal((B, MTP, Hq, D)).astype(np.float32) * 30)
+    qs = rng.uniform(0.01, 0.1, (B, MTP, Hq)).astype(np.float32)
+    table = rng.permutation(P).astype(np.int32).reshape(B, max_pages)
+    ctx = np.array([max_pages * PS - 9, 2 * PS + 1], np.int32)
+    ones = np.ones((P, Hkv, PS), np.float32)
+    q = np.zeros((B, MTP, Hq, D), np.float32)
+    common = dict(window=0, sm_scale=D ** -0.5, q8=q8, q8_scale=qs)
+    a = orc.paged_decode_mx(q, kc, ke, vc, ve, table, ctx, **common)
+    b = orc.paged_decode(q, k8, v8, ones, ones, table, ctx, **common)
+    assert np.array_equal(a, b) and np.abs(a).max() > 0
