@@ -260,6 +260,27 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache,
                               const sage_tensor* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* sage_paged_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and kernels, with the split partials kept in a fixed device
+ * scratch array of SAGE_DECODE_SCRATCH_BYTES per device instead of a
+ * workspace.  The caller still owns q, the caches, scales, page table,
+ * lengths and out.  The call allocates nothing (no hipMalloc or allocating
+ * library routine); its first call on a device looks the array's address up
+ * once (hipGetSymbolAddress).  A decode whose partials need more than
+ * SAGE_DECODE_SCRATCH_BYTES (sage_paged_decode_workspace_size) is refused
+ * with SAGE_ERR_WORKSPACE before anything is enqueued.  Every call on a
+ * device shares that device's scratch, which keeps the last call's contents
+ * (nothing in it needs clearing between calls): calls that overlap in time
+ * on one device -- on different streams or threads -- race and give wrong
+ * results; calls enqueued on one stream are ordered and safe. */
+#define SAGE_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+sage_status sage_paged_decode_noalloc(const sage_tensor* q, const sage_tensor* k_cache,
+                                      const sage_tensor* v_cache, const sage_tensor* k_scale,
+                                      const sage_tensor* v_scale, const sage_tensor* page_table,
+                                      const sage_tensor* ctx_lens, const sage_decode_params* params,
+                                      const sage_tensor* out, void* stream);
+
 /* Number of splits per sequence the plan uses for a window:
  * (window + mtp - 1 - 1 + 255) / 256 + 1 when window > 0, else
  * ceil(max_ctx / 256) ([aiter #7388] window tiles). */

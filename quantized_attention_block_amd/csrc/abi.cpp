@@ -15,6 +15,8 @@
 #include "../../include/sage.h"
 #include "sage_launch.hpp"
 
+static_assert(SAGE_DECODE_SCRATCH_BYTES == sage::kDecodeScratchBytes, "scratch size in sage.h");
+
 struct sage_hadamard {
     int32_t R;
     int32_t device;
@@ -514,11 +516,14 @@ sage_status sage_paged_decode_workspace_size(const sage_tensor* q, const sage_te
     return ok();
 }
 
-sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, const sage_tensor* v_cache,
-                              const sage_tensor* k_scale, const sage_tensor* v_scale,
-                              const sage_tensor* page_table, const sage_tensor* ctx_lens,
-                              const sage_decode_params* p, const sage_tensor* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+namespace {
+// Validation and kernel arguments shared by the two decode entry points
+// (everything but the partials' memory); *need = bytes of partials.
+sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const sage_tensor* v_cache,
+                         const sage_tensor* k_scale, const sage_tensor* v_scale,
+                         const sage_tensor* page_table, const sage_tensor* ctx_lens,
+                         const sage_decode_params* p, const sage_tensor* out, sage::DecodeArgs* out_args,
+                         size_t* need) {
     DecShape s;
     sage_status st = decode_query(q, page_table, p, &s);
     if (st) return st;
@@ -572,15 +577,9 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     for (int i = 0; i < 3; ++i)
         if (out->shape[i] > 1 && (out->stride[i] * 2) % 16)
             return fail(SAGE_ERR_ALIGNMENT, "out: stride of dim %d is not a multiple of 16 bytes", i);
-    const size_t need = decode_ws(s, Hkv);
-    if (!workspace || workspace_bytes < need)
-        return fail(SAGE_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(SAGE_ERR_ALIGNMENT, "workspace not 16-byte aligned");
     if (!std::isfinite(p->sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale is not finite");
-    if ((st = check_device())) return st;
-
-    sage::DecodeArgs a;
+    *need = decode_ws(s, Hkv);
+    sage::DecodeArgs& a = *out_args;
     a.q = q->data;
     a.q_sB = q->stride[0];
     a.q_sM = q->stride[1];
@@ -611,8 +610,48 @@ sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, 
     a.mx = mx ? 1 : 0;
     a.scale_per_tensor = per_tensor ? 1 : 0;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)s.D));
+    a.partials = nullptr;
+    return SAGE_OK;
+}
+}  // namespace
+
+sage_status sage_paged_decode(const sage_tensor* q, const sage_tensor* k_cache, const sage_tensor* v_cache,
+                              const sage_tensor* k_scale, const sage_tensor* v_scale,
+                              const sage_tensor* page_table, const sage_tensor* ctx_lens,
+                              const sage_decode_params* p, const sage_tensor* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    sage::DecodeArgs a;
+    size_t need = 0;
+    sage_status st = decode_setup(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, p, out, &a, &need);
+    if (st) return st;
+    if (!workspace || workspace_bytes < need)
+        return fail(SAGE_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(SAGE_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+    if ((st = check_device())) return st;
     a.partials = (float*)workspace;
     return launch_status(sage::launch_paged_decode(a, (hipStream_t)stream), "paged decode");
+}
+
+sage_status sage_paged_decode_noalloc(const sage_tensor* q, const sage_tensor* k_cache,
+                                      const sage_tensor* v_cache, const sage_tensor* k_scale,
+                                      const sage_tensor* v_scale, const sage_tensor* page_table,
+                                      const sage_tensor* ctx_lens, const sage_decode_params* p,
+                                      const sage_tensor* out, void* stream) {
+    sage::DecodeArgs a;
+    size_t need = 0;
+    sage_status st = decode_setup(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, p, out, &a, &need);
+    if (st) return st;
+    if (need > sage::kDecodeScratchBytes)
+        return fail(SAGE_ERR_WORKSPACE,
+                    "decode needs %zu bytes of partials, above the fixed scratch of %zu bytes "
+                    "(use sage_paged_decode with a workspace)", need, sage::kDecodeScratchBytes);
+    if ((st = check_device())) return st;
+    void* scratch = nullptr;
+    hipError_t e = sage::decode_scratch(&scratch);
+    if (e != hipSuccess) return launch_status(e, "decode scratch lookup");
+    a.partials = (float*)scratch;
+    return launch_status(sage::launch_paged_decode(a, (hipStream_t)stream), "paged decode (no allocation)");
 }
 
 // ---- Hadamard handle ------------------------------------------------------------

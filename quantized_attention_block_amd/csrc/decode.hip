@@ -29,6 +29,7 @@
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace sage {
@@ -594,6 +595,33 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
 }
 
 }  // namespace
+
+// Scratch of the no-allocation decode entry point: the split partials, which
+// the allocating entry point keeps in the caller's workspace.  One copy per
+// device, held until the process ends; every call on a device shares it.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    // Device address of this device's copy of `scratch`, looked up once per
+    // device (with that device current) and kept; the array's name in host
+    // code is only a host-side stand-in and is never passed to a kernel.
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;

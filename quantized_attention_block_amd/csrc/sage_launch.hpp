@@ -135,6 +135,12 @@ struct DecodeArgs {
 };
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Fixed scratch of the no-allocation decode entry point (a file-scope device
+// array of this many bytes per device); decode_scratch returns the current
+// device's address of it.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_hadamard_build(int R, void* bf16_mat, void* f16_mat, hipStream_t stream);
 
 }  // namespace sage

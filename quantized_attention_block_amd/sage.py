@@ -28,6 +28,7 @@ STATUS_NAMES = ["SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_DTYPE", "SAGE_ERR_S
 # sage_dtype
 F16, BF16, F32, I8, I32, U8, FP8_E4M3FN, FP8_E4M3FNUZ, FP4X2_E2M1, E8M0 = range(1, 11)
 QK_INT8, QK_MXFP4 = 0, 1
+DECODE_SCRATCH_BYTES = 32 << 20   # SAGE_DECODE_SCRATCH_BYTES: scratch of sage_paged_decode_noalloc
 
 _TORCH_DTYPES = {
     torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, torch.int8: I8,
@@ -101,6 +102,8 @@ def lib():
                                                        ctypes.POINTER(ctypes.c_size_t)]
         L.sage_paged_decode.argtypes = [_T, _T, _T, _T, _T, _T, _T, ctypes.POINTER(DecodeParams),
                                         _T, _P, ctypes.c_size_t, _P]
+        L.sage_paged_decode_noalloc.argtypes = [_T, _T, _T, _T, _T, _T, _T,
+                                                ctypes.POINTER(DecodeParams), _T, _P]
         L.sage_hadamard_create.argtypes = [ctypes.c_int32, ctypes.c_int32, _P,
                                            ctypes.POINTER(ctypes.c_void_p)]
         L.sage_hadamard_destroy.argtypes = [_P]
@@ -112,6 +115,7 @@ def lib():
         for name in ("sage_quantize_qk_workspace_size", "sage_quantize_qk",
                      "sage_quantize_v_workspace_size", "sage_quantize_v", "sage_attn_fwd",
                      "sage_paged_decode_workspace_size", "sage_paged_decode",
+                     "sage_paged_decode_noalloc",
                      "sage_hadamard_create", "sage_hadamard_destroy", "sage_debug_qk_tile",
                      "sage_debug_qk_tile_mx", "sage_set_quant_wait_us"):
             getattr(L, name).restype = st
@@ -371,6 +375,21 @@ def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_len
                                    ctypes.byref(desc(ctx_lens)), ctypes.byref(prm),
                                    ctypes.byref(desc(out)), ctypes.c_void_p(workspace.data_ptr()),
                                    workspace.numel(), _stream(q.device)))
+    return out
+
+
+def sage_paged_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, out, *,
+                              max_ctx: int, window: int = 0, sm_scale: float = 0.0,
+                              v_transposed: bool = True) -> torch.Tensor:
+    """sage_paged_decode without a workspace: the library's fixed per-device
+    scratch holds the split partials (calls that overlap on one device race).
+    `out` is required; nothing is allocated."""
+    prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx))
+    _check(lib().sage_paged_decode_noalloc(ctypes.byref(desc(q)), ctypes.byref(desc(k_cache)),
+                                           ctypes.byref(desc(v_cache)), ctypes.byref(desc(k_scale)),
+                                           ctypes.byref(desc(v_scale)), ctypes.byref(desc(page_table)),
+                                           ctypes.byref(desc(ctx_lens)), ctypes.byref(prm),
+                                           ctypes.byref(desc(out)), _stream(q.device)))
     return out
 
 

@@ -285,3 +285,22 @@ def test_fused_q_refusals(S):
     assert attn(T(S.BF16, (B, L + 1, H, D))) == S.ERR_SHAPE
     assert attn(T(S.BF16, (B, L, H, D), stride=(L * H * D, 64, D, 1))) == S.ERR_LAYOUT   # rows overlap
     assert attn(T(S.BF16, (B, L, H, D)), qk_mode=S.QK_MXFP4) != S.OK         # MXFP4 keeps its q_scale
+
+
+def test_paged_decode_noalloc_refuses_above_its_scratch(S):
+    """The no-allocation decode refuses, before any HIP call, a decode whose
+    split partials need more than the fixed scratch (4096 sequences x 18
+    splits x 64 rows x 272 bytes > 32 MiB); a fitting one passes validation
+    up to the device check only on a GPU, so it is not called here."""
+    r = ctypes.byref
+    B, page = 4096, 128
+    q = T(S.BF16, (B, 4, 16, 128))
+    kc, vc = T(S.FP8_E4M3FN, (8, 1, page, 128)), T(S.FP8_E4M3FN, (8, 1, 128, page))
+    ksc, vsc = T(S.F32, (8, 1, page)), T(S.F32, (8, 1, page))
+    pt, cl = T(S.I32, (B, 64)), T(S.I32, (B,))
+    prm = S.DecodeParams(0.0, 4096, 1, 8192)
+    st = S.lib().sage_paged_decode_noalloc(r(q), r(kc), r(vc), r(ksc), r(vsc), r(pt), r(cl), r(prm),
+                                           r(T(S.BF16, (B, 4, 16, 128))), None)
+    assert st == S.ERR_WORKSPACE
+    assert b"scratch" in S.lib().sage_last_error()
+    assert S.DECODE_SCRATCH_BYTES == 32 << 20
