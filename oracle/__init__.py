@@ -16,7 +16,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+BUILT_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY selects another build of oracle.cpp (the sanitizer build)
+LIB_PATH = os.environ.get("ORACLE_LIBRARY") or BUILT_PATH
 SOURCES = [os.path.join(_HERE, "oracle.cpp")]
 
 QK_INT8, QK_MXFP4, QK_FLOAT = 0, 1, 2
@@ -25,14 +27,14 @@ QK_INT8, QK_MXFP4, QK_FLOAT = 0, 1, 2
 def build(force: bool = True) -> str:
     """Compiles liboracle.so with g++ (plain C++17, no fast-math, no FMA
     contraction)."""
-    if not force and os.path.exists(LIB_PATH):
-        return LIB_PATH
-    tmp = LIB_PATH + ".tmp"
+    if not force and os.path.exists(BUILT_PATH):
+        return BUILT_PATH
+    tmp = BUILT_PATH + ".tmp"
     cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", "-pthread", "-Wall", "-o", tmp] + SOURCES
     subprocess.run(cmd, check=True, cwd=_HERE)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, BUILT_PATH)
+    return BUILT_PATH
 
 
 _lib = None

@@ -45,16 +45,25 @@ def src_hash(names):
 
 
 def stats(db, out, command):
+    """One line per (kernel, launch grid): launches of one kernel on different
+    workloads differ in grid size, so their durations are kept apart."""
     con = sqlite3.connect(db)
-    rows = con.execute("select name, total_calls, total_duration, average, percentage "
-                       "from top_kernels order by total_duration desc").fetchall()
+    rows = con.execute(
+        "select name, grid_x, grid_y, grid_z, workgroup_x * workgroup_y * workgroup_z, "
+        "count(*), avg(duration), min(duration), sum(duration), max(vgpr_count), "
+        "max(accum_vgpr_count), max(sgpr_count), max(lds_size), max(scratch_size) "
+        "from kernels group by name, grid_x, grid_y, grid_z order by sum(duration) desc").fetchall()
+    total = sum(r[8] for r in rows) or 1
     with open(out, "w") as f:
-        f.write("# rocprofv3 --kernel-trace --stats summary\n")
+        f.write("# rocprofv3 --kernel-trace --stats summary, one line per kernel and launch grid\n")
         f.write(f"# command: {' '.join(command)}\n")
-        f.write("# durations in microseconds\n")
-        f.write(f"{'calls':>7} {'avg_us':>10} {'total_us':>12} {'pct':>6}  kernel\n")
-        for name, calls, total, avg, pct in rows:
-            f.write(f"{calls:>7} {avg:>10.2f} {total:>12.1f} {pct:>6.2f}  {name[:150]}\n")
+        f.write("# durations in microseconds; grid in work-items (x*y*z), block = work-items per workgroup;\n")
+        f.write("# vgpr/agpr/sgpr per lane or wave as allocated, lds and scratch in bytes per workgroup / lane\n")
+        f.write(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'total_us':>11} {'pct':>6} {'grid':>9} {'block':>5} "
+                f"{'vgpr':>4} {'agpr':>4} {'sgpr':>4} {'lds':>6} {'scr':>4}  kernel\n")
+        for (name, gx, gy, gz, wg, n, avg, mn, tot, vg, ag, sg, lds, scr) in rows:
+            f.write(f"{n:>6} {avg / 1e3:>10.2f} {mn / 1e3:>10.2f} {tot / 1e3:>11.1f} {100.0 * tot / total:>6.2f} "
+                    f"{gx * gy * gz:>9} {wg:>5} {vg:>4} {ag:>4} {sg:>4} {lds:>6} {scr:>4}  {name[:120]}\n")
 
 
 def _pmc(d, counter):

@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsage.so")
+# SAGE_LIBRARY selects another build of the same library (the host-only
+# sanitizer build of the C ABI, whose launchers always fail)
+LIB_PATH = os.environ.get("SAGE_LIBRARY") or os.path.join(_HERE, "libsage.so")
 
 # sage_status
 OK, ERR_INVALID_ARG, ERR_DTYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIGNMENT, ERR_WORKSPACE, \
