@@ -204,17 +204,20 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale,
 int32_t sage_attn_kv_tile(void);
 
 /* ------------------------------------------------------------------------- */
-/* Paged decode over an FP8 e4m3 KV cache ([aiter #7388]).
- *   q          BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides), query token m sits
- *              at position ctx_lens[b] - MTP + m
+/* Paged decode over an FP8 e4m3 KV cache ([aiter #7388]; its shape matrix
+ * covers D 64 / 128 / 256, bf16, fp16 and e4m3 queries, per-tensor and
+ * per-token scales, transposed and plain V).
+ *   q          BF16 or F16 [B, MTP, Hq, D], or FP8_E4M3FN with the scales
+ *              params.q_scale (any B/MTP/Hq strides, rows 16-byte aligned);
+ *              query token m sits at position ctx_lens[b] - MTP + m
  *   k_cache    FP8_E4M3FN [P, Hkv, page, D] contiguous
  *   v_cache    FP8_E4M3FN [P, Hkv, D, page] contiguous when v_transposed = 1,
- *              [P, Hkv, page, D] otherwise
+ *              [P, Hkv, page, D] ("plain") when v_transposed = 0
  *   k_scale, v_scale  F32 [P, Hkv, page] (per-token scales), or F32 [1] each
  *              (one scale per cache tensor)
  *   page_table I32 [B, max_pages]: page of token t is page_table[b][t / page]
  *   ctx_lens   I32 [B]
- *   out        BF16 [B, MTP, Hq, D] (any B/MTP/Hq strides)
+ *   out        BF16 or F16 [B, MTP, Hq, D] (any B/MTP/Hq strides)
  * With window W > 0 query position p sees keys [p - W + 1, p]; otherwise
  * [0, p].  The work is split into 256-token tiles aligned to absolute
  * positions, one split per tile ([aiter #7388], "Batch-first plan grid
@@ -222,11 +225,11 @@ int32_t sage_attn_kv_tile(void);
  * write (m, l, O) partials to the workspace and a merge step combines them
  * (O is kept normalized, O / l, in fp16 scaled into [-448, 448]: the merge's
  * inputs carry a relative rounding of 2^-11, below the bf16 output's 2^-9).
- * Q rows are quantized to e4m3 with a per-(token, head) scale; scores use FP8
- * MFMA; P is requantized per tile with the tile's largest per-token V scale.
- * D must be 128, or 64 with an e4m3 cache; the page size must be a multiple
- * of 16 that divides 256 or
- * is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
+ * bf16 / fp16 Q rows are quantized to e4m3 with a per-(token, head) scale
+ * (an e4m3 q is used as given, with its scale); scores use FP8 MFMA; P is
+ * requantized per tile with the tile's largest per-token V scale.  D must be
+ * 64, 128 or 256 (MXFP4 cache: 128); the page size must be a multiple of 16
+ * that divides 256 or is a multiple of 256; MTP * (Hq / Hkv) <= 64.  Page-table entries of tokens
  * below ctx_lens[b] must be valid page indices, and ctx_lens[b] <=
  * params.max_ctx; device data is not validated, but a page id outside
  * [0, P) reads page 0 and a length above max_ctx is treated as max_ctx, so
@@ -239,15 +242,20 @@ int32_t sage_attn_kv_tile(void);
  *           nibble), v_scale E8M0 [P, Hkv, D, page/32] (one scale per 32 keys
  *           of a channel: the PV reduction axis)
  * QK and PV run on the block-scaled MFMA with these scales, P8 =
- * e4m3(448 p); the page size must be a multiple of 64, and the V scale of
+ * e4m3(448 p); the page size must be a multiple of 64, V must be transposed
+ * (the only layout whose blocks run along the keys), and the V scale of
  * every 32-key block that holds a key below ctx_lens[b] must be set (blocks
  * wholly past it are ignored).
  */
 typedef struct {
     float sm_scale;        /* <= 0: 1/sqrt(D)                  */
     int32_t window;        /* 0: no sliding window             */
-    int32_t v_transposed;  /* layout flag of v_cache           */
+    int32_t v_transposed;  /* layout flag of v_cache (1 transposed, 0 plain) */
     int32_t max_ctx;       /* upper bound of ctx_lens (sizes the split plan) */
+    /* FP8_E4M3FN q only (NULL otherwise): F32 [1] (one scale for q) or
+     * [B, MTP, Hq] (one per (token, head) row), contiguous; q's value is
+     * code * scale */
+    const sage_tensor* q_scale;
 } sage_decode_params;
 
 sage_status sage_paged_decode_workspace_size(const sage_tensor* q, const sage_tensor* k_cache,

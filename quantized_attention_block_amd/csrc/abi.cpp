@@ -477,10 +477,15 @@ sage_status decode_query(const sage_tensor* q, const sage_tensor* page_table,
                          const sage_decode_params* p, DecShape* s) {
     sage_status st = check_basic(q, "q", 4);
     if (st) return st;
-    if (q->dtype != SAGE_BF16) return fail(SAGE_ERR_DTYPE, "q: expected bf16, got %s", dtype_name(q->dtype));
+    if (q->dtype == SAGE_FP8_E4M3FN || q->dtype == SAGE_FP8_E4M3FNUZ) {
+        if ((st = check_fp8(q, "q"))) return st;
+    } else if (q->dtype != SAGE_BF16 && q->dtype != SAGE_F16) {
+        return fail(SAGE_ERR_DTYPE, "q: expected bf16, f16 or fp8_e4m3fn, got %s", dtype_name(q->dtype));
+    }
     if (q->shape[3] > 1 && q->stride[3] != 1) return fail(SAGE_ERR_LAYOUT, "q: head-dim stride must be 1");
+    const int64_t qeb = (int64_t)elem_bytes(q->dtype);
     for (int i = 0; i < 3; ++i)
-        if (q->shape[i] > 1 && (q->stride[i] * 2) % 16)
+        if (q->shape[i] > 1 && (q->stride[i] * qeb) % 16)
             return fail(SAGE_ERR_ALIGNMENT, "q: stride of dim %d is not a multiple of 16 bytes", i);
     if (!p) return fail(SAGE_ERR_INVALID_ARG, "params: null");
     if ((st = check_basic(page_table, "page_table", 2))) return st;
@@ -497,8 +502,10 @@ sage_status decode_query(const sage_tensor* q, const sage_tensor* page_table,
     s->rows_pad = 64;
     return SAGE_OK;
 }
+// partial rows: fp16 h[DD] + fp32 m, l, vmax + pad, DD = 128 (D <= 128) or 256
 size_t decode_ws(const DecShape& s, int Hkv) {
-    return align256((size_t)s.B * Hkv * s.splits * s.rows_pad * (2 * 128 + 16));
+    const size_t dd = s.D > 128 ? 256 : 128;
+    return align256((size_t)s.B * Hkv * s.splits * s.rows_pad * (2 * dd + 16));
 }
 }  // namespace
 
@@ -534,17 +541,21 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
     if (!mx && (st = check_fp8(v_cache, "v_cache"))) return st;
     const int P = (int)k_cache->shape[0], Hkv = (int)k_cache->shape[1], page = (int)k_cache->shape[2];
     if (k_cache->shape[3] != (mx ? s.D / 2 : s.D)) return fail(SAGE_ERR_SHAPE, "k_cache head dim differs from q");
-    if (s.D != 128 && (mx || s.D != 64))
-        return fail(SAGE_ERR_UNSUPPORTED, "decode head dim must be 128 (or 64 with an e4m3 cache)");
+    if (mx ? s.D != 128 : (s.D != 64 && s.D != 128 && s.D != 256))
+        return fail(SAGE_ERR_UNSUPPORTED, "decode head dim must be 64, 128 or 256 (MXFP4 cache: 128)");
     if (Hkv < 1 || s.Hq % Hkv) return fail(SAGE_ERR_SHAPE, "query heads %d not a multiple of KV heads %d", s.Hq, Hkv);
     const int G = s.Hq / Hkv;
     if (G > 64 || s.MTP * G > 64) return fail(SAGE_ERR_UNSUPPORTED, "MTP x (Hq / Hkv) must be <= 64");
     if (page < 16 || page % 16 || !(256 % page == 0 || page % 256 == 0))
         return fail(SAGE_ERR_UNSUPPORTED, "page size %d: need a multiple of 16 that divides 256 or is a multiple of 256", page);
     if (P < 1) return fail(SAGE_ERR_SHAPE, "empty KV pool");
-    if (!p->v_transposed) return fail(SAGE_ERR_UNSUPPORTED, "only the transposed V cache [P, Hkv, D, page] is implemented");
+    if (p->v_transposed != 0 && p->v_transposed != 1)
+        return fail(SAGE_ERR_INVALID_ARG, "params.v_transposed must be 0 or 1");
     bool per_tensor = false;
     if (mx) {
+        if (!p->v_transposed)
+            return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 cache: V must be transposed [P, Hkv, D, page/2] "
+                        "(its E8M0 blocks run along the keys)");
         if (page % 64) return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 cache: page size %d is not a multiple of 64", page);
         const int64_t ks[4] = {P, Hkv, page, s.D / 2}, vt[4] = {P, Hkv, s.D, page / 2};
         const int64_t kse[4] = {P, Hkv, page, s.D / 32}, vse[4] = {P, Hkv, s.D, page / 32};
@@ -556,7 +567,7 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
         const int64_t ks[4] = {P, Hkv, page, s.D}, vt[4] = {P, Hkv, s.D, page}, ss[3] = {P, Hkv, page};
         const int64_t one[1] = {1};
         if ((st = check_exact(k_cache, "k_cache", SAGE_FP8_E4M3FN, 4, ks))) return st;
-        if ((st = check_exact(v_cache, "v_cache", SAGE_FP8_E4M3FN, 4, vt))) return st;
+        if ((st = check_exact(v_cache, "v_cache", SAGE_FP8_E4M3FN, 4, p->v_transposed ? vt : ks))) return st;
         // per-token scales [P, Hkv, page], or one per tensor [1] (both K and V)
         per_tensor = k_scale && k_scale->ndim == 1;
         if ((st = check_exact(k_scale, "k_scale", SAGE_F32, per_tensor ? 1 : 3, per_tensor ? one : ss))) return st;
@@ -569,8 +580,21 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
                     (long long)page_table->shape[1] * page, p->max_ctx);
     const int64_t cs[1] = {s.B};
     if ((st = check_exact(ctx_lens, "ctx_lens", SAGE_I32, 1, cs))) return st;
+    // e4m3 queries carry their scales: F32 [1] (per tensor) or [B, MTP, Hq]
+    const bool q8 = q->dtype == SAGE_FP8_E4M3FN;
+    bool q_per_tensor = false;
+    if (q8) {
+        if (!p->q_scale) return fail(SAGE_ERR_INVALID_ARG, "params.q_scale: required for an fp8_e4m3fn q");
+        const int64_t one[1] = {1}, rows[3] = {s.B, s.MTP, s.Hq};
+        q_per_tensor = p->q_scale->ndim == 1;
+        if ((st = check_exact(p->q_scale, "q_scale", SAGE_F32, q_per_tensor ? 1 : 3, q_per_tensor ? one : rows)))
+            return st;
+    } else if (p->q_scale) {
+        return fail(SAGE_ERR_INVALID_ARG, "params.q_scale: only an fp8_e4m3fn q takes scales");
+    }
     if ((st = check_basic(out, "out", 4))) return st;
-    if (out->dtype != SAGE_BF16) return fail(SAGE_ERR_DTYPE, "out: expected bf16");
+    if (out->dtype != SAGE_BF16 && out->dtype != SAGE_F16)
+        return fail(SAGE_ERR_DTYPE, "out: expected bf16 or f16, got %s", dtype_name(out->dtype));
     for (int i = 0; i < 4; ++i)
         if (out->shape[i] != q->shape[i]) return fail(SAGE_ERR_SHAPE, "out must be shaped like q");
     if (out->shape[3] > 1 && out->stride[3] != 1) return fail(SAGE_ERR_LAYOUT, "out: head-dim stride must be 1");
@@ -609,6 +633,10 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
     a.max_ctx = p->max_ctx;
     a.mx = mx ? 1 : 0;
     a.scale_per_tensor = per_tensor ? 1 : 0;
+    a.q_kind = q8 ? sage::kQueryE4M3 : (q->dtype == SAGE_F16 ? sage::kQueryF16 : sage::kQueryBF16);
+    a.q_scale = q8 ? (const float*)p->q_scale->data : nullptr;
+    a.q_scale_per_tensor = q_per_tensor ? 1 : 0;
+    a.out_f16 = out->dtype == SAGE_F16 ? 1 : 0;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)s.D));
     a.partials = nullptr;
     return SAGE_OK;

@@ -39,12 +39,12 @@ constexpr int kThreads = 256;
 constexpr int kRows = 64;            // query rows per KV head (padded): 16 per wave
 constexpr int kTile = kDecodeTile;   // 256 keys per split
 constexpr int kD = 128;
-// Partial row of one (sequence, KV head, split, query row): h[D] as fp16,
-// then m, l and vmax as fp32, then 4 pad bytes.  h = O8 / (448 l) with O8 =
-// sum P8 V8 (e4m3 codes): P8 <= 448 p and |V8| <= 448 give |h| <= 448, so the
-// fp16 rounding is relative (2^-11) whatever the cache's scales; the split's
-// output is h vmax.
-constexpr int kPartBytes = 2 * kD + 16;
+// Partial row of one (sequence, KV head, split, query row): h[DD] as fp16,
+// then m, l and vmax as fp32, then 4 pad bytes (DD = 128 for D <= 128, else
+// 256).  h = O8 / (448 l) with O8 = sum P8 V8 (e4m3 codes): P8 <= 448 p and
+// |V8| <= 448 give |h| <= 448, so the fp16 rounding is relative (2^-11)
+// whatever the cache's scales; the split's output is h vmax.
+__host__ __device__ constexpr int part_bytes(int DD) { return 2 * DD + 16; }
 
 // Keeps the first n bytes of v (all for n >= 16, none for n <= 0), zeroes the rest.
 __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
@@ -113,18 +113,44 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* scalar_ptr
     return (const __attribute__((address_space(4))) T*)p;
 }
 
+// Plain (not transposed) V tile [256 keys][128 B] per plane: chunk c of key
+// k is stored at c ^ pv_swz(k).  PV reads it with ds_read_b64_tr_b8: in each
+// 16-lane group, source lane 2 j + h points at key kb + j, channels
+// [16 db + 8 h, +8); the transposing read hands output lane 8 h + i the
+// bytes of channel 16 db + 8 h + i for keys kb .. kb + 7 (lane layout
+// measured on gfx950), the A operand of O^T = V^T P^T.  A half-wave then
+// reads 16 rows (two lane groups, 8 rows each) at one chunk; the XOR puts the
+// 8 rows of each row parity on 8 distinct chunks.
+__device__ __forceinline__ int pv_swz(int key) { return ((key >> 1) & 3) | (((key >> 5) & 1) << 2); }
+
+__device__ __forceinline__ uint2 keep_bytes8(uint2 v, int n) {
+    const uint32_t m0 = n >= 4 ? 0xFFFFFFFFu : (n <= 0 ? 0u : (1u << (8 * n)) - 1u);
+    const int n1 = n - 4;
+    const uint32_t m1 = n1 >= 4 ? 0xFFFFFFFFu : (n1 <= 0 ? 0u : (1u << (8 * n1)) - 1u);
+    return make_uint2(v.x & m0, v.y & m1);
+}
+
 // PW: keys per page-block, min(page, 256) (a page of at most 256 keys divides
 // 256; a larger page holds the whole tile at offset t0 % page).
 // MX: MXFP4 cache (E2M1 codes two per byte, E8M0 scales per 32 channels of
 // each K row and per 32 keys of each V^T row), QK and PV on the block-scaled
 // MFMA with the cache's scales; otherwise e4m3 with per-token fp32 scales.
-template <int PW, bool MX>
+// DD: 128 (D 64 runs as 128 with zero channels) or 256 (e4m3 only): the
+// channels are held as DD / 128 planes of 128, each with the D = 128 tile
+// layouts, QK accumulating over the planes.
+// VT: V cache transposed [P, Hkv, D, page] (the tile's V^T rows are copied as
+// they are); otherwise plain [P, Hkv, page, D] (e4m3 only), copied like K and
+// transposed by the LDS reads of PV.
+template <int PW, bool MX, int DD, bool VT>
 __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float alpha) {
     static_assert(!MX || PW >= 64, "MXFP4 pages of 64 keys or more");
+    static_assert(!MX || (DD == 128 && VT), "MXFP4: D 128 and transposed V");
+    constexpr int kPlanes = DD / 128;
     constexpr int kNpb = kTile / PW;                 // page-blocks per tile
     constexpr int kLgn = PW == 16 ? 0 : PW == 32 ? 1 : PW == 64 ? 2 : PW == 128 ? 3 : 4;   // log2(PW / 16)
-    constexpr int kRowB = MX ? kD / 2 : kD;          // bytes of one K row / of 256 keys of a V^T row
+    constexpr int kRowB = MX ? kD / 2 : kD;          // bytes of one K row (per plane)
     constexpr int kVLgn = MX ? kLgn - 1 : kLgn;      // log2 of 16-byte chunks per V^T row of a page-block
+    constexpr int kPlaneB = kTile * kD;              // bytes of one plane of a tile
     // Every kernel argument the block uses is read at entry, in one batch:
     // left to itself the compiler loads the pointers only after the context
     // length has arrived, one more round trip before the tile copies start.
@@ -146,35 +172,52 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, q4 = lane >> 4;
 
-    // ---- 1. this lane's Q slice: row r = 16 wave + c16, channels [32 q4, +32),
-    // also in flight with the context length (rows past R read row 0 of the
-    // head, in bounds, and are zeroed below)
+    // ---- 1. this lane's Q slice of each plane: row r = 16 wave + c16,
+    // channels [32 q4, +32); MX: [16 q4, +16) and [64 + 16 q4, +16) (the e4m3
+    // operand's byte order that meets the E2M1 operand's, see kx).  In
+    // flight with the context length; rows past R read row 0 of the head, in
+    // bounds, and are zeroed below.  bf16 / fp16: 64 bytes per plane; e4m3:
+    // the 32 code bytes in qraw[p][0..1].
     const int r = 16 * wave + c16;
     const int mt = (r < R ? r : 0) / G, gq = (r < R ? r : 0) % G;
     // the context length's scalar load goes out first: issued after the Q
     // loads, it waited for them, two memory latencies in a row
     const int ctx_raw = scalar_ptr(a.ctx_lens)[b];
-    uint4 qraw[4];
+    const int64_t qrow_idx = (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM + (int64_t)(hk * G + gq) * a.q_sH;
+    uint4 qraw[kPlanes][4];
     {
-        // channels [32 q4, +32); MX: [16 q4, +16) and [64 + 16 q4, +16) (the
-        // e4m3 operand's byte order that meets the E2M1 operand's, see kx)
-        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)mt * a.q_sM +
-                             (int64_t)(hk * G + gq) * a.q_sH;
         const int c0 = MX ? 16 * q4 : 32 * q4, c1 = MX ? 64 + 16 * q4 : 32 * q4 + 16;
-        if (MX || c0 < a.D) {
-            qraw[0] = *(const uint4*)(qp + c0);
-            qraw[1] = *(const uint4*)(qp + c0 + 8);
-            qraw[2] = *(const uint4*)(qp + c1);
-            qraw[3] = *(const uint4*)(qp + c1 + 8);
-        } else {   // D = 64: channels [64, 128) are zero
-            qraw[0] = qraw[1] = qraw[2] = qraw[3] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p) {
+            const int o0 = 128 * p + c0, o1 = 128 * p + c1;
+            if (a.q_kind == kQueryE4M3) {
+                const uint8_t* qp = (const uint8_t*)a.q + qrow_idx;
+                const bool in = MX || o0 < a.D;
+                qraw[p][0] = in ? *(const uint4*)(qp + o0) : make_uint4(0, 0, 0, 0);
+                qraw[p][1] = in ? *(const uint4*)(qp + o1) : make_uint4(0, 0, 0, 0);
+                qraw[p][2] = qraw[p][3] = make_uint4(0, 0, 0, 0);
+            } else if (MX || o0 < a.D) {
+                const uint16_t* qp = (const uint16_t*)a.q + qrow_idx;
+                qraw[p][0] = *(const uint4*)(qp + o0);
+                qraw[p][1] = *(const uint4*)(qp + o0 + 8);
+                qraw[p][2] = *(const uint4*)(qp + o1);
+                qraw[p][3] = *(const uint4*)(qp + o1 + 8);
+            } else {   // D = 64: channels [64, 128) are zero
+                qraw[p][0] = qraw[p][1] = qraw[p][2] = qraw[p][3] = make_uint4(0, 0, 0, 0);
+            }
         }
     }
+    // e4m3 queries: the row's scale (one per tensor, or per (token, head) row)
+    float qs_given = 0.0f;
+    if (a.q_kind == kQueryE4M3) qs_given = a.q_scale[a.q_scale_per_tensor ? 0 : (int64_t)(b * a.MTP + mt) * a.Hq + hk * G + gq];
     // Both are awaited here, so the Q loads cannot be moved below the early
     // exits (after the length arrives).
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        asm volatile("" : "+v"(qraw[i].x), "+v"(qraw[i].y), "+v"(qraw[i].z), "+v"(qraw[i].w) : "s"(ctx_raw));
+    for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            asm volatile("" : "+v"(qraw[p][i].x), "+v"(qraw[p][i].y), "+v"(qraw[p][i].z), "+v"(qraw[p][i].w)
+                         : "s"(ctx_raw));
 
     // context lengths beyond max_ctx (which sizes the split plan) or beyond
     // what the page table covers are clamped to them
@@ -185,10 +228,22 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
     const int t0 = T * kTile, last = ctx - 1;
 
-    // (sized for e4m3; MX uses the first half of each.  A size that depends
-    // on the template arguments leaves the host-side launch stub undefined.)
-    __shared__ __attribute__((aligned(16))) uint8_t kt_s[kTile * kD];
-    __shared__ __attribute__((aligned(16))) uint8_t vt_s[kTile * kD];
+    // K tile and V tile, kPlanes planes of [256 keys][128 B] (V^T: [page-block]
+    // [128 d][PW keys]); MX uses the first half of each plane.  (Declared
+    // with literal sizes in the branch of each plane count: a __shared__ size
+    // that depends on the template arguments leaves this compiler's host-side
+    // launch stubs undefined.)
+    uint8_t* kt_s;
+    uint8_t* vt_s;
+    if constexpr (kPlanes == 2) {
+        __shared__ __attribute__((aligned(16))) uint8_t kt2[2 * kTile * kD], vt2[2 * kTile * kD];
+        kt_s = kt2;
+        vt_s = vt2;
+    } else {
+        __shared__ __attribute__((aligned(16))) uint8_t kt1[kTile * kD], vt1[kTile * kD];
+        kt_s = kt1;
+        vt_s = vt1;
+    }
     // per-token fp32 scales; MX: the E8M0 bytes ([key][D/32] and [page-block][d][PW/32])
     __shared__ __attribute__((aligned(16))) float kss[kTile], vss[kTile];
 
@@ -230,16 +285,16 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         }
     }
 
-    // ---- 3. tile copies: 8 K and 8 V^T instructions per wave, 1 KB each
-    // (MX: 4 and 4).  Instruction i = wave + 4 j fills LDS chunks [64 i, +64)
-    // of each tile; both tiles hold 128 n chunks per page-block (n = PW / 16
-    // chunks per V^T row; MX: PW / 32), so it lies in page-block
-    // (wave + 4 j) / (2 n): a constant for n >= 2, and 2 j + wave / 2 for
-    // 16-key pages (a wave-uniform choice between two page ids).
-    // bytes of one page of one KV head; e4m3 rows of D = 64 channels sit in
-    // the tiles as 128-byte rows whose upper half (and V^T rows d >= 64) the
-    // copies fill with zeros: their offsets fall past the page's resource
-    const int kpage = a.page * (MX ? kRowB : a.D);
+    // ---- 3. tile copies, per plane 8 K and 8 V instructions per wave, 1 KB
+    // each (MX: 4 and 4).  Instruction i = wave + 4 j fills LDS chunks
+    // [64 i, +64) of a plane; the K plane (and a plain V plane) holds keys
+    // [8 i, +8), in page-block 8 i / PW: a constant for PW >= 32, and
+    // 2 j + wave / 2 for 16-key pages (a wave-uniform choice between two page
+    // ids).  A V^T plane holds 128 n chunks per page-block (n = PW / 16 chunks
+    // per row; MX: PW / 32).  Channels at or past D (D = 64, and for every
+    // copy whose plane lies past D) get offsets past the page's resource,
+    // which reads as zeros.
+    const int kpage = a.page * (MX ? kRowB : a.D);   // bytes of one page of one KV head
     if constexpr (MX) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -258,56 +313,88 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16, d * (a.page / 2) + koff / 2 + 16 * c,
                                                      0, 0, 0);
         }
-    } else
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int i = wave + 4 * j;
-        int pg;
-        if constexpr (PW == 16) pg = (wave & 2) ? pid[2 * j + 1] : pid[2 * j];
-        else pg = pid[j >> (kLgn - 1)];
-        // K: keys [8 i, +8) of the tile
-        const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
-        const int key = 8 * i + (lane >> 3);
-        const int kc = (lane & 7) ^ dk_swz(key);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + 1024 * i, 16,
-                                                 16 * kc < a.D ? (koff + key % PW) * a.D + 16 * kc : kpage,
-                                                 0, 0, 0);
-        // V^T: rows d of page-block (j >> kShift), chunks c
-        const int within = ((64 * i) & ((128 << kLgn) - 1)) + lane;
-        const int d = within >> kLgn, c = (within & ((1 << kLgn) - 1)) ^ dv_swz<kLgn>(d);
-        const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16, d * a.page + koff + 16 * c,
-                                                 0, 0, 0);
+        for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = wave + 4 * j;
+            int pg;
+            if constexpr (PW == 16) pg = (wave & 2) ? pid[2 * j + 1] : pid[2 * j];
+            else pg = pid[j >> (kLgn - 1)];
+            // K: keys [8 i, +8) of the tile, channels [128 p, +128)
+            const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+            const int key = 8 * i + (lane >> 3);
+            const int kc = (lane & 7) ^ dk_swz(key);
+            const int kch = 128 * p + 16 * kc;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + p * kPlaneB + 1024 * i, 16,
+                                                     kch < a.D ? (koff + key % PW) * a.D + kch : kpage,
+                                                     0, 0, 0);
+            const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
+            if constexpr (VT) {
+                // V^T: rows d of page-block (j >> kShift), chunks c
+                const int within = ((64 * i) & ((128 << kLgn) - 1)) + lane;
+                const int d = within >> kLgn, c = (within & ((1 << kLgn) - 1)) ^ dv_swz<kLgn>(d);
+                const int dg = 128 * p + d;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + p * kPlaneB + 1024 * i, 16,
+                                                         dg < a.D ? dg * a.page + koff + 16 * c : kpage, 0, 0, 0);
+            } else {
+                // plain V: laid out like K, with the PV read swizzle
+                const int vc = (lane & 7) ^ pv_swz(key);
+                const int vch = 128 * p + 16 * vc;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + p * kPlaneB + 1024 * i, 16,
+                                                         vch < a.D ? (koff + key % PW) * a.D + vch : kpage,
+                                                         0, 0, 0);
+            }
+        }
     }
     // keep the Q arithmetic below (which waits for the Q loads) from being
     // scheduled in between the copy instructions
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 4. Q row -> e4m3 with a per-row scale (the B operand of QK) ---------
-    v8i qf;
+    // ---- 4. Q row -> e4m3 with a per-row scale (the B operand of QK), or the
+    // given e4m3 codes and scale ------------------------------------------------
+    v8i qf[kPlanes];
     float qs;
-    {
-        float x[32];
+    if (a.q_kind == kQueryE4M3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[8 * i + 2 * k] = r < R ? bf16_bits_to_f32(w[k] & 0xFFFF) : 0.0f;
-                x[8 * i + 2 * k + 1] = r < R ? bf16_bits_to_f32(w[k] >> 16) : 0.0f;
-            }
+        for (int p = 0; p < kPlanes; ++p) {
+            const uint4 lo = r < R ? qraw[p][0] : make_uint4(0, 0, 0, 0);
+            const uint4 hi = r < R ? qraw[p][1] : make_uint4(0, 0, 0, 0);
+            qf[p] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
+        qs = r < R ? qs_given : 0.0f;
+    } else {
+        const bool f16 = a.q_kind == kQueryF16;
+        float x[kPlanes][32];
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w[4] = {qraw[p][i].x, qraw[p][i].y, qraw[p][i].z, qraw[p][i].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float v0 = f16 ? f16_bits_to_f32(w[k] & 0xFFFF) : bf16_bits_to_f32(w[k] & 0xFFFF);
+                    const float v1 = f16 ? f16_bits_to_f32(w[k] >> 16) : bf16_bits_to_f32(w[k] >> 16);
+                    x[p][8 * i + 2 * k] = r < R ? v0 : 0.0f;
+                    x[p][8 * i + 2 * k + 1] = r < R ? v1 : 0.0f;
+                }
+            }
         float am = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) am = fmaxf(am, fabsf(x[k]));
+        for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+            for (int k = 0; k < 32; ++k) am = fmaxf(am, fabsf(x[p][k]));
         am = fmaxf(am, __shfl_xor(am, 16));
         am = fmaxf(am, __shfl_xor(am, 32));
         const float inv = am > 0.0f ? kFp8Max / am : 0.0f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            uint32_t c0 = cvt_pk_fp8<false>(x[4 * w] * inv, x[4 * w + 1] * inv, 0);
-            qf[w] = (int)cvt_pk_fp8<true>(x[4 * w + 2] * inv, x[4 * w + 3] * inv, c0);
-        }
+        for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                uint32_t c0 = cvt_pk_fp8<false>(x[p][4 * w] * inv, x[p][4 * w + 1] * inv, 0);
+                qf[p][w] = (int)cvt_pk_fp8<true>(x[p][4 * w + 2] * inv, x[p][4 * w + 3] * inv, c0);
+            }
         qs = am / kFp8Max;
     }
 
@@ -350,7 +437,8 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     }
 
     // ---- 5. S^T for 256 keys x this wave's 16 rows: MFMA (g, m) holds, in
-    // element i of lane l, key 128 g + 32 (l / 16) + 4 m + i of query row r.
+    // element i of lane l, key 128 g + 32 (l / 16) + 4 m + i of query row r
+    // (summed over the planes).
     v4f S[2][8];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -362,15 +450,19 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
                 // row's E8M0 byte for that block
                 const v4i k4 = *(const v4i*)(kt_s + key * kRowB + 16 * (q4 ^ dk_swz_mx(key)));
                 const int sk = (int)((const uint8_t*)kss)[4 * key + q4];
-                S[g][m] = mfma_f4f8_16x16x128(__builtin_shufflevector(k4, k4, 0, 1, 2, 3, -1, -1, -1, -1), qf,
+                S[g][m] = mfma_f4f8_16x16x128(__builtin_shufflevector(k4, k4, 0, 1, 2, 3, -1, -1, -1, -1), qf[0],
                                               v4f{0.0f, 0.0f, 0.0f, 0.0f}, sk);
             } else {
                 const int sw = dk_swz(key);
-                const uint8_t* krow = kt_s + key * kD;
-                const v4i lo = *(const v4i*)(krow + 16 * ((2 * q4) ^ sw));
-                const v4i hi = *(const v4i*)(krow + 16 * ((2 * q4 + 1) ^ sw));
-                S[g][m] = mfma_f8_16x16x128(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf,
-                                            v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int p = 0; p < kPlanes; ++p) {
+                    const uint8_t* krow = kt_s + p * kPlaneB + key * kD;
+                    const v4i lo = *(const v4i*)(krow + 16 * ((2 * q4) ^ sw));
+                    const v4i hi = *(const v4i*)(krow + 16 * ((2 * q4 + 1) ^ sw));
+                    acc = mfma_f8_16x16x128(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf[p], acc);
+                }
+                S[g][m] = acc;
             }
         }
 
@@ -447,13 +539,14 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 
     // ---- 7. O^T = V^T P^T: element i of lane l of d-block db is channel
     // 16 db + 4 (l / 16) + i of query row r
+    constexpr int kDB = 8 * kPlanes;
     const bool all_in = t0 + kTile <= ctx;   // no page slot past the context in this tile
-    v4f O[8];
+    v4f O[kDB];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < kDB; ++db) {
         O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        const int d = 16 * db + c16;
-        const int sw = dv_swz<kLgn>(d);
+        const int p = db / 8, dl = 16 * (db % 8) + c16;   // plane, channel within the plane
+        const uint8_t* vplane = vt_s + p * kPlaneB;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int k0 = 128 * g + 32 * q4;           // tile-relative first key of this lane's 32
@@ -462,6 +555,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
                 // value past ctx meets P = 0) and that block's E8M0 byte; a
                 // block wholly past ctx may hold an unwritten scale (E8M0 255
                 // is NaN), so it gets 2^0
+                const int d = dl;
                 const int pb = k0 / PW, c = (k0 % PW) / 32;
                 const uint8_t* vrow = vt_s + (pb * 128 + d) * (PW / 2);
                 const v4i v4 = *(const v4i*)(vrow + 16 * (c ^ dv_swz<kVLgn>(d)));
@@ -471,23 +565,43 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
                                             O[db], sv);
                 continue;
             }
-            const int pb = k0 / PW, c = (k0 % PW) / 16;
-            const uint8_t* vrow = vt_s + (pb * 128 + d) * PW;
-            // keys [k0 + 16, +16): the next chunk of the row, or with 16-key
-            // pages the row of the next page-block
-            const uint8_t* vrow_hi = PW == 16 ? vrow + 128 * PW : vrow;
-            const int c_hi = PW == 16 ? 0 : c + 1;
             // keys at or beyond ctx may hold any bytes (e4m3 NaN codes
             // included) and 0 * NaN would poison the product: zero them
-            uint4 lo4 = *(const uint4*)(vrow + 16 * (c ^ sw));
-            uint4 hi4 = *(const uint4*)(vrow_hi + 16 * (c_hi ^ sw));
-            if (!all_in) {
-                const int nv = ctx - (t0 + k0);
-                lo4 = keep_bytes(lo4, nv);
-                hi4 = keep_bytes(hi4, nv - 16);
+            v8i av;
+            if constexpr (VT) {
+                const int d = dl;
+                const int sw = dv_swz<kLgn>(d);
+                const int pb = k0 / PW, c = (k0 % PW) / 16;
+                const uint8_t* vrow = vplane + (pb * 128 + d) * PW;
+                // keys [k0 + 16, +16): the next chunk of the row, or with 16-key
+                // pages the row of the next page-block
+                const uint8_t* vrow_hi = PW == 16 ? vrow + 128 * PW : vrow;
+                const int c_hi = PW == 16 ? 0 : c + 1;
+                uint4 lo4 = *(const uint4*)(vrow + 16 * (c ^ sw));
+                uint4 hi4 = *(const uint4*)(vrow_hi + 16 * (c_hi ^ sw));
+                if (!all_in) {
+                    const int nv = ctx - (t0 + k0);
+                    lo4 = keep_bytes(lo4, nv);
+                    hi4 = keep_bytes(hi4, nv - 16);
+                }
+                av = v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                         (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+            } else {
+                // four transposing reads of 8 keys each (see pv_swz)
+                const int sl = lane & 15;
+                const int cb = 16 * (db % 8) + 8 * (sl & 1);   // channels of this source lane
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int key = k0 + 8 * rr + (sl >> 1);
+                    const uint8_t* src = vplane + key * kD + 16 * ((cb >> 4) ^ pv_swz(key)) + (cb & 8);
+                    const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i*)(src));
+                    uint2 u = make_uint2((uint32_t)t[0], (uint32_t)t[1]);
+                    if (!all_in) u = keep_bytes8(u, ctx - (t0 + k0 + 8 * rr));
+                    av[2 * rr] = (int)u.x;
+                    av[2 * rr + 1] = (int)u.y;
+                }
             }
-            const v8i av = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                            (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
             O[db] = mfma_f8_16x16x128(av, pf[g], O[db]);
         }
     }
@@ -496,30 +610,35 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     // moved into the r < R branch below, where the padding rows' lanes would
     // feed stale registers into the valid rows' channels.
 #pragma unroll
-    for (int db = 0; db < 8; ++db) asm volatile("" : "+v"(O[db]));
+    for (int db = 0; db < kDB; ++db) asm volatile("" : "+v"(O[db]));
     if (r < R) {
         const float hs = ls > 0.0f ? 1.0f / (kFp8Max * ls) : 0.0f;
-        uint8_t* prow = (uint8_t*)a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPartBytes;
+        constexpr int kPB = 2 * DD + 16;
+        uint8_t* prow = (uint8_t*)a.partials + (((int64_t)bk * a.num_splits + s) * kRows + r) * kPB;
         // MX: h = O / (448 l vmax) with vmax = 2^(em - 127) (|h| <= 6)
         auto hv = [&](float o) { return MX ? __builtin_ldexpf(o * hs, 127 - em) : o * hs; };
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < kDB; ++db)
             if (16 * db < a.D)
                 *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
                     make_uint2(pack_h2(hv(O[db][0]), hv(O[db][1])), pack_h2(hv(O[db][2]), hv(O[db][3])));
-        if (q4 == 0) *(float4*)(prow + 2 * kD) = make_float4(rmax, ls, vmax, 0.0f);
+        if (q4 == 0) *(float4*)(prow + 2 * DD) = make_float4(rmax, ls, vmax, 0.0f);
     }
 }
 
 // Merge of the split partials of one (sequence, KV head, row): m* = max m_s,
 // out = sum 2^(m_s - m*) l_s (h_s vmax_s) / sum 2^(m_s - m*) l_s (fp32, split
-// order), bf16; l_s h_s vmax_s is the split's O_s.
-// One wave per row; the weights are broadcast and every lane merges two
+// order), bf16 or fp16; l_s h_s vmax_s is the split's O_s.
+// One wave per row; the weights are broadcast and every lane merges DD / 64
 // output channels over all splits with coalesced loads.
 constexpr int kMergeRowsPerBlock = 4;
 constexpr int kMergeBatch = 32;
 
+template <int DD>
 __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(DecodeArgs a) {
+    constexpr int kCh = DD / 64;                  // channels per lane: 2 or 4
+    using Word = typename std::conditional<kCh == 2, uint32_t, uint2>::type;
+    constexpr int kPB = part_bytes(DD);
     const int lane = threadIdx.x & 63;
     const int rowg = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
     const int R = a.MTP * (a.Hq / a.Hkv);
@@ -528,70 +647,85 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
     const int ctx_raw = a.ctx_lens[b];
     const int G = a.Hq / a.Hkv;
-    const uint8_t* base = (const uint8_t*)a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPartBytes;
-    const int64_t sstride = (int64_t)kRows * kPartBytes;
+    const uint8_t* base = (const uint8_t*)a.partials + ((int64_t)bk * a.num_splits * kRows + r) * kPB;
+    const int64_t sstride = (int64_t)kRows * kPB;
     // The first batch's loads go out together with the context length's,
     // for every allocated split (rows of splits this sequence does not have
     // are read but never used), instead of waiting for the split count.
     // (Split indexes are clamped to the allocated ones rather than guarded:
     // guarded loads become branches that the compiler waits on one by one.)
     const int na = min(kMergeBatch, a.num_splits);
-    const float4 ml_first = *(const float4*)(base + min(lane, na - 1) * sstride + 2 * kD);
-    uint32_t o_first[kMergeBatch];
+    const float4 ml_first = *(const float4*)(base + min(lane, na - 1) * sstride + 2 * DD);
+    Word o_first[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) o_first[u] = *(const uint32_t*)(base + min(u, na - 1) * sstride + 4 * lane);
+    for (int u = 0; u < kMergeBatch; ++u)
+        o_first[u] = *(const Word*)(base + min(u, na - 1) * sstride + sizeof(Word) * lane);
     const int ctx = min(min(ctx_raw, a.max_ctx), a.max_pages * a.page);   // as in k_paged_decode
     const int lo_b = a.window > 0 ? max(0, ctx - a.MTP - a.window + 1) : 0;
     const int nsp = ctx > 0 ? (ctx - 1) / kTile - lo_b / kTile + 1 : 0;
     // Splits are taken kMergeBatch at a time with every load of a batch in
-    // flight at once: lane s holds split s's (m, l), every lane two output
-    // channels of each split.  With at most kMergeBatch splits (windowed
-    // decode) this is the plain two-step merge; longer contexts carry a
-    // running max across batches and rescale the running sums.
-    float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    // flight at once: lane s holds split s's (m, l), every lane kCh output
+    // channels of each split.  With at most kMergeBatch splits this is the
+    // plain two-step merge; longer contexts carry a running max across
+    // batches and rescale the running sums.
+    float M = -INFINITY, L = 0.0f, o[kCh] = {};
     for (int s0 = 0; s0 < nsp; s0 += kMergeBatch) {
         const int n = min(kMergeBatch, nsp - s0);
         float4 ml = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);   // m, l, vmax
-        uint32_t o[kMergeBatch];
+        Word w[kMergeBatch];
         if (s0 == 0) {
             if (lane < n) ml = ml_first;
 #pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) o[u] = o_first[u];
+            for (int u = 0; u < kMergeBatch; ++u) w[u] = o_first[u];
         } else {
-            if (lane < n) ml = *(const float4*)(base + (s0 + lane) * sstride + 2 * kD);
+            if (lane < n) ml = *(const float4*)(base + (s0 + lane) * sstride + 2 * DD);
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u)
-                o[u] = u < n ? *(const uint32_t*)(base + (s0 + u) * sstride + 4 * lane) : 0u;
+                w[u] = u < n ? *(const Word*)(base + (s0 + u) * sstride + sizeof(Word) * lane) : Word{};
         }
         const float Mn = fmaxf(M, wave_max(ml.x));
         if (Mn == -INFINITY) continue;               // no visible key so far
         if (M != -INFINITY && M != Mn) {
             const float sc = __builtin_amdgcn_exp2f(M - Mn);
             L *= sc;
-            o0 *= sc;
-            o1 *= sc;
+#pragma unroll
+            for (int c = 0; c < kCh; ++c) o[c] *= sc;
         }
         M = Mn;
-        const float w = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
-        const float lw = w * ml.y;
+        const float wgt = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
+        const float lw = wgt * ml.y;
         const float ow = lw * ml.z;
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             if (u < n) {
                 const float wj = __shfl(ow, u);
-                const float2 h = unpack_h2(o[u]);
                 L = L + __shfl(lw, u);
-                o0 = o0 + wj * h.x;
-                o1 = o1 + wj * h.y;
+                const uint32_t* hw = (const uint32_t*)&w[u];
+#pragma unroll
+                for (int c = 0; c < kCh / 2; ++c) {
+                    const float2 h = unpack_h2(hw[c]);
+                    o[2 * c] = o[2 * c] + wj * h.x;
+                    o[2 * c + 1] = o[2 * c + 1] + wj * h.y;
+                }
             }
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int mt = r / G, g = r % G;
     uint16_t* op = (uint16_t*)a.out + (int64_t)b * a.o_sB + (int64_t)mt * a.o_sM +
-                   (int64_t)(hk * G + g) * a.o_sH + 2 * lane;
-    if (2 * lane < a.D)
-        *(uint32_t*)op = f32_to_bf16_bits(o0 * inv) | ((uint32_t)f32_to_bf16_bits(o1 * inv) << 16);
+                   (int64_t)(hk * G + g) * a.o_sH + kCh * lane;
+    if (kCh * lane < a.D) {
+        uint32_t ow[kCh / 2];
+#pragma unroll
+        for (int c = 0; c < kCh / 2; ++c)
+            ow[c] = a.out_f16 ? pack_h2(o[2 * c] * inv, o[2 * c + 1] * inv)
+                              : (uint32_t)f32_to_bf16_bits(o[2 * c] * inv) |
+                                    ((uint32_t)f32_to_bf16_bits(o[2 * c + 1] * inv) << 16);
+        if constexpr (kCh == 2)
+            *(uint32_t*)op = ow[0];
+        else
+            *(uint2*)op = make_uint2(ow[0], ow[1]);
+    }
 }
 
 }  // namespace
@@ -626,24 +760,39 @@ hipError_t decode_scratch(void** ptr) {
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid(a.num_splits, a.B * a.Hkv);
+    const int pw = a.page < kTile ? a.page : kTile;
     if (a.mx) {
-        switch (a.page < kTile ? a.page : kTile) {
-            case 64: k_paged_decode<64, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            case 128: k_paged_decode<128, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            default: k_paged_decode<256, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        switch (pw) {
+            case 64: k_paged_decode<64, true, 128, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            case 128: k_paged_decode<128, true, 128, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+            default: k_paged_decode<256, true, 128, true><<<grid, kThreads, 0, stream>>>(a, alpha); break;
         }
     } else {
-        switch (a.page < kTile ? a.page : kTile) {
-            case 16: k_paged_decode<16, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            case 32: k_paged_decode<32, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            case 64: k_paged_decode<64, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            case 128: k_paged_decode<128, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
-            default: k_paged_decode<256, false><<<grid, kThreads, 0, stream>>>(a, alpha); break;
+        // e4m3 cache: page-block width x head dim (128, or 256) x V layout
+        auto go = [&](auto pw_tag) {
+            constexpr int PW = decltype(pw_tag)::value;
+            if (a.D > 128) {
+                if (a.v_transposed) k_paged_decode<PW, false, 256, true><<<grid, kThreads, 0, stream>>>(a, alpha);
+                else k_paged_decode<PW, false, 256, false><<<grid, kThreads, 0, stream>>>(a, alpha);
+            } else {
+                if (a.v_transposed) k_paged_decode<PW, false, 128, true><<<grid, kThreads, 0, stream>>>(a, alpha);
+                else k_paged_decode<PW, false, 128, false><<<grid, kThreads, 0, stream>>>(a, alpha);
+            }
+        };
+        switch (pw) {
+            case 16: go(std::integral_constant<int, 16>{}); break;
+            case 32: go(std::integral_constant<int, 32>{}); break;
+            case 64: go(std::integral_constant<int, 64>{}); break;
+            case 128: go(std::integral_constant<int, 128>{}); break;
+            default: go(std::integral_constant<int, 256>{}); break;
         }
     }
     const int rows = a.B * a.Hkv * kRows;
-    k_decode_merge<<<(rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock, 64 * kMergeRowsPerBlock, 0,
-                     stream>>>(a);
+    const int mblocks = (rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock;
+    if (a.D > 128)
+        k_decode_merge<256><<<mblocks, 64 * kMergeRowsPerBlock, 0, stream>>>(a);
+    else
+        k_decode_merge<128><<<mblocks, 64 * kMergeRowsPerBlock, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -113,8 +113,9 @@ hipError_t launch_debug_qk_mx(const uint8_t* q, const uint8_t* q_scale, const ui
                               const uint8_t* k_scale, int B, int H, int Lqp, int Lkp, int q0, int nq,
                               int k0, int nk, float* out, hipStream_t stream);
 
+constexpr int kQueryBF16 = 0, kQueryF16 = 1, kQueryE4M3 = 2;
 struct DecodeArgs {
-    const void* q;            // bf16
+    const void* q;            // bf16 / fp16 / e4m3 (q_kind)
     int64_t q_sB, q_sM, q_sH;
     const uint8_t* k_cache;   // [P,Hkv,page,D]
     const uint8_t* v_cache;   // [P,Hkv,D,page] or [P,Hkv,page,D]
@@ -130,8 +131,12 @@ struct DecodeArgs {
     int max_ctx;              // context lengths are clamped to it (it sizes the split plan)
     int mx;                   // 1: MXFP4 cache (E2M1 codes, E8M0 scales) as documented in sage.h
     int scale_per_tensor;     // e4m3 cache: k_scale / v_scale hold one value each
+    int q_kind;               // kQueryBF16 / kQueryF16 / kQueryE4M3
+    const float* q_scale;     // e4m3 q: [1] or [B, MTP, Hq]
+    int q_scale_per_tensor;
+    int out_f16;              // out is fp16 (else bf16)
     float sm_scale;
-    float* partials;          // [B, Hkv, num_splits, rows] rows of fp16 h[D], fp32 m, l, vmax, pad
+    float* partials;          // [B, Hkv, num_splits, rows] rows of fp16 h[DD], fp32 m, l, vmax, pad
 };
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -70,7 +70,8 @@ class AttnParams(ctypes.Structure):
 
 class DecodeParams(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("window", ctypes.c_int32),
-                ("v_transposed", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+                ("v_transposed", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("q_scale", ctypes.POINTER(SageTensor))]
 
 
 _lib = None
@@ -352,18 +353,31 @@ def sage_decode_num_splits(window: int, mtp: int, max_ctx: int) -> int:
     return int(lib().sage_decode_num_splits(window, mtp, max_ctx))
 
 
+def _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale):
+    """DecodeParams plus the descriptor it points to (kept alive by the caller)."""
+    qsd = desc(q_scale) if q_scale is not None else None
+    prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx),
+                       ctypes.pointer(qsd) if qsd is not None else None)
+    return prm, qsd
+
+
 def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *, max_ctx: int,
                       window: int = 0, sm_scale: float = 0.0, v_transposed: bool = True,
-                      out: Optional[torch.Tensor] = None,
+                      q_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """q bf16 [B, MTP, Hq, D]; caches e4m3 [P, Hkv, page, D] (V transposed:
-    [P, Hkv, D, page]) with fp32 scales [P, Hkv, page], or MXFP4 caches
-    (torch.float4_e2m1fn_x2) K [P, Hkv, page, D/2], V [P, Hkv, D, page/2]
-    with E8M0 scales (torch.float8_e8m0fnu) K [P, Hkv, page, D/32] and
-    V [P, Hkv, D, page/32]; page_table int32 [B, pages]; ctx_lens int32 [B]."""
+    """q bf16 / fp16 [B, MTP, Hq, D], or e4m3 with fp32 `q_scale` ([1] or
+    [B, MTP, Hq]); caches e4m3 [P, Hkv, page, D] (V transposed: [P, Hkv, D,
+    page], or plain like K with v_transposed False) with fp32 scales
+    [P, Hkv, page] or [1], or MXFP4 caches (torch.float4_e2m1fn_x2) K
+    [P, Hkv, page, D/2], V [P, Hkv, D, page/2] with E8M0 scales
+    (torch.float8_e8m0fnu) K [P, Hkv, page, D/32] and V [P, Hkv, D, page/32];
+    page_table int32 [B, pages]; ctx_lens int32 [B].  `out` (allocated when
+    None) is bf16 or fp16 shaped like q; by default q's dtype, bf16 for an
+    e4m3 q."""
     if out is None:
-        out = torch.empty_like(q)
-    prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx))
+        odt = q.dtype if q.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale)
     qd, ptd, kcd = desc(q), desc(page_table), desc(k_cache)
     if workspace is None:
         nbytes = ctypes.c_size_t()
@@ -382,11 +396,12 @@ def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_len
 
 def sage_paged_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, out, *,
                               max_ctx: int, window: int = 0, sm_scale: float = 0.0,
-                              v_transposed: bool = True) -> torch.Tensor:
+                              v_transposed: bool = True,
+                              q_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sage_paged_decode without a workspace: the library's fixed per-device
     scratch holds the split partials (calls that overlap on one device race).
     `out` is required; nothing is allocated."""
-    prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx))
+    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale)
     _check(lib().sage_paged_decode_noalloc(ctypes.byref(desc(q)), ctypes.byref(desc(k_cache)),
                                            ctypes.byref(desc(v_cache)), ctypes.byref(desc(k_scale)),
                                            ctypes.byref(desc(v_scale)), ctypes.byref(desc(page_table)),
@@ -396,7 +411,7 @@ def sage_paged_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, page_table,
 
 
 def sage_paged_decode_workspace_size(q, k_cache, page_table, *, max_ctx: int, window: int = 0) -> int:
-    prm = DecodeParams(0.0, int(window), 1, int(max_ctx))
+    prm = DecodeParams(0.0, int(window), 1, int(max_ctx), None)
     nbytes = ctypes.c_size_t()
     _check(lib().sage_paged_decode_workspace_size(ctypes.byref(desc(q)), ctypes.byref(desc(k_cache)),
                                                   ctypes.byref(desc(page_table)),

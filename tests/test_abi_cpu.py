@@ -190,12 +190,36 @@ def test_paged_decode_refusals(S):
     assert call(prm, kc_=T(S.FP8_E4M3FNUZ, (P_, Hkv, page, D))) == S.ERR_DTYPE
     assert call(prm, vc_=T(S.FP8_E4M3FNUZ, (P_, Hkv, D, page))) == S.ERR_DTYPE
     assert call(prm, kc_=T(S.BF16, (P_, Hkv, page, D))) == S.ERR_DTYPE
-    assert call(prm, q_=T(S.F16, (B, MTP, Hq, D))) == S.ERR_DTYPE
+    assert call(prm, q_=T(S.I32, (B, MTP, Hq, D))) == S.ERR_DTYPE
+    assert call(prm, q_=T(S.FP8_E4M3FNUZ, (B, MTP, Hq, D))) == S.ERR_DTYPE   # not gfx950's FP8
+    # an e4m3 q needs its scales ([1] or [B, MTP, Hq]); a bf16 q takes none
+    q8 = T(S.FP8_E4M3FN, (B, MTP, Hq, D))
+    assert call(prm, q_=q8) == S.ERR_INVALID_ARG
+    qs_bad = T(S.F32, (B, MTP))
+    assert call(S.DecodeParams(0.0, 256, 1, 512, ctypes.pointer(qs_bad)), q_=q8) == S.ERR_SHAPE
+    qs_i32 = T(S.I32, (1,))
+    assert call(S.DecodeParams(0.0, 256, 1, 512, ctypes.pointer(qs_i32)), q_=q8) == S.ERR_DTYPE
+    qs_one = T(S.F32, (1,))
+    assert call(S.DecodeParams(0.0, 256, 1, 512, ctypes.pointer(qs_one))) == S.ERR_INVALID_ARG
+    # e4m3 q rows must start 16-byte aligned: a token stride of 8 bytes is refused
+    assert call(S.DecodeParams(0.0, 256, 1, 512, ctypes.pointer(qs_one)),
+                q_=T(S.FP8_E4M3FN, (B, MTP, Hq, D), stride=(MTP * Hq * D, 8, D, 1))) == S.ERR_ALIGNMENT
     assert call(prm, ws=64) == S.ERR_WORKSPACE
     assert call(S.DecodeParams(0.0, 256, 1, 4096)) == S.ERR_SHAPE       # table too short
-    assert call(S.DecodeParams(0.0, 256, 0, 512)) == S.ERR_UNSUPPORTED  # plain V layout
+    assert call(S.DecodeParams(0.0, 256, 2, 512)) == S.ERR_INVALID_ARG  # layout flag is 0 or 1
     assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
-    # head dims other than 128, and 64 with e4m3 caches
+    # plain V [P, Hkv, page, D]: a transposed-shaped cache is refused (page 64 != D)
+    kc64, vt64 = T(S.FP8_E4M3FN, (P_, Hkv, 64, D)), T(S.FP8_E4M3FN, (P_, Hkv, D, 64))
+    sc64 = T(S.F32, (P_, Hkv, 64))
+    plain = S.DecodeParams(0.0, 256, 0, 512)
+    st = S.lib().sage_paged_decode(r(q), r(kc64), r(vt64), r(sc64), r(sc64), r(T(S.I32, (B, 8))), r(cl),
+                                   r(plain), r(out), ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert st == S.ERR_SHAPE
+    # fp32 output is refused (bf16 or f16)
+    o32 = T(S.F32, (B, MTP, Hq, D))
+    assert S.lib().sage_paged_decode(r(q), r(kc), r(vc), r(ksc), r(vsc), r(pt), r(cl), r(prm), r(o32),
+                                     ctypes.c_void_p(FAKE), 1 << 30, None) == S.ERR_DTYPE
+    # head dims other than 64, 128 and 256
     q96, o96 = T(S.BF16, (B, MTP, Hq, 96)), T(S.BF16, (B, MTP, Hq, 96))
     assert S.lib().sage_paged_decode(r(q96), r(T(S.FP8_E4M3FN, (P_, Hkv, page, 96))),
                                      r(T(S.FP8_E4M3FN, (P_, Hkv, 96, page))), r(ksc), r(vsc), r(pt), r(cl),

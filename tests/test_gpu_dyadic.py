@@ -66,21 +66,33 @@ def test_mxfp4_pipeline_equals_base2_attention(dev, causal):
     assert np.abs(g - ref).max() <= REL * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("window,PS,D", [(0, 32, 128), (20, 32, 128), (20, 16, 128), (20, 32, 64)])
-def test_paged_decode_equals_base2_attention(dev, window, PS, D):
+@pytest.mark.parametrize("window,PS,D,plain_v,qkind", [
+    (0, 32, 128, False, "bf16"), (20, 32, 128, False, "bf16"), (20, 16, 128, False, "bf16"),
+    (20, 32, 64, False, "bf16"),
+    (20, 32, 128, True, "bf16"), (0, 16, 64, True, "f16"),           # plain V
+    (20, 32, 256, False, "bf16"), (20, 16, 256, True, "bf16"),       # D 256
+    (20, 32, 128, False, "e4m3"), (0, 64, 256, True, "e4m3")])       # e4m3 queries
+def test_paged_decode_equals_base2_attention(dev, window, PS, D, plain_v, qkind):
     B, MTP, Hq, Hkv = 2, 4, 4, 1
     max_pages = 128 // PS
     ctx = np.array([100, 57], np.int32)
     q, kf, vf, ks, vs, table = dyadic_decode(93, B=B, MTP=MTP, Hq=Hq, Hkv=Hkv, D=D, PS=PS,
                                              max_pages=max_pages)
-    say("dyadic paged decode", f"window {window} ctx {ctx.tolist()} page {PS}")
+    say("dyadic paged decode", f"window {window} ctx {ctx.tolist()} page {PS} D {D} plain V {plain_v} q {qkind}")
     to8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn)
-    kc, vt = to8(kf), to8(vf.transpose(0, 1, 3, 2))
+    kc, vt = to8(kf), to8(vf if plain_v else vf.transpose(0, 1, 3, 2))
     assert np.array_equal(kc.float().numpy(), kf)
-    out = sage.sage_paged_decode(torch.from_numpy(q).to(torch.bfloat16).to(dev), kc.to(dev), vt.to(dev),
+    qt = torch.from_numpy(q)
+    # every query value (0, +-2, 448) is exact in each query format; e4m3
+    # codes are the values themselves with one scale of 1
+    qd = {"bf16": qt.to(torch.bfloat16), "f16": qt.to(torch.float16), "e4m3": qt.to(torch.float8_e4m3fn)}[qkind]
+    assert np.array_equal(qd.float().numpy(), q)
+    q_scale = torch.ones(1, device=dev) if qkind == "e4m3" else None
+    out = sage.sage_paged_decode(qd.to(dev), kc.to(dev), vt.to(dev),
                                  torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev),
                                  torch.from_numpy(table).to(dev), torch.from_numpy(ctx).to(dev),
-                                 max_ctx=max_pages * PS, window=window, sm_scale=SM_SCALE)
+                                 max_ctx=max_pages * PS, window=window, sm_scale=SM_SCALE,
+                                 v_transposed=not plain_v, q_scale=q_scale)
     torch.cuda.synchronize()
     ref = base2_decode(q, kf, vf, ks, vs, table, ctx, window, Hkv)
     g = out.float().cpu().numpy()
