@@ -84,16 +84,15 @@ def _wall(fn, steps):
     return (time.perf_counter() - t0) / steps
 
 
-def prefill_bench(wname, steps, warmup, dev, time_unfused=False):
-    """INT8 workloads quantize Q in the attention kernel's prologue
-    (sage_quantize_qk(None, k) + sage_attn_fwd(q=...)); that step's output is
-    checked bit-equal to the unfused step's (Q quantized by sage_quantize_qk)
-    before timing."""
+def prefill_bench(wname, steps, warmup, dev, time_unfused=False, fused_q=True):
+    """fused_q: Q is quantized in the attention kernel's prologue
+    (sage_quantize_qk(None, k) + sage_attn_fwd(q=...), MXFP4 with the Hadamard
+    rotation there too); that step's output is checked bit-equal to the
+    unfused step's (Q quantized by sage_quantize_qk) before timing."""
     from quantized_attention_block_amd import sage
     from quantized_attention_block_amd import workloads as wl
     w = wl.WORKLOADS[wname]
     mode = sage.QK_MXFP4 if w.qk_mode == "mxfp4" else sage.QK_INT8
-    fused_q = mode == sage.QK_INT8
     print(f"bench: {wname}: drawing inputs", file=sys.stderr, flush=True)
     inp = wl.make_prefill(w, device=dev)
     had = sage.Hadamard(dev.index or 0) if mode == sage.QK_MXFP4 else None
@@ -114,7 +113,7 @@ def prefill_bench(wname, steps, warmup, dev, time_unfused=False):
 
     def attn():
         sage.sage_attn_fwd(qk, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out,
-                           q=inp.q if fused_q else None)
+                           q=inp.q if fused_q else None, hadamard=had if fused_q else None)
 
     def step():
         quant_qk()
@@ -134,11 +133,11 @@ def prefill_bench(wname, steps, warmup, dev, time_unfused=False):
     # the unfused step (Q's INT8 copy written and read) gives the same bits
     t_step_unfused = None
     if fused_q:
-        qk_u = sage.sage_quantize_qk(inp.q, inp.k, want_mean=False)
+        qk_u = sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, want_mean=False)
         out_u = torch.empty_like(out)
 
         def step_u():
-            sage.sage_quantize_qk(inp.q, inp.k, workspace=ws_qk, into=qk_u)
+            sage.sage_quantize_qk(inp.q, inp.k, mode=mode, hadamard=had, workspace=ws_qk, into=qk_u)
             quant_v()
             sage.sage_attn_fwd(qk_u, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out_u)
         step()
@@ -185,15 +184,16 @@ def prefill_bench(wname, steps, warmup, dev, time_unfused=False):
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": _traffic(f"attn_fwd_{wname}", src)}
-    res = {"value": round(literal / t_step / 1e12, 2), "unit": "TOPS",
+    res = {"value": round(literal / t_step / 1e12, 2), "unit": "TOPS", "fused_q": fused_q,
            "ms_per_step": round(t_step * 1e3, 4),
            "ms_per_step_hip_graph": round(t_step_graph * 1e3, 4),
            "attn_kernel_us": round(t_attn * 1e6, 2),
            "attn_kernel_tops_literal": round(literal / t_attn / 1e12, 1),
            "attn_algorithmic_ops": ops_alg,
            "quantize_qk_us": round(t_qk * 1e6, 2), "quantize_v_us": round(t_v * 1e6, 2),
-           "step": ("quantize_qk (K) + quantize_v + attn_fwd (Q quantized in its prologue)"
-                    if fused_q else "quantize_qk (Hadamard + MXFP4) + quantize_v + attn_fwd"),
+           "step": (("quantize_qk (K) + quantize_v + attn_fwd (Q quantized in its prologue"
+                     + (", Hadamard + MXFP4)" if mode == sage.QK_MXFP4 else ")")) if fused_q else
+                    "quantize_qk (Q and K) + quantize_v + attn_fwd"),
            "roofline": roof}
     if t_step_unfused is not None:
         res["ms_per_step_unfused_q"] = round(t_step_unfused * 1e3, 4)
@@ -365,7 +365,7 @@ def main():
              "ms_per_step_hip_graph": r["ms_per_step_hip_graph"]}
     if not args.no_extra:
         for wn in ("video_dit_mxfp4", "llm_prefill"):
-            _, rr = prefill_bench(wn, args.steps, args.warmup, dev, time_unfused=wn == "llm_prefill")
+            _, rr = prefill_bench(wn, args.steps, args.warmup, dev, time_unfused=True)
             extra[wn] = rr
         extra["paged_decode"] = decode_bench(args.steps, args.warmup, dev)
         extra["paged_decode_mxfp4"] = decode_bench(args.steps, args.warmup, dev, mx=True)

@@ -120,8 +120,8 @@ typedef struct sage_hadamard sage_hadamard;
  *      q_out   FP4X2 [B, H, SAGE_PAD(Lq), D/2]   q_scale E8M0 [B, H, SAGE_PAD(Lq), D/32]
  *      k_out   FP4X2 [B, H, SAGE_PAD(Lk), D/2]   k_scale E8M0 [B, H, SAGE_PAD(Lk), D/32]
  *  q, k: F16 or BF16 logical [B, L, H, D], D in {64, 128}, any B/L/H strides.
- *    q NULL (SAGE_QK_INT8 only): K alone, with q_out and q_scale NULL; Q is
- *    then quantized inside sage_attn_fwd (q_scale NULL there).
+ *    q NULL: K alone, with q_out and q_scale NULL; Q is then quantized inside
+ *    sage_attn_fwd (q_scale NULL there; MXFP4: with the same hadamard).
  *  k_mean: optional F32 [B, H, D] output of mu (NULL: kept in the workspace).
  *  workspace: sage_quantize_qk_workspace_size bytes, 16-byte aligned.  Its
  *    contents need no initialization and may be anything between calls; the
@@ -167,19 +167,21 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
  * so part of the numeric result): S = QK^T on INT8 (or scaled MXFP4) MFMA with int32 (fp32)
  * accumulation; x = S * q_scale * k_scale * sm_scale * log2(e); online
  * softmax with fp32 running max m and row sum l (l summed from the fp32
- * probabilities, before conversion); P = e4m3(448 p), with 448 p evaluated as
- * exp2(fma(S, c, -(m - log2 448))); O += P V on FP8 MFMA with fp32
+ * probabilities, before conversion); P = e4m3(448 p) (the kernel evaluates
+ * 448 p as exp2(fma(S, c, -(m - log2 448))), the same value up to the
+ * rounding of the exponent); O += P V on FP8 MFMA with fp32
  * accumulation; out = O * v_scale[d] / (448 l), rounded to out's dtype,
  * written with out's strides ([Sage2 README], [aiter #7388]: 448 = FP8_MAX
  * of OCP e4m3).  Causal masks keep key j <= query i (Lq == Lk);
  * fully masked tiles are skipped.
  *   q_q, q_scale, k_q, k_scale: sage_quantize_qk outputs (mode = qk_mode)
- *   q_scale NULL (SAGE_QK_INT8 only): q_q is the F16/BF16 Q, logical
- *     [B, Lq, H, D] with any B/L/H strides (token stride >= D, one head within
- *     2^31 bytes), quantized per 128-query block in the kernel's prologue with
- *     sage_quantize_qk's INT8 arithmetic: the codes and scales, hence the
- *     output, are those of the unfused path bit for bit; Q's INT8 copy is
- *     neither written nor read.
+ *   q_scale NULL: q_q is the F16/BF16 Q, logical [B, Lq, H, D] with any
+ *     B/L/H strides (token stride >= D, one head within 2^31 bytes),
+ *     quantized in the kernel's prologue with sage_quantize_qk's arithmetic:
+ *     INT8 per 128-query block, or (SAGE_QK_MXFP4) rotated by
+ *     params.hadamard and quantized to MXFP4.  The codes and scales, hence
+ *     the output, are those of the unfused path bit for bit; Q's quantized
+ *     copy is neither written nor read.
  *   v_q, v_scale: sage_quantize_v outputs
  *   out: F16, BF16 or F32 logical [B, Lq, H, D], any B/L/H strides
  * num_kv_heads: K/V heads (H % num_kv_heads == 0; query head h reads KV head
@@ -192,6 +194,9 @@ typedef struct {
     int32_t batch, heads, seqlen_q, seqlen_k, head_dim;
     int32_t num_kv_heads;  /* 0: heads                                         */
     int32_t q_block, k_block;  /* INT8 scale granularities used by quantize_qk */
+    /* SAGE_QK_MXFP4 with q_scale NULL only (else NULL): the rotation applied to
+     * Q in the prologue; NULL there means no rotation */
+    const sage_hadamard* hadamard;
 } sage_attn_params;
 
 sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale,

@@ -183,8 +183,6 @@ sage_status qk_inputs(const sage_tensor* q, const sage_tensor* k, const sage_qk_
         return fail(SAGE_ERR_SHAPE, "empty q or k (B, H, L must be >= 1)");
     if (p->mode != SAGE_QK_INT8 && p->mode != SAGE_QK_MXFP4)
         return fail(SAGE_ERR_INVALID_ARG, "params.mode: unknown qk mode %d", p->mode);
-    if (!q && p->mode != SAGE_QK_INT8)
-        return fail(SAGE_ERR_UNSUPPORTED, "K-only quantization (q NULL) is INT8 only");
     if (p->smooth_k != 0 && p->smooth_k != 1)
         return fail(SAGE_ERR_INVALID_ARG, "params.smooth_k must be 0 or 1");
     if (p->mode == SAGE_QK_INT8) {
@@ -276,9 +274,13 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
     } else {
         const int64_t qs[4] = {s.B, s.H, Lqp, s.D / 2}, ks[4] = {s.B, s.H, Lkp, s.D / 2};
         const int64_t qe[4] = {s.B, s.H, Lqp, s.D / 32}, ke[4] = {s.B, s.H, Lkp, s.D / 32};
-        if ((st = check_exact(q_out, "q_out", SAGE_FP4X2_E2M1, 4, qs))) return st;
+        if (!q) {
+            if (q_out || q_scale) return fail(SAGE_ERR_INVALID_ARG, "q is NULL: q_out and q_scale must be NULL");
+        } else {
+            if ((st = check_exact(q_out, "q_out", SAGE_FP4X2_E2M1, 4, qs))) return st;
+            if ((st = check_exact(q_scale, "q_scale", SAGE_E8M0, 4, qe))) return st;
+        }
         if ((st = check_exact(k_out, "k_out", SAGE_FP4X2_E2M1, 4, ks))) return st;
-        if ((st = check_exact(q_scale, "q_scale", SAGE_E8M0, 4, qe))) return st;
         if ((st = check_exact(k_scale, "k_scale", SAGE_E8M0, 4, ke))) return st;
         if (hadamard && (hadamard->R != 128 || s.D % hadamard->R != 0))
             return fail(SAGE_ERR_SHAPE, "hadamard: order %d must be 128 and divide D", hadamard->R);
@@ -339,8 +341,8 @@ sage_status sage_quantize_qk(const sage_tensor* q, const sage_tensor* k, const s
         e = sage::launch_quant_qk_mxfp4(
             qv, kv, s.B, s.H, s.Lq, s.Lk, s.D, mu, hadamard ? hadamard->bf16_mat : nullptr,
             hadamard ? hadamard->f16_mat : nullptr, hadamard ? hadamard->inv_sqrt_r : 1.0f, mu_rot,
-            (uint8_t*)q_out->data, (uint8_t*)q_scale->data, (uint8_t*)k_out->data,
-            (uint8_t*)k_scale->data, strm);
+            q ? (uint8_t*)q_out->data : nullptr, q ? (uint8_t*)q_scale->data : nullptr,
+            (uint8_t*)k_out->data, (uint8_t*)k_scale->data, strm);
     }
     return launch_status(e, "quantize qk");
 }
@@ -398,23 +400,29 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
     if (!std::isfinite(p->sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale is not finite");
     const int64_t Lqp = sage::pad128(Lq), Lkp = sage::pad128(Lk);
     sage_status st;
-    // q_scale NULL (INT8 only): q_q is the fp16/bf16 Q itself, quantized in
-    // the kernel's prologue
-    const bool q_fused = p->qk_mode == SAGE_QK_INT8 && q_scale == nullptr;
+    // q_scale NULL: q_q is the fp16/bf16 Q itself, quantized in the kernel's
+    // prologue (MXFP4: rotated by params.hadamard when given)
+    const bool q_fused = q_scale == nullptr;
+    if (p->hadamard && !(q_fused && p->qk_mode == SAGE_QK_MXFP4))
+        return fail(SAGE_ERR_INVALID_ARG,
+                    "params.hadamard: only used when the kernel quantizes Q to MXFP4 (q_scale NULL)");
+    if (p->hadamard && (p->hadamard->R != 128 || D % p->hadamard->R))
+        return fail(SAGE_ERR_SHAPE, "params.hadamard: order %d must be 128 and divide D", p->hadamard->R);
+    if (q_fused) {
+        if ((st = check_half_view(q_q, "q_q"))) return st;
+        if (q_q->shape[0] != B || q_q->shape[1] != Lq || q_q->shape[2] != H || q_q->shape[3] != D)
+            return fail(SAGE_ERR_SHAPE, "q_q (fp16/bf16 Q) must be [B, Lq, H, D]");
+        if (Lq > 1 && q_q->stride[1] < D)
+            return fail(SAGE_ERR_LAYOUT, "q_q: rows of one head overlap (token stride < D)");
+        if (((int64_t)(Lq - 1) * q_q->stride[1] + D) * 2 > 0x7FFFFF00LL)
+            return fail(SAGE_ERR_UNSUPPORTED, "q_q: one head spans more than 2^31 bytes");
+    }
     if (p->qk_mode == SAGE_QK_INT8) {
         if (p->q_block != 128) return fail(SAGE_ERR_UNSUPPORTED, "q_block must be 128");
         if (p->k_block != 64 && p->k_block != 128) return fail(SAGE_ERR_UNSUPPORTED, "k_block must be 64 or 128");
         const int64_t qs[4] = {B, H, Lqp, D}, ks[4] = {B, Hkv, Lkp, D};
         const int64_t qss[3] = {B, H, Lqp / p->q_block}, kss[3] = {B, Hkv, Lkp / p->k_block};
-        if (q_fused) {
-            if ((st = check_half_view(q_q, "q_q"))) return st;
-            if (q_q->shape[0] != B || q_q->shape[1] != Lq || q_q->shape[2] != H || q_q->shape[3] != D)
-                return fail(SAGE_ERR_SHAPE, "q_q (fp16/bf16 Q) must be [B, Lq, H, D]");
-            if (Lq > 1 && q_q->stride[1] < D)
-                return fail(SAGE_ERR_LAYOUT, "q_q: rows of one head overlap (token stride < D)");
-            if (((int64_t)(Lq - 1) * q_q->stride[1] + D) * 2 > 0x7FFFFF00LL)
-                return fail(SAGE_ERR_UNSUPPORTED, "q_q: one head spans more than 2^31 bytes");
-        } else if ((st = check_exact(q_q, "q_q", SAGE_I8, 4, qs))) {
+        if (!q_fused && (st = check_exact(q_q, "q_q", SAGE_I8, 4, qs))) {
             return st;
         }
         if ((st = check_exact(k_q, "k_q", SAGE_I8, 4, ks))) return st;
@@ -423,9 +431,9 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
     } else {
         const int64_t qs[4] = {B, H, Lqp, D / 2}, ks[4] = {B, Hkv, Lkp, D / 2};
         const int64_t qe[4] = {B, H, Lqp, D / 32}, ke[4] = {B, Hkv, Lkp, D / 32};
-        if ((st = check_exact(q_q, "q_q", SAGE_FP4X2_E2M1, 4, qs))) return st;
+        if (!q_fused && (st = check_exact(q_q, "q_q", SAGE_FP4X2_E2M1, 4, qs))) return st;
         if ((st = check_exact(k_q, "k_q", SAGE_FP4X2_E2M1, 4, ks))) return st;
-        if ((st = check_exact(q_scale, "q_scale", SAGE_E8M0, 4, qe))) return st;
+        if (!q_fused && (st = check_exact(q_scale, "q_scale", SAGE_E8M0, 4, qe))) return st;
         if ((st = check_exact(k_scale, "k_scale", SAGE_E8M0, 4, ke))) return st;
     }
     const int64_t vs[4] = {B, Hkv, D, Lkp}, vss[3] = {B, Hkv, D};
@@ -441,12 +449,22 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
         if (out->shape[i] > 1 && (out->stride[i] * (int64_t)elem_bytes(out->dtype)) % 16)
             return fail(SAGE_ERR_ALIGNMENT, "out: stride of dim %d is not a multiple of 16 bytes", i);
     if ((st = check_device())) return st;
+    if (p->hadamard) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (dev != p->hadamard->device)
+            return fail(SAGE_ERR_INVALID_ARG, "params.hadamard lives on device %d, current device is %d",
+                        p->hadamard->device, dev);
+    }
 
     sage::AttnArgs a;
     a.q = q_q->data;
     a.q_scale = q_fused ? nullptr : q_scale->data;
     a.q_fused = q_fused ? 1 : 0;
     a.qh = q_fused ? half_view(q_q) : sage::HalfView{nullptr, 0, 0, 0, 0};
+    a.hmat_bf16 = p->hadamard ? p->hadamard->bf16_mat : nullptr;
+    a.hmat_f16 = p->hadamard ? p->hadamard->f16_mat : nullptr;
+    a.inv_sqrt_r = p->hadamard ? p->hadamard->inv_sqrt_r : 1.0f;
     a.k = k_q->data;
     a.k_scale = k_scale->data;
     a.v = (const uint8_t*)v_q->data;

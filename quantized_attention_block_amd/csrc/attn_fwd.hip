@@ -380,7 +380,74 @@ __device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&
     return amax > 0.0f ? amax / 127.0f : 0.0f;
 }
 
-// QF: Q quantized in the prologue from the fp16/bf16 view a.qh (INT8 only).
+// Fused MXFP4 Q quantization (D = 128): lane (row, half) of a wave loads its
+// query row's channels [16 kc + 8 half, +8), the Hadamard matrix a.hmat
+// (NULL: no rotation) is copied to `ring` (the KV ring, still unused), and
+// the rows are rotated and quantized as the MXFP4 quantizer does.  The lane
+// keeps MX blocks 2 c + half (c = 0, 1), the A/B operand chunks of the QK
+// step: its own halves of those blocks and, swapped with its partner lane
+// l ^ 32, the partner's halves.  Returns after a block barrier, so the ring is
+// free for the tile copies.
+__device__ __forceinline__ void mx_fused_qfrag(QFrag<128, true>& qf, const AttnKernelArgs& a, const HalfView& qh,
+                                               int b, int h, int qrow, uint8_t* ring) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const bool valid = qrow < a.Lq;
+    const uint16_t* row = (const uint16_t*)qh.ptr + (int64_t)b * qh.sB + (int64_t)(valid ? qrow : 0) * qh.sL +
+                          (int64_t)h * qh.sH;
+    float y[4][16];
+    if (a.hmat) {
+        uint4 xb[8];
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc)
+            xb[kc] = valid ? *(const uint4*)(row + 16 * kc + 8 * half) : make_uint4(0, 0, 0, 0);
+        // 32 KB of +-1 entries: 32 regions of 1 KB, eight per wave
+        const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.hmat, D * D * 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int region = 4 * j + wave;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, ring + 1024 * region, 16, 1024 * region + 16 * lane, 0, 0, 0);
+        }
+        wait_dma();
+        __syncthreads();
+        mx_rotate_rows((const uint16_t*)ring, xb, qh.bf16, a.inv_sqrt_r, nullptr, valid, y);
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch0 = 32 * cb + 8 * i + 4 * half;
+                const uint2 u = valid ? *(const uint2*)(row + ch0) : make_uint2(0, 0);
+                const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t bits = (w[j / 2] >> (16 * (j % 2))) & 0xFFFF;
+                    const float t = qh.bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+                    y[cb][4 * i + j] = valid ? t : 0.0f;
+                }
+            }
+    }
+    int ex[4];
+    uint16_t pk[4][4];
+    mx_quant_rows(y, ex, pk);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int mine = 2 * c + half, theirs = 2 * c + (1 - half);
+        uint32_t wd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // bytes 4 i + {0, 1} of a block come from half 0, 4 i + {2, 3} from half 1
+            const uint32_t other = (uint32_t)__shfl_xor((int)pk[theirs][i], 32) & 0xFFFFu;
+            wd[i] = half == 0 ? (uint32_t)pk[mine][i] | (other << 16) : other | ((uint32_t)pk[mine][i] << 16);
+        }
+        qf.f[c] = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+        qf.s[c] = ex[mine] + 127;
+    }
+    __syncthreads();   // every wave is done reading the Hadamard matrix from the ring
+}
+
+// QF: Q quantized in the prologue from the fp16/bf16 view qh (INT8 per
+// 128-row block, or MXFP4 with the Hadamard rotation).
 template <int D, bool MX, bool QF = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_attn_fwd(
     AttnKernelArgs a, float alpha, HalfView qh) {
@@ -441,18 +508,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     uint8_t* const vs_lds = smem + kStages * G::kStageBytes;
     // fused Q: this lane's fp16/bf16 Q loads go out ahead of the copies, so
     // that the Q block's amax does not wait for the first two KV tiles
-    uint4 qraw[QF ? D / 16 : 1];
-    if constexpr (QF) load_q_rows<D>(qraw, qh, b, h, a.Lq, qrow, half);
+    uint4 qraw[QF && !MX ? D / 16 : 1];
+    if constexpr (QF && !MX) load_q_rows<D>(qraw, qh, b, h, a.Lq, qrow, half);
     if (wave == 0 && lane < D / 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.v_scale + (int64_t)bhk * D, D * 4), vs_lds, 16,
                                                  16 * lane, 0, 0, 0);
+    QFrag<D, MX> qf;
+    // Fused MXFP4 Q: the block's 128 rows are rotated and quantized with the
+    // MXFP4 quantizer's own arithmetic (mx_rotate_rows / mx_quant_rows), so the
+    // codes are its codes bit for bit.  The Hadamard matrix is staged in the
+    // KV ring before any tile is copied there (32 KB of the ring's 36.75 KB).
+    if constexpr (QF && MX) mx_fused_qfrag(qf, a, qh, b, h, qrow, smem);
     // tiles 0 and 1 in flight before the loop; tile j + 2 is issued in step j
     Dma::issue(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane);
     if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
 
-    QFrag<D, MX> qf;
     float q_s = 0.0f;
-    if constexpr (QF) {
+    if constexpr (QF && MX) {
+        // done above
+    } else if constexpr (QF) {
         q_s = qh.bf16 ? quant_qfrag<D, true>(qf, qraw, (float*)(vs_lds + 512), wave)
                       : quant_qfrag<D, false>(qf, qraw, (float*)(vs_lds + 512), wave);
         q_s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, q_s)));
@@ -705,9 +779,13 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
     dim3 grid((unsigned)(nqb * a.B * a.H));
     const AttnKernelArgs k{a.q, a.q_scale, a.k, a.k_scale, a.v, a.v_scale, a.out, a.B, a.H, a.Hkv,
-                           a.Lq, a.Lk, a.D, a.q_block, a.k_block, a.causal};
+                           a.Lq, a.Lk, a.D, a.q_block, a.k_block, a.causal,
+                           a.q_fused ? (a.qh.bf16 ? a.hmat_bf16 : a.hmat_f16) : nullptr, a.inv_sqrt_r};
     if (a.mxfp4) {
-        k_attn_fwd<128, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
+        if (a.q_fused)
+            k_attn_fwd<128, true, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
+        else
+            k_attn_fwd<128, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);
     } else if (a.D == 128) {
         if (a.q_fused)
             k_attn_fwd<128, false, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);

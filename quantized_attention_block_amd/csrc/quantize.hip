@@ -920,27 +920,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
             xb[kc] = valid ? *(const uint4*)(row + 16 * kc + 8 * half) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            v16f acc = {0};
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                const uint4 ha = *(const uint4*)&hs[(32 * cb + col) * D + 16 * kc + 8 * half];
-                if (src.bf16)
-                    acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ha),
-                                             __builtin_bit_cast(bf16x8, xb[kc]), acc);
-                else
-                    acc = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, ha),
-                                            __builtin_bit_cast(f16x8, xb[kc]), acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int ch = 32 * cb + 8 * (e / 4) + 4 * half + (e % 4);
-                float t = acc[e];
-                if (!isq && mu_rot) t = t - mu_rot[(int64_t)bh * D + ch];
-                y[cb][e] = valid ? t * inv_sqrt_r : 0.0f;
-            }
-        }
+        mx_rotate_rows(hs, xb, src.bf16, inv_sqrt_r, (!isq && mu_rot) ? mu_rot + (int64_t)bh * D : nullptr,
+                       valid, y);
     } else {
         const uint16_t* row = (const uint16_t*)src.ptr + (int64_t)b * src.sB +
                               (int64_t)(valid ? token : 0) * src.sL + (int64_t)h * src.sH;
@@ -963,24 +944,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
 
     uint8_t* out = isq ? q_out : k_out;
     uint8_t* oe = isq ? q_e8 : k_e8;
+    int ex[4];
+    uint16_t pk[4][4];
+    mx_quant_rows(y, ex, pk);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        float amax = 0.0f;
+        if (half == 0 && token < Lp) oe[((int64_t)bh * Lp + token) * (D / 32) + cb] = (uint8_t)(ex[cb] + 127);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[cb][e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const int ex = mx_exponent(amax);
-        if (half == 0 && token < Lp) oe[((int64_t)bh * Lp + token) * (D / 32) + cb] = (uint8_t)(ex + 127);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t n[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) n[j] = e2m1_rne(__builtin_ldexpf(y[cb][4 * i + j], -ex));
-            const uint16_t packed = (uint16_t)(n[0] | (n[1] << 4) | (n[2] << 8) | (n[3] << 12));
+        for (int i = 0; i < 4; ++i)
             if (token < Lp)
-                *(uint16_t*)(out + ((int64_t)bh * Lp + token) * (D / 2) + 16 * cb + 4 * i + 2 * half) =
-                    packed;
-        }
+                *(uint16_t*)(out + ((int64_t)bh * Lp + token) * (D / 2) + 16 * cb + 4 * i + 2 * half) = pk[cb][i];
     }
 }
 

@@ -124,6 +124,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                              0x00020000);   // gfx9 raw-buffer config
 }
 
+// ---- Hadamard rotation + MXFP4 quantization of one wave's 32 tokens -------
+// Shared by the MXFP4 quantizer and the attention kernel's fused-Q prologue, so
+// that both give the same codes bit for bit.  Lane l holds token (l % 32):
+//   xb[kc]: its channels [16 kc + 8 (l / 32), +8) (half precision, bf16 or fp16)
+//   hs:     the 128 x 128 +-1 Hadamard matrix in LDS, row-major, same precision
+// Y^T = H X^T on MFMA (H's entries and the inputs are exact, fp32 accumulation
+// over kc ascending), then y = (Y - sub) * inv_sqrt_r, with y[cb][e] channel
+// 32 cb + 8 (e / 4) + 4 (l / 32) + (e % 4) of the token; sub (the rotated K
+// mean, per channel) may be NULL.  Invalid tokens give 0.
+__device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (&xb)[8], bool bf16,
+                                               float inv_sqrt_r, const float* sub, bool valid,
+                                               float (&y)[4][16]) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        v16f acc = {0};
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+            const uint4 ha = *(const uint4*)&hs[(32 * cb + col) * D + 16 * kc + 8 * half];
+            if (bf16)
+                acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ha), __builtin_bit_cast(bf16x8, xb[kc]), acc);
+            else
+                acc = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, ha), __builtin_bit_cast(f16x8, xb[kc]), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int ch = 32 * cb + 8 * (e / 4) + 4 * half + (e % 4);
+            float t = acc[e];
+            if (sub) t = t - sub[ch];
+            y[cb][e] = valid ? t * inv_sqrt_r : 0.0f;
+        }
+    }
+}
+
+// MX blocks of the values above: per 32-channel block cb the shared exponent
+// ex[cb] = floor(log2 amax) - 2 (the lane and its partner l ^ 32 hold the
+// block's two halves) and the E2M1 codes of y * 2^-ex, packed four per
+// uint16: pk[cb][i] holds channels 32 cb + 8 i + 4 (l / 32) + 0..3, i.e.
+// bytes 4 i + 2 (l / 32) + {0, 1} of the block's 16 packed bytes.
+__device__ __forceinline__ void mx_quant_rows(const float (&y)[4][16], int (&ex)[4], uint16_t (&pk)[4][4]) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[cb][e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        ex[cb] = mx_exponent(amax);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t n[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) n[j] = e2m1_rne(__builtin_ldexpf(y[cb][4 * i + j], -ex[cb]));
+            pk[cb][i] = (uint16_t)(n[0] | (n[1] << 4) | (n[2] << 8) | (n[3] << 12));
+        }
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

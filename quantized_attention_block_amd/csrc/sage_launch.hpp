@@ -85,9 +85,14 @@ struct AttnArgs {
     int mxfp4;
     float sm_scale;
     // q_fused: Q is the caller's fp16/bf16 [B, Lq, H, D] view qh (q and
-    // q_scale unused), quantized to INT8 per 128-row block in the prologue
+    // q_scale unused), quantized in the prologue: INT8 per 128-row block, or
+    // (mxfp4) rotated by the Hadamard matrices below (NULL: no rotation) and
+    // quantized to MXFP4
     int q_fused;
     HalfView qh;
+    const void* hmat_bf16;
+    const void* hmat_f16;
+    float inv_sqrt_r;
 };
 // The part of AttnArgs the attention kernel itself takes (the fused-Q view
 // travels as a kernel argument of its own).
@@ -102,6 +107,8 @@ struct AttnKernelArgs {
     int B, H, Hkv, Lq, Lk, D;
     int q_block, k_block;
     int causal;
+    const void* hmat;     // fused MXFP4 Q: the 128 x 128 Hadamard in Q's precision (NULL: none)
+    float inv_sqrt_r;
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 

@@ -65,7 +65,8 @@ class AttnParams(ctypes.Structure):
                 ("qk_mode", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32)]
+                ("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32),
+                ("hadamard", ctypes.c_void_p)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -201,8 +202,9 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
                      workspace: Optional[torch.Tensor] = None,
                      into: Optional[QuantizedQK] = None) -> QuantizedQK:
     """q, k: logical [B, L, H, D] fp16/bf16 (any B/L/H strides).  `into`
-    reuses the output tensors of an earlier call with the same shapes.  q None
-    (INT8 only): K alone; Q is then quantized inside sage_attn_fwd(q=...)."""
+    reuses the output tensors of an earlier call with the same shapes.  q None:
+    K alone; Q is then quantized inside sage_attn_fwd(q=...) (MXFP4: pass the
+    same hadamard there)."""
     B, Lk, H, D = k.shape
     Lq = q.shape[1] if q is not None else 0
     dev = k.device
@@ -218,6 +220,12 @@ def sage_quantize_qk(q: torch.Tensor, k: torch.Tensor, *, mode: int = QK_INT8, q
         k_out = torch.empty((B, H, pad128(Lk), D), dtype=torch.int8, device=dev)
         k_sc = torch.empty((B, H, pad128(Lk) // k_block), dtype=torch.float32, device=dev)
         qd, kd, qsd, ksd = None, desc(k_out), None, desc(k_sc)
+    elif q is None:
+        q_out = q_sc = None
+        k_out = torch.empty((B, H, pad128(Lk), D // 2), dtype=torch.uint8, device=dev)
+        k_sc = torch.empty((B, H, pad128(Lk), D // 32), dtype=torch.uint8, device=dev)
+        qd, qsd = None, None
+        kd, ksd = desc(k_out, FP4X2_E2M1), desc(k_sc, E8M0)
     elif mode == QK_INT8:
         q_out = torch.empty((B, H, pad128(Lq), D), dtype=torch.int8, device=dev)
         k_out = torch.empty((B, H, pad128(Lk), D), dtype=torch.int8, device=dev)
@@ -299,12 +307,13 @@ def sage_quantize_v(v: torch.Tensor, workspace: Optional[torch.Tensor] = None, i
 def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, causal: bool = False,
                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                   out_dtype: torch.dtype = torch.bfloat16, num_kv_heads: int = 0,
-                  q: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  q: Optional[torch.Tensor] = None,
+                  hadamard: Optional[Hadamard] = None) -> torch.Tensor:
     """Quantized attention; `out` is a logical [B, Lq, H, D] fp16/bf16 tensor
     with any B/L/H strides (allocated contiguous when None).  When qk holds K
     alone (sage_quantize_qk(None, k)), `q` is the fp16/bf16 [B, Lq, H, D] Q,
-    quantized to INT8 in the kernel's prologue (the same codes and scales as
-    sage_quantize_qk's)."""
+    quantized in the kernel's prologue to the same codes and scales as
+    sage_quantize_qk's (MXFP4: rotated by `hadamard`, None for no rotation)."""
     if (qk.q is None) != (q is not None):
         raise ValueError("pass q exactly when qk was quantized without Q")
     if q is not None:
@@ -317,14 +326,17 @@ def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, 
     if out is None:
         out = torch.empty((B, Lq, H, D), dtype=out_dtype, device=dev)
     prm = AttnParams(float(sm_scale), int(causal), qk.mode, B, H, Lq, qk.Lk, D,
-                     num_kv_heads, qk.q_block, qk.k_block)
+                     num_kv_heads, qk.q_block, qk.k_block,
+                     hadamard.handle if hadamard is not None else None)
+    mx = qk.mode == QK_MXFP4
+    kd = desc(qk.k, FP4X2_E2M1) if mx else desc(qk.k)
+    ksd = desc(qk.k_scale, E8M0) if mx else desc(qk.k_scale)
     if q is not None:
-        qd, qsd, kd, ksd = desc(q), None, desc(qk.k), desc(qk.k_scale)
-    elif qk.mode == QK_INT8:
-        qd, qsd, kd, ksd = desc(qk.q), desc(qk.q_scale), desc(qk.k), desc(qk.k_scale)
+        qd, qsd = desc(q), None
+    elif not mx:
+        qd, qsd = desc(qk.q), desc(qk.q_scale)
     else:
-        qd, kd = desc(qk.q, FP4X2_E2M1), desc(qk.k, FP4X2_E2M1)
-        qsd, ksd = desc(qk.q_scale, E8M0), desc(qk.k_scale, E8M0)
+        qd, qsd = desc(qk.q, FP4X2_E2M1), desc(qk.q_scale, E8M0)
     _check(lib().sage_attn_fwd(ctypes.byref(qd), _ref(qsd), ctypes.byref(kd),
                                ctypes.byref(ksd), ctypes.byref(desc(v_q)),
                                ctypes.byref(desc(v_scale)), ctypes.byref(prm),
@@ -334,14 +346,13 @@ def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, 
 
 def sage_attention(q, k, v, *, causal=False, sm_scale=0.0, mode=QK_INT8, k_block=64,
                    hadamard: Optional[Hadamard] = None, out=None):
-    """quantize_qk + quantize_v + attn_fwd on strided [B, L, H, D] inputs (INT8:
-    Q quantized inside the attention kernel)."""
-    fuse = mode == QK_INT8
-    qk = sage_quantize_qk(None if fuse else q, k, mode=mode, k_block=k_block, hadamard=hadamard,
-                          want_mean=False)
+    """quantize_qk (K) + quantize_v + attn_fwd on strided [B, L, H, D] inputs,
+    Q quantized inside the attention kernel (INT8, or MXFP4 rotated by
+    `hadamard`)."""
+    qk = sage_quantize_qk(None, k, mode=mode, k_block=k_block, hadamard=hadamard, want_mean=False)
     v_q, v_s = sage_quantize_v(v)
     return sage_attn_fwd(qk, v_q, v_s, causal=causal, sm_scale=sm_scale, out=out,
-                         out_dtype=q.dtype, q=q if fuse else None)
+                         out_dtype=q.dtype, q=q, hadamard=hadamard if mode == QK_MXFP4 else None)
 
 
 def sage_attn_kv_tile() -> int:

@@ -291,7 +291,8 @@ def test_fused_q_refusals(S):
         return lib.sage_quantize_qk(None, r(k), r(prm), q_out and r(q_out), q_scale and r(q_scale), r(kq), r(ks),
                                     None, None, ctypes.c_void_p(FAKE), 1 << 30, None)
 
-    assert qk(S.QkParams(S.QK_MXFP4, 128, 64, 1)) == S.ERR_UNSUPPORTED     # INT8 only
+    # MXFP4 K-only takes FP4X2 / E8M0 outputs (INT8 ones are refused)
+    assert qk(S.QkParams(S.QK_MXFP4, 128, 64, 1)) == S.ERR_DTYPE
     assert qk(S.QkParams(S.QK_INT8, 128, 64, 1), q_out=T(S.I8, (B, H, L, D))) == S.ERR_INVALID_ARG
     nbytes = ctypes.c_size_t()
     assert lib.sage_quantize_qk_workspace_size(None, r(k), r(S.QkParams(S.QK_INT8, 128, 64, 1)),
@@ -308,7 +309,10 @@ def test_fused_q_refusals(S):
     assert attn(T(S.I8, (B, H, L, D))) == S.ERR_DTYPE                      # needs the fp16/bf16 Q
     assert attn(T(S.BF16, (B, L + 1, H, D))) == S.ERR_SHAPE
     assert attn(T(S.BF16, (B, L, H, D), stride=(L * H * D, 64, D, 1))) == S.ERR_LAYOUT   # rows overlap
-    assert attn(T(S.BF16, (B, L, H, D)), qk_mode=S.QK_MXFP4) != S.OK         # MXFP4 keeps its q_scale
+    # MXFP4 fused: K codes must be FP4X2 / E8M0 (INT8 ones are refused); a
+    # Hadamard only goes with an MXFP4 Q quantized in the kernel
+    assert attn(T(S.BF16, (B, L, H, D)), qk_mode=S.QK_MXFP4) == S.ERR_DTYPE
+    assert attn(T(S.BF16, (B, L, H, D)), hadamard=FAKE) == S.ERR_INVALID_ARG
 
 
 def test_paged_decode_noalloc_refuses_above_its_scratch(S):

@@ -371,3 +371,34 @@ def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
     assert torch.equal(got, ref)
     bf = sage.sage_attention(q, k, v, causal=causal, sm_scale=w.sm_scale)   # the fused convenience path
     assert torch.equal(bf, ref.to(dtype))
+
+
+@pytest.mark.parametrize("Lq,Lk,H,dtype,rotate", [
+    (1000, 1000, 2, torch.bfloat16, True),      # strided video-DiT views, ragged last block
+    (333, 333, 2, torch.bfloat16, False),       # no rotation
+    (700, 1500, 2, torch.bfloat16, True),       # Lq != Lk
+    (256, 256, 3, torch.float16, True),         # fp16 inputs: the fp16 Hadamard matrix
+    (32760, 32760, 1, torch.bfloat16, True),    # the full video-DiT length, one head
+])
+def test_fused_mxfp4_q_equals_unfused(dev, Lq, Lk, H, dtype, rotate):
+    """Q rotated and quantized to MXFP4 in the attention prologue
+    (sage_quantize_qk(None, k) + sage_attn_fwd(q=..., hadamard=...)) gives the
+    unfused MXFP4 path's output bit for bit: the prologue runs the MXFP4
+    quantizer's rotation and block arithmetic on the same rows."""
+    w = wl.WORKLOADS["video_dit_mxfp4"]
+    inp = wl.make_prefill(w, Lq=Lq, Lk=Lk, H=H, device=dev)
+    q, k, v = inp.q, inp.k, inp.v
+    if dtype != q.dtype:
+        q, k, v = (x.to(dtype) for x in (q, k, v))
+    had = sage.Hadamard(0) if rotate else None
+    say("fused MXFP4 Q", Lq, Lk, H, dtype, "rotation" if rotate else "no rotation")
+    qk = sage.sage_quantize_qk(q, k, mode=sage.QK_MXFP4, hadamard=had)
+    kq = sage.sage_quantize_qk(None, k, mode=sage.QK_MXFP4, hadamard=had)
+    v_q, v_s = sage.sage_quantize_v(v)
+    ref = sage.sage_attn_fwd(qk, v_q, v_s, sm_scale=w.sm_scale, out_dtype=torch.float32)
+    got = sage.sage_attn_fwd(kq, v_q, v_s, sm_scale=w.sm_scale, out_dtype=torch.float32, q=q, hadamard=had)
+    torch.cuda.synchronize()
+    assert kq.q is None and torch.equal(kq.k, qk.k) and torch.equal(kq.k_scale, qk.k_scale)
+    assert torch.equal(got, ref)
+    conv = sage.sage_attention(q, k, v, sm_scale=w.sm_scale, mode=sage.QK_MXFP4, hadamard=had)
+    assert torch.equal(conv, ref.to(dtype))
