@@ -128,6 +128,42 @@ struct TileDma {
     static_assert(kKRegions % NWAVES == 0 && kVRegions % NWAVES == 0, "regions split evenly");
     static_assert(kKSChunks <= 64, "K scales fit one wave instruction");
 
+    // Per-lane parts of the copy offsets with four waves.  Region j * 4 + wave
+    // of a tile starts at byte 1024 (j * 4 + wave) of the K block, or at V^T
+    // row 16 (j * 4 + wave); the swizzle of a chunk depends on the lane and
+    // the wave only (for K on row bits that region j * 4 adds nothing to, for
+    // V^T on (row / 4) % 4 = lane / 16), so each copy's per-lane offset is
+    // one of these two values and j moves only the scalar offset: two live
+    // registers across the KV loop instead of one per copy instruction.
+    struct LaneOffsets {
+        int k, v;
+    };
+    __device__ __forceinline__ static LaneOffsets lane_offsets(int Lkp, int wave, int lane) {
+        static_assert(NWAVES == 4, "offsets shared across regions need four waves");
+        const int p = wave * 64 + lane;   // region `wave`, chunk `lane`
+        const int r = p / G::kRowChunks, c = (p % G::kRowChunks) ^ k_swz<D, MX>(r);
+        const int d = p / G::kVRowChunks, cv = (p % G::kVRowChunks) ^ v_swz(d);
+        return {r * G::kRowBytes + 16 * c, d * Lkp + 16 * cv};
+    }
+    __device__ __forceinline__ static void issue4(uint8_t* stage, __amdgpu_buffer_rsrc_t kr,
+                                                  __amdgpu_buffer_rsrc_t ksr, __amdgpu_buffer_rsrc_t vr,
+                                                  int Lkp, int kt, int wave, int lane, const LaneOffsets& lo) {
+#pragma unroll
+        for (int j = 0; j < kKRegions / NWAVES; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, stage + (j * NWAVES + wave) * 1024, 16, lo.k,
+                                                     kt * G::kKBytes + j * NWAVES * 1024, 0, 0);
+        if constexpr (MX) {
+            if (wave == 0 && lane < kKSChunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksr, stage + G::kKBytes, 16, 16 * lane,
+                                                         kt * G::kKScaleBytes, 0, 0);
+        }
+        uint8_t* vstage = stage + G::kVOff;
+#pragma unroll
+        for (int j = 0; j < kVRegions / NWAVES; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vstage + (j * NWAVES + wave) * 1024, 16, lo.v,
+                                                     kt * kBN + j * NWAVES * 16 * Lkp, 0, 0);
+    }
+
     // kr: K codes of this (b, kv head) [Lkp][row bytes]; ksr: its E8M0 scales
     // [Lkp][D/32] (MXFP4); vr: V^T of this (b, kv head) [D][Lkp].  Buffer
     // resources bound to exactly those extents (reads outside return 0); the
@@ -193,45 +229,31 @@ struct QFrag {
     int s[MX ? kN : 1];
 };
 
-// INT8 scores are accumulated on top of the bit pattern of 1.5 * 2^23: the
-// int32 result, read as a float, is then exactly 1.5 * 2^23 + S (floats in
-// [2^23, 2^24) are the integers, and |S| <= D * 127^2 < 2^22 for D <= 256),
-// so one subtraction yields fp32(S) exactly, cheaper than v_cvt_f32_i32.
-// Integer comparison of biased scores orders them like S.
-constexpr int kSBias = 0x4B400000;
-constexpr float kSBiasF = 12582912.0f;   // 1.5 * 2^23
+// INT8 scores are exact int32 (|S| <= D * 127^2); fp32(S) is one
+// v_cvt_f32_i32, exact for |S| < 2^24.  (Accumulating on top of the bit
+// pattern of 1.5 * 2^23 would make the conversion an add, but its sixteen
+// accumulator registers pushed the kernel past its register budget into
+// spills whose reloads inside the KV loop waited for every tile copy in
+// flight.)  The row max is taken on the integer scores (rounding is monotone).
 // Row max of raw scores: integer max for INT8, fmaxf for MXFP4 (scores are
 // finite, so fmaxf's NaN rule never applies; a compare-and-select does not
 // map to v_max3_f32).
 __device__ __forceinline__ int vmax(int a, int b) { return a > b ? a : b; }
 __device__ __forceinline__ float vmax(float a, float b) { return fmaxf(a, b); }
-__device__ __forceinline__ float score_f(int biased) { return __int_as_float(biased) - kSBiasF; }
+__device__ __forceinline__ float score_f(int s) { return (float)s; }
 __device__ __forceinline__ float score_f(float s) { return s; }
 
-// Sixteen copies of the bias, kept in registers across the KV loop as the
-// first MFMA's accumulator input (an opaque value, so the compiler does not
-// re-materialize the literal into every accumulator).
-__device__ __forceinline__ v16i score_bias() {
-    v16i b;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) b[e] = kSBias;
-    asm volatile("" : "+v"(b));
-    return b;
-}
-
-// The QK step of one 32-key sub-tile t of a staged tile (biased int32
-// scores; bias = score_bias()).  Shared by the attention kernel and the debug
-// tile kernel.
+// The QK step of one 32-key sub-tile t of a staged tile (int32 scores).
+// Shared by the attention kernel and the debug tile kernel.
 template <int D>
-__device__ __forceinline__ v16i qk_subtile_i8(uint8_t* stage, const QFrag<D, false>& q, int t,
-                                              int lane, const v16i& bias) {
-    static_assert(D <= 256, "biased INT8 scores need |S| < 2^22");
+__device__ __forceinline__ v16i qk_subtile_i8(uint8_t* stage, const QFrag<D, false>& q, int t, int lane) {
+    static_assert(D <= 1024, "int32 scores exact in fp32 need |S| < 2^24");
     const int half = lane >> 5;
     const int r = 32 * t + kappa(lane & 31);
     v4i kf[D / 32];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) kf[c] = *(const v4i*)k_lds_addr<D, false>(stage, r, 2 * c + half);
-    v16i acc = mfma_i8_32x32x32(kf[0], q.f[0], bias);
+    v16i acc = mfma_i8_32x32x32(kf[0], q.f[0], v16i{0});
 #pragma unroll
     for (int c = 1; c < D / 32; ++c) acc = mfma_i8_32x32x32(kf[c], q.f[c], acc);
     return acc;
@@ -266,12 +288,11 @@ template <int D, bool MX>
 using SAccT = typename std::conditional<MX, v16f, v16i>::type;
 
 template <int D, bool MX>
-__device__ __forceinline__ SAccT<D, MX> qk_subtile(uint8_t* stage, const QFrag<D, MX>& q, int t,
-                                                   int lane, const v16i& bias) {
+__device__ __forceinline__ SAccT<D, MX> qk_subtile(uint8_t* stage, const QFrag<D, MX>& q, int t, int lane) {
     if constexpr (MX)
         return qk_subtile_mx<D>(stage, q, t, lane);
     else
-        return qk_subtile_i8<D>(stage, q, t, lane, bias);
+        return qk_subtile_i8<D>(stage, q, t, lane);
 }
 
 // O^T += V^T P^T for one staged 64-key tile.  A operand: V^T row (channel
@@ -360,8 +381,11 @@ __device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&
     for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, red[w]);
     amax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax)));   // uniform
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    // adding 1.5 * 2^23 rounds to the nearest integer (ties to even) and leaves
+    // it in the low bits of the float
+    constexpr float kRne = 12582912.0f;
     auto code = [&](float x) {   // float bits whose low byte is the code
-        return __float_as_uint(fminf(127.0f, fmaxf(-127.0f, x * inv)) + kSBiasF);
+        return __float_as_uint(fminf(127.0f, fmaxf(-127.0f, x * inv)) + kRne);
     };
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -520,8 +544,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // KV ring before any tile is copied there (32 KB of the ring's 36.75 KB).
     if constexpr (QF && MX) mx_fused_qfrag(qf, a, qh, b, h, qrow, smem);
     // tiles 0 and 1 in flight before the loop; tile j + 2 is issued in step j
-    Dma::issue(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane);
-    if (ntiles > 1) Dma::issue(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane);
+    const typename Dma::LaneOffsets dma_lane = Dma::lane_offsets(Lkp, wave, lane);
+    Dma::issue4(stage_of(0), krs, ksrs, vrs, Lkp, 0, wave, lane, dma_lane);
+    if (ntiles > 1) Dma::issue4(stage_of(1), krs, ksrs, vrs, Lkp, 1, wave, lane, dma_lane);
 
     float q_s = 0.0f;
     if constexpr (QF && MX) {
@@ -541,12 +566,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const float* kscale_f = MX ? nullptr : (const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block);
     const __attribute__((address_space(4))) float* kscale_c =
         (const __attribute__((address_space(4))) float*)kscale_f;
+    // K scale block of tile kt: kt * kBN / k_block, a shift (k_block is 64 or
+    // 128; a division here cost ~20 scalar instructions per tile)
+    const int kshift = __builtin_amdgcn_readfirstlane(a.k_block == 2 * kBN ? 1 : 0);
     auto tile_c = [&](int kt) -> float {
         if constexpr (MX) return alpha;
-        else return (q_s * kscale_c[kt * kBN / a.k_block]) * alpha;
+        else return (q_s * kscale_c[kt >> kshift]) * alpha;
     };
 
-    const v16i sbias = MX ? v16i{0} : score_bias();
     v16f O[kDB];
 #pragma unroll
     for (int i = 0; i < kDB; ++i) O[i] = v16f{0};
@@ -571,7 +598,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             dma_barrier<kDma>();
         else
             dma_barrier<0>();
-        if (j + 2 < ntiles) Dma::issue(stage2, krs, ksrs, vrs, Lkp, j + 2, wave, lane);
+        if (j + 2 < ntiles) Dma::issue4(stage2, krs, ksrs, vrs, Lkp, j + 2, wave, lane, dma_lane);
         const float c = tile_c(j);
         const int key0 = j * kBN;
 
@@ -595,7 +622,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         // S: element (t, e) is key key0 + 32 t + 16 half + e of query qrow
         SAcc S[kNT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) S[t] = qk_subtile<D, MX>(stage, qf, t, lane, sbias);
+        for (int t = 0; t < kNT; ++t) S[t] = qk_subtile<D, MX>(stage, qf, t, lane);
 
         // row max (on the integer scores for INT8: rounding is monotone)
         float tmax = -INFINITY;
@@ -728,12 +755,12 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t* q, const int8_t* 
     load_qfrag<D, false>(qf, qbase, nullptr, q0 + 32 * qg + col, lane);
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        const v16i s = qk_subtile_i8<D>(stage, qf, t, lane, score_bias());
+        const v16i s = qk_subtile_i8<D>(stage, qf, t, lane);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int key = kBN * kg + 32 * t + 16 * half + e;   // relative to k0
             const int qq = 32 * qg + col;                         // relative to q0
-            out[((int64_t)bh * nq + qq) * nk + key] = s[e] - kSBias;
+            out[((int64_t)bh * nq + qq) * nk + key] = s[e];
         }
     }
 }
