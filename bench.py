@@ -20,6 +20,11 @@ line:
                  LLM-prefill: one warm-up and three timed runs each, median
   extra        = the same measurements for LLM-prefill (causal) and the MXFP4
                  video-DiT path, and the paged FP8 / MXFP4 decodes (HBM GB/s).
+
+--only PART runs one part alone (video_dit, video_dit_mxfp4, llm_prefill,
+paged_decode, paged_decode_mxfp4) and prints its result: the per-workload
+rocprofv3 --pmc runs behind profiles/traffic.json use it, so each run holds
+one workload's launches.
 """
 from __future__ import annotations
 
@@ -60,6 +65,13 @@ def _traffic(kernel_key, src_names):
     if t.get("src_hash") != _src_hash(*src_names):
         return None
     return t.get("bytes_per_launch")
+
+
+def _decode_traffic(label):
+    """HBM bytes of one decode call: the decode kernel's and the merge's."""
+    src = ["decode.hip", "sage_device.hpp"]
+    d, m = _traffic(f"k_paged_decode@{label}", src), _traffic(f"k_decode_merge@{label}", src)
+    return d + m if d is not None and m is not None else None
 
 
 def _events_time(fn, reps, stream):
@@ -183,7 +195,7 @@ def prefill_bench(wname, steps, warmup, dev, time_unfused=False, fused_q=True):
     src = ["attn_fwd.hip", "sage_device.hpp"]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": _traffic(f"attn_fwd_{wname}", src)}
+            "traffic": _traffic(f"k_attn_fwd@{wname}", src)}
     res = {"value": round(literal / t_step / 1e12, 2), "unit": "TOPS", "fused_q": fused_q,
            "ms_per_step": round(t_step * 1e3, 4),
            "ms_per_step_hip_graph": round(t_step_graph * 1e3, 4),
@@ -274,8 +286,7 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
             "kv_pools_rotated": pools,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": _traffic("paged_decode_mxfp4" if mx else "paged_decode",
-                                             ["decode.hip", "sage_device.hpp"])}}
+                         "traffic": _decode_traffic("paged_decode_mxfp4" if mx else "paged_decode")}}
 
 
 def cpu_baseline(target_run_s=1.5):
@@ -349,6 +360,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--only", choices=["video_dit", "video_dit_mxfp4", "llm_prefill", "paged_decode",
+                                       "paged_decode_mxfp4"], help="run one part alone (profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -358,6 +371,13 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
+    if args.only:
+        if args.only.startswith("paged_decode"):
+            r = decode_bench(args.steps, args.warmup, dev, mx=args.only.endswith("mxfp4"))
+        else:
+            _, r = prefill_bench(args.only, args.steps, args.warmup, dev)
+        print(json.dumps({"part": args.only, **r}), flush=True)
+        return
     w, r = prefill_bench(HEADLINE, args.steps, args.warmup, dev)
     extra = {"attn_kernel_us": r["attn_kernel_us"],
              "attn_kernel_tops_literal": r["attn_kernel_tops_literal"],

@@ -3,12 +3,19 @@
 stats   <run_results.db> <out.txt> <command...>
     Per-kernel call count, average and total duration from a
     `rocprofv3 --kernel-trace --stats` run (table top_kernels).
-traffic <fetch_dir> <write_dir> <cal_fetch_dir> <cal_write_dir> <copy_bytes> <out.json>
-    Per-launch FETCH_SIZE / WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc
-    -f csv) of the library's kernels, scaled by the copy calibration
-    (known bytes / counter reading of a plain copy of copy_bytes), keyed by
-    kernel and workload, with the hash of the kernel's source files so a
-    reader can tell when the numbers no longer describe the code.
+traffic <out.json> <copy_bytes> <copy_rd_dir>,<copy_wr_dir> <label>=<rd_dir>,<wr_dir> ...
+    HBM bytes per launch of the library's kernels from the L2-to-memory
+    request counters, read directly: bytes read = 32 TCC_EA0_RDREQ_32B +
+    64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B, bytes written =
+    64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) (the
+    first pass per label collects the four read counters, the second the
+    two write counters; rocprofv3 --pmc -f csv).  No scale factor is
+    applied: the copy run (copy_bytes read and written by one plain device
+    copy, see `copy`) is reported beside them as a check of the formulas.
+    Entries are keyed "<kernel>@<label>" and carry the hash of the kernel's
+    source files, so a reader can tell when they no longer describe the code.
+copy <bytes>
+    Three device-to-device copies of <bytes> (the check run of `traffic`).
 counters <kernel fragment> <MFMA instructions per wave-step> <out.txt> <label=pass_dir[,pass_dir...]>...
     SQ / GRBM counters of one kernel (rocprofv3 --pmc passes over the same
     command, one directory per pass) per workload label, as per-wave-step
@@ -25,15 +32,31 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "quantized_attention_block_amd", "csrc")
 
-# kernel-name fragment -> (traffic key, source files it is built from)
-KERNELS = {
-    "k_attn_fwd<128, false, true>": ("attn_fwd_llm_prefill", ["attn_fwd.hip", "sage_device.hpp"]),
-    "k_paged_decode<128, false>": ("paged_decode", ["decode.hip", "sage_device.hpp"]),
-    "k_paged_decode<128, true>": ("paged_decode_mxfp4", ["decode.hip", "sage_device.hpp"]),
-    "k_decode_merge": ("decode_merge", ["decode.hip", "sage_device.hpp"]),
-    "k_quant_qk_fused<128, true>": ("quant_qk_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
-    "k_quant_v_fused<128, true>": ("quant_v_llm_prefill", ["quantize.hip", "sage_device.hpp"]),
+# library kernel (base name) -> the source files it is built from
+KERNEL_SOURCES = {
+    "k_attn_fwd": ["attn_fwd.hip", "sage_device.hpp"],
+    "k_paged_decode": ["decode.hip", "sage_device.hpp"],
+    "k_decode_merge": ["decode.hip", "sage_device.hpp"],
+    "k_quant_qk_fused": ["quantize.hip", "sage_device.hpp"],
+    "k_quant_v_fused": ["quantize.hip", "sage_device.hpp"],
+    "k_quant_mxfp4": ["quantize.hip", "sage_device.hpp"],
+    "k_quant_int8": ["quantize.hip", "sage_device.hpp"],
+    "k_mean_partial": ["quantize.hip", "sage_device.hpp"],
+    "k_v_amax": ["quantize.hip", "sage_device.hpp"],
+    "k_v_quant": ["quantize.hip", "sage_device.hpp"],
 }
+# how the runs behind a traffic summary are taken (from /tmp, TMPDIR=/tmp)
+COLLECTION = {
+    "read_pass": "rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum "
+                 "TCC_EA0_RDREQ_128B_sum -d <dir> -o run --output-format csv -- python bench.py --only <label> "
+                 "--steps 2 --warmup 1",
+    "write_pass": "rocprofv3 --pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum -d <dir> -o run --output-format csv "
+                  "-- python bench.py --only <label> --steps 2 --warmup 1",
+    "copy_passes": "the same two passes over: python quantized_attention_block_amd/rocprof_summary.py copy 268435456",
+    "summary": "python quantized_attention_block_amd/rocprof_summary.py traffic profiles/traffic.json 268435456 "
+               "<copy_rd>,<copy_wr> <label>=<rd>,<wr> ...",
+}
+READ_COUNTERS = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64, "TCC_EA0_RDREQ_128B_sum": 128}
 
 
 def src_hash(names):
@@ -66,44 +89,73 @@ def stats(db, out, command):
                     f"{gx * gy * gz:>9} {wg:>5} {vg:>4} {ag:>4} {sg:>4} {lds:>6} {scr:>4}  {name[:120]}\n")
 
 
-def _pmc(d, counter):
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+def _pmc_rows(d):
+    """(kernel name, counter) -> per-dispatch values of every counter CSV under d."""
     vals = {}
-    for fn in files:
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(fn)):
-            if r["Counter_Name"] != counter:
-                continue
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     return vals
 
 
-def _avg_for(vals, frag):
-    got = [v for k, vs in vals.items() if frag in k for v in vs]
-    return (sum(got) / len(got), len(got)) if got else (None, 0)
+def _bytes(rd, wr, name):
+    """Average bytes read and written per dispatch of kernel `name` (None if absent)."""
+    reads = [rd.get((name, c)) for c in READ_COUNTERS]
+    wq, w64 = wr.get((name, "TCC_EA0_WRREQ_sum")), wr.get((name, "TCC_EA0_WRREQ_64B_sum"))
+    if any(v is None for v in reads) or wq is None or w64 is None:
+        return None
+    avg = lambda v: sum(v) / len(v)
+    rbytes = sum(avg(v) * size for v, size in zip(reads, READ_COUNTERS.values()))
+    wbytes = 64.0 * avg(w64) + 32.0 * (avg(wq) - avg(w64))
+    total_req = rd.get((name, "TCC_EA0_RDREQ_sum"))
+    sized_req = sum(avg(v) for v in reads)
+    return {"read_bytes": round(rbytes), "write_bytes": round(wbytes),
+            "bytes_per_launch": round(rbytes + wbytes), "dispatches": [len(reads[0]), len(wq)],
+            # requests of a size none of the three counters sees (0 when they partition the total)
+            "unsized_read_requests": round(avg(total_req) - sized_req) if total_req else None}
 
 
-def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_bytes, out):
-    cf, cw = _pmc(cal_fetch_dir, "FETCH_SIZE"), _pmc(cal_write_dir, "WRITE_SIZE")
-    # the copy kernel is the only (or the largest) dispatch of the calibration run
-    cal_fetch = max(sum(v) / len(v) for v in cf.values()) * 1024.0
-    cal_write = max(sum(v) / len(v) for v in cw.values()) * 1024.0
-    f_scale, w_scale = copy_bytes / cal_fetch, copy_bytes / cal_write
-    fv, wv = _pmc(fetch_dir, "FETCH_SIZE"), _pmc(write_dir, "WRITE_SIZE")
-    res = {"_calibration": {"copy_bytes": copy_bytes, "fetch_counter_bytes": cal_fetch,
-                            "write_counter_bytes": cal_write, "fetch_scale": f_scale,
-                            "write_scale": w_scale}}
-    for frag, (key, srcs) in KERNELS.items():
-        fa, nf = _avg_for(fv, frag)
-        wa, nw = _avg_for(wv, frag)
-        if fa is None or wa is None:
-            continue
-        fb, wb = fa * 1024.0 * f_scale, wa * 1024.0 * w_scale
-        res[key] = {"kernel": frag, "dispatches": [nf, nw], "fetch_bytes": round(fb),
-                    "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
-                    "src_hash": src_hash(srcs)}
+def traffic(out, copy_bytes, copy_dirs, groups):
+    crd, cwr = (_pmc_rows(d) for d in copy_dirs.split(","))
+    names = {k[0] for k in crd}
+    copy = max((_bytes(crd, cwr, n) for n in names), key=lambda b: b["read_bytes"] if b else -1)
+    res = {"method": "direct TCC_EA0 request counters, no scale factor (see rocprof_summary.py)",
+           "collection": COLLECTION,
+           "copy_check": {"bytes_copied": copy_bytes, "read_bytes": copy["read_bytes"],
+                          "write_bytes": copy["write_bytes"],
+                          "read_ratio": round(copy["read_bytes"] / copy_bytes, 4),
+                          "write_ratio": round(copy["write_bytes"] / copy_bytes, 4)},
+           "kernels": {}}
+    for g in groups:
+        label, dirs = g.split("=", 1)
+        rd, wr = (_pmc_rows(d) for d in dirs.split(","))
+        for name in sorted({k[0] for k in rd}):
+            base = next((b for b in KERNEL_SOURCES if b + "<" in name or b + "(" in name), None)
+            if base is None:
+                continue
+            b = _bytes(rd, wr, name)
+            if b is None:
+                continue
+            key = f"{base}@{label}"
+            if key in res["kernels"]:   # several instances of one kernel: keep the busiest
+                if res["kernels"][key]["bytes_per_launch"] >= b["bytes_per_launch"]:
+                    continue
+            res["kernels"][key] = {"kernel": name[:160], **b, "src_hash": src_hash(KERNEL_SOURCES[base])}
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
+
+
+def copy(nbytes):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {nbytes} bytes 3 times", flush=True)
 
 
 def counters(frag, mfma_per_step, out, groups):
@@ -147,6 +199,8 @@ if __name__ == "__main__":
     elif sys.argv[1] == "counters":
         counters(sys.argv[2], int(sys.argv[3]), sys.argv[4], sys.argv[5:])
     elif sys.argv[1] == "traffic":
-        traffic(*sys.argv[2:6], int(sys.argv[6]), sys.argv[7])
+        traffic(sys.argv[2], int(sys.argv[3]), sys.argv[4], sys.argv[5:])
+    elif sys.argv[1] == "copy":
+        copy(int(sys.argv[2]))
     else:
         raise SystemExit(__doc__)
