@@ -39,6 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 64;            // query rows per KV head (padded): 16 per wave
 constexpr int kTile = kDecodeTile;   // 256 keys per split
 constexpr int kD = 128;
+constexpr float kLog2Fp8Max = 8.807354922057604f;   // log2(448)
 // Partial row of one (sequence, KV head, split, query row): h[DD] as fp16,
 // then m, l and vmax as fp32, then 4 pad bytes (DD = 128 for D <= 128, else
 // 256).  h = O8 / (448 l) with O8 = sum P8 V8 (e4m3 codes): P8 <= 448 p and
@@ -156,6 +157,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     // length has arrived, one more round trip before the tile copies start.
     asm volatile("" ::"s"(a.q), "s"(a.q_sB), "s"(a.q_sM), "s"(a.q_sH), "s"(a.k_cache), "s"(a.v_cache),
                  "s"(a.k_scale), "s"(a.v_scale), "s"(a.partials));
+    // (split, sequence x KV head): the splits of a sequence are dispatched
+    // together (numbering the blocks split-major, or the window's first tile
+    // last, measured 1.4 us slower per call)
     const int s = blockIdx.x, bk = blockIdx.y;
     const int b = bk / a.Hkv, hk = bk % a.Hkv;
     // A page table of at most 64 pages per sequence is read whole, one entry
@@ -227,6 +231,11 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     const int T = lo_b / kTile + s;
     if (T > (ctx - 1) / kTile) return;            // this sequence has fewer splits
     const int t0 = T * kTile, last = ctx - 1;
+    // A 128-key half of the tile with no key in [lo_b, ctx) (the first tile
+    // of a window, the last of a context) is not read from memory: its copies
+    // take offsets past the page's resource, which land zeros in LDS (every
+    // key of it is masked, and zero V codes keep P V finite).
+    const bool live[2] = {t0 + kTile / 2 > lo_b, t0 + kTile / 2 < ctx};
 
     // K tile and V tile, kPlanes planes of [256 keys][128 B] (V^T: [page-block]
     // [128 d][PW keys]); MX uses the first half of each plane.  (Declared
@@ -299,19 +308,22 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = wave + 4 * j;
+            // K keys [16 i, +16) (and a V^T page-block of at most 128 keys)
+            // lie in half j / 2; a 256-key V^T page-block spans both
+            const bool k_live = live[j >> 1], v_live = PW == 256 ? (live[0] || live[1]) : k_live;
             const int pg = pid[j >> (kLgn - 2)];   // page-block 16 i / PW (PW >= 64)
             // K: keys [16 i, +16) of the tile, 4 chunks each
             const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
             const int key = 16 * i + (lane >> 2);
             const int kc = (lane & 3) ^ dk_swz_mx(key);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + 1024 * i, 16,
-                                                     (koff + key % PW) * kRowB + 16 * kc, 0, 0, 0);
+                                                     k_live ? (koff + key % PW) * kRowB + 16 * kc : kpage, 0, 0, 0);
             // V^T: rows d of page-block (i >> (log2 n + 1)), chunks c
             const int within = ((64 * i) & ((128 << kVLgn) - 1)) + lane;
             const int d = within >> kVLgn, c = (within & ((1 << kVLgn) - 1)) ^ dv_swz<kVLgn>(d);
             const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16, d * (a.page / 2) + koff / 2 + 16 * c,
-                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + 1024 * i, 16,
+                                                     v_live ? d * (a.page / 2) + koff / 2 + 16 * c : kpage, 0, 0, 0);
         }
     } else {
 #pragma unroll
@@ -319,6 +331,10 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = wave + 4 * j;
+            // keys [8 i, +8) of K (and of a plain V, and of a V^T page-block of
+            // at most 128 keys) lie in half j / 4; a 256-key V^T page-block
+            // spans both, copied when either is live
+            const bool k_live = live[j >> 2], v_live = PW == 256 ? (live[0] || live[1]) : k_live;
             int pg;
             if constexpr (PW == 16) pg = (wave & 2) ? pid[2 * j + 1] : pid[2 * j];
             else pg = pid[j >> (kLgn - 1)];
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             const int kc = (lane & 7) ^ dk_swz(key);
             const int kch = 128 * p + 16 * kc;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kt_s + p * kPlaneB + 1024 * i, 16,
-                                                     kch < a.D ? (koff + key % PW) * a.D + kch : kpage,
+                                                     k_live && kch < a.D ? (koff + key % PW) * a.D + kch : kpage,
                                                      0, 0, 0);
             const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + ((int64_t)pg * a.Hkv + hk) * kpage, kpage);
             if constexpr (VT) {
@@ -337,13 +353,14 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
                 const int d = within >> kLgn, c = (within & ((1 << kLgn) - 1)) ^ dv_swz<kLgn>(d);
                 const int dg = 128 * p + d;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + p * kPlaneB + 1024 * i, 16,
-                                                         dg < a.D ? dg * a.page + koff + 16 * c : kpage, 0, 0, 0);
+                                                         v_live && dg < a.D ? dg * a.page + koff + 16 * c : kpage,
+                                                         0, 0, 0);
             } else {
                 // plain V: laid out like K, with the PV read swizzle
                 const int vc = (lane & 7) ^ pv_swz(key);
                 const int vch = 128 * p + 16 * vc;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vt_s + p * kPlaneB + 1024 * i, 16,
-                                                         vch < a.D ? (koff + key % PW) * a.D + vch : kpage,
+                                                         v_live && vch < a.D ? (koff + key % PW) * a.D + vch : kpage,
                                                          0, 0, 0);
             }
         }
@@ -353,17 +370,20 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. Q row -> e4m3 with a per-row scale (the B operand of QK), or the
-    // given e4m3 codes and scale ------------------------------------------------
+    // given e4m3 codes and scale.  A negative given scale is moved into the
+    // codes' signs, so the row's score factor below is never negative.
     v8i qf[kPlanes];
     float qs;
     if (a.q_kind == kQueryE4M3) {
+        const uint32_t flip = r < R && qs_given < 0.0f ? 0x80808080u : 0u;
 #pragma unroll
         for (int p = 0; p < kPlanes; ++p) {
             const uint4 lo = r < R ? qraw[p][0] : make_uint4(0, 0, 0, 0);
             const uint4 hi = r < R ? qraw[p][1] : make_uint4(0, 0, 0, 0);
-            qf[p] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            qf[p] = v8i{(int)(lo.x ^ flip), (int)(lo.y ^ flip), (int)(lo.z ^ flip), (int)(lo.w ^ flip),
+                        (int)(hi.x ^ flip), (int)(hi.y ^ flip), (int)(hi.z ^ flip), (int)(hi.w ^ flip)};
         }
-        qs = r < R ? qs_given : 0.0f;
+        qs = r < R ? fabsf(qs_given) : 0.0f;
     } else {
         const bool f16 = a.q_kind == kQueryF16;
         float x[kPlanes][32];
@@ -403,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         kss[tid] = ks;
         vss[tid] = vs;
     } else {
-        kss[tid] = kpos_s < ctx ? ks : 0.0f;
+        kss[tid] = kpos_s < ctx ? ks * alpha : 0.0f;   // alpha = sm_scale log2(e) folded in
         vss[tid] = kpos_s < ctx ? vs : 0.0f;
     }
     __syncthreads();   // every wave's copies have landed (vmcnt(0)) and the scales are in LDS
@@ -466,9 +486,16 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             }
         }
 
-    // ---- 6. masked scores, row max and sum over the 4 lanes of the row -------
+    // ---- 6. scores x = t c with t = S k_scale alpha (the K scale and alpha
+    // are in kss; MX: t = S, the K scale is inside S) and the row factor
+    // c = q_scale (MX: q_scale alpha), kept positive, so the row max of x is
+    // c times that of t; masked keys get t = -inf.  Row max and sum over the
+    // 4 lanes of the row.
     const int pos = ctx - a.MTP + mt;
     const int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    // (a zero row has t = 0 on every key: any c > 0 gives it x = 0, and
+    // -inf * c stays -inf)
+    const float cr = fmaxf(MX ? qs * alpha : qs, 1.0e-30f);
     // A tile whose every key is visible to every query row (all but the first
     // and last tiles of a window) skips the per-key mask; rows past R are
     // padding whose results are never stored.
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float xv = MX ? (S[g][m][i] * qs) * alpha : ((S[g][m][i] * qs) * kk[i]) * alpha;
+                    const float xv = MX ? S[g][m][i] : S[g][m][i] * kk[i];
                     if constexpr (ALL) {
                         S[g][m][i] = xv;
                     } else {
@@ -507,10 +534,15 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         scores(std::false_type{});
     rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
     rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-    const float Mb = rmax == -INFINITY ? 0.0f : rmax;
-    // p = 2^(x - m); P' = p * v_scale -> e4m3 with the tile's vmax, packed as
-    // the B operand of PV (byte 4 m + i of group g = key kl0 + 4 m + i)
-    const float pinv = vmax > 0.0f ? kFp8Max / vmax : 0.0f;
+    // the row max of x (-inf: no visible key in this tile)
+    const float M = rmax == -INFINITY ? -INFINITY : rmax * cr;
+    // p = 2^(x - M) and P' = p v_scale 448 / vmax -> e4m3 (MX: 448 p), packed
+    // as the B operand of PV (byte 4 m + i of group g = key kl0 + 4 m + i).
+    // The constant factor 448 / vmax is folded into the exponent, u =
+    // 2^(fma(t, c, -(M - log2(448 / vmax)))) = p 448 / vmax, so l = sum u
+    // vmax / 448 (with vmax = 0 every P' is 0 and u = p).
+    const float lp = MX ? kLog2Fp8Max : (vmax > 0.0f ? kLog2Fp8Max - __builtin_amdgcn_logf(vmax) : 0.0f);
+    const float Mo = (rmax == -INFINITY ? 0.0f : M) - lp;
     float ls = 0.0f;
     v8i pf[2];
 #pragma unroll
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
         const int kl0 = 128 * g + 32 * q4;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            float vv[4] = {1.0f, 1.0f, 1.0f, 1.0f};   // MX: P8 = e4m3(448 p), V's scales are in the MFMA
+            float vv[4] = {1.0f, 1.0f, 1.0f, 1.0f};   // MX: V's scales are in the MFMA
             if constexpr (!MX) {
                 const float4 v4 = *(const float4*)&vss[kl0 + 4 * m];
                 vv[0] = v4.x, vv[1] = v4.y, vv[2] = v4.z, vv[3] = v4.w;
@@ -526,9 +558,9 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             float pp[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(S[g][m][i] - Mb);
-                ls += p;
-                pp[i] = MX ? p * kFp8Max : (p * vv[i]) * pinv;
+                const float u = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g][m][i], cr, -Mo));
+                ls += u;
+                pp[i] = MX ? u : u * vv[i];
             }
             const uint32_t c0 = cvt_pk_fp8<false>(pp[0], pp[1], 0);
             pf[g][m] = (int)cvt_pk_fp8<true>(pp[2], pp[3], c0);
@@ -536,6 +568,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     }
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
+    ls = MX ? ls / kFp8Max : (vmax > 0.0f ? (ls * vmax) / kFp8Max : ls);
 
     // ---- 7. O^T = V^T P^T: element i of lane l of d-block db is channel
     // 16 db + 4 (l / 16) + i of query row r
@@ -622,7 +655,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             if (16 * db < a.D)
                 *(uint2*)(prow + 2 * (16 * db + 4 * q4)) =
                     make_uint2(pack_h2(hv(O[db][0]), hv(O[db][1])), pack_h2(hv(O[db][2]), hv(O[db][3])));
-        if (q4 == 0) *(float4*)(prow + 2 * DD) = make_float4(rmax, ls, vmax, 0.0f);
+        if (q4 == 0) *(float4*)(prow + 2 * DD) = make_float4(M, ls, vmax, 0.0f);
     }
 }
 
@@ -759,7 +792,7 @@ hipError_t decode_scratch(void** ptr) {
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const float alpha = a.sm_scale * kLog2e;
-    dim3 grid(a.num_splits, a.B * a.Hkv);
+    const dim3 grid(a.num_splits, a.B * a.Hkv);
     const int pw = a.page < kTile ? a.page : kTile;
     if (a.mx) {
         switch (pw) {
