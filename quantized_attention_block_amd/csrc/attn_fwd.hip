@@ -37,11 +37,11 @@
 //    B operand of the PV product O^T = V^T P^T (v_mfma_f32_32x32x64 e4m3), so
 //    P never leaves registers, and V^T (stored transposed, keys contiguous)
 //    is read in natural key order, two 16-byte LDS reads per operand.
-//  - INT8 scores leave the MFMA biased by 1.5 * 2^23 (the accumulator starts
-//    at that float's bit pattern), so fp32(S) is one exact subtraction.  Row
+//  - INT8 scores are exact int32; fp32(S) is one exact v_cvt_f32_i32.  Row
 //    max is taken on the integer scores (rounding is monotone, so
 //    max fp32(S c) = fp32(max S c)); the O/l rescale is skipped when no row of
-//    the wave changed its max; 448 is folded into the exp2 offset.
+//    the wave that has seen a key changed its max; 448 is folded into the
+//    exp2 offset.
 //  - Q may arrive as the caller's fp16/bf16 tensor instead of INT8 codes: the
 //    block's 128 rows are exactly one Q scale block, so the prologue quantizes
 //    them with the quantize kernels' arithmetic (codes and scale bit-identical)
@@ -640,7 +640,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             }
         }
         const float m_new = fmaxf(m, half_pair_max(tmax));
-        if (__any(m_new > m)) {   // online-softmax rescale, skipped when no row's max moved
+        // online-softmax rescale, skipped when no row's max moved; a row that
+        // has seen no key yet (m = -inf) holds O = 0 and l = 0, which the
+        // rescale by 0 leaves as they are, so its first max does not count
+        if (__any(m_new > m && m != -INFINITY)) {
             const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
             l *= sc;
 #pragma unroll

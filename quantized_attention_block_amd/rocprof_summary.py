@@ -158,11 +158,27 @@ def copy(nbytes):
     print(f"copied {nbytes} bytes 3 times", flush=True)
 
 
+# the passes behind a `counters` summary (one rocprofv3 run each, from /tmp)
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+    "SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_ANY SQ_LDS_IDX_ACTIVE",
+    "SQ_INSTS_SALU SQ_INSTS_SMEM SQ_INST_CYCLES_VMEM SQ_WAIT_ANY SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_SCA "
+    "SQ_INSTS_BRANCH SQ_ACTIVE_INST_FLAT",
+]
+
+
 def counters(frag, mfma_per_step, out, groups):
     n_xcd, n_simd = 8, 1024
     lines = ["# rocprofv3 --pmc counter summary of kernels matching '%s' (average per dispatch)" % frag,
              "# per wave-step = per wave and per KV tile (SQ_INSTS_MFMA / %d)" % mfma_per_step,
-             "# SQ_*_CYCLES and SQ_WAVE_CYCLES count quad-cycles; GRBM_GUI_ACTIVE is summed over XCDs"]
+             "# SQ_*_CYCLES and SQ_WAVE_CYCLES count quad-cycles; GRBM_GUI_ACTIVE is summed over XCDs",
+             "# passes (from /tmp, TMPDIR=/tmp; <label> = the workload):"]
+    lines += ["#   rocprofv3 --pmc %s -d <dir>/p%d -o run --output-format csv -- python bench.py --only <label> "
+              "--steps 2 --warmup 1" % (c, i + 1) for i, c in enumerate(COUNTER_PASSES)]
+    lines.append("# then: python quantized_attention_block_amd/rocprof_summary.py counters '%s' %d <out> "
+                 "<label>=<dir>/p1,<dir>/p2,<dir>/p3 ..." % (frag, mfma_per_step))
     for g in groups:
         label, dirs = g.split("=", 1)
         m = {}

@@ -1,9 +1,12 @@
 """Seeded synthetic workloads for quantized attention.
 
 This module only draws random numbers and lays them out; it holds none of the
-method's arithmetic (no quantization, no softmax, no attention).  Both the CPU
-oracle and the HIP path read the arrays it returns, so the two sides always see
-the same inputs.
+method's arithmetic (no softmax, no attention, none of the method's
+quantizers).  The one encoding it does is input synthesis: the FP8 decode
+cache is built from float draws with torch's float8_e4m3fn cast and a
+per-token amax / 448 scale, because a paged cache arrives already encoded
+(the MXFP4 cache is drawn directly as E2M1 codes and E8M0 exponents).  Both the CPU oracle and the HIP path read the
+arrays it returns, so the two sides always see the same inputs.
 
 Every tensor is drawn with ``numpy.random.default_rng([config_id, tensor_id])``
 (tensor ids: Q=0, K=1, V=2, K channel offset=3, outlier channels=4, pages=5),

@@ -42,6 +42,33 @@ def require_gpu():
 # then reproduce base-2 attention on the integer scores, written out below in
 # float64.
 
+def softmax_accumulation_bound(n):
+    """Bound on |out - exact| / max|v| for the GPU softmax-PV on dyadic inputs
+    (integer scores, power-of-two or unit scales, e4m3-exact values), where
+    every quantization step is exact and only fp32 arithmetic rounds:
+
+    * the row sum l adds n positive fp32 terms on the vector ALU
+      (round-to-nearest): relative error at most gamma(n, u) = n u / (1 - n u),
+      u = 2^-24, in any summation order;
+    * O = sum P8 V8 has exact products (e4m3 x e4m3 fits fp32) accumulated
+      by the MFMA, whose internal order and rounding are not documented:
+      bounded as if each of the n additions could lose a whole ulp
+      (truncation), gamma(n, 2u) sum |P8 V8| <= gamma(n, 2u) 448 l max|V8|
+      (P8 >= 0), that is gamma(n, 2u) max|v| after the division by l.  (With
+      round-to-nearest here too, the causal MXFP4 case at n = 160 measured
+      2.4e-5 of max|v|, above the 2.1e-5 that model allows.);
+    * each p = 2^(S c - m + log2 448) comes from the approximate hardware exp2
+      of a non-integer argument (log2 448 and the folded offset are rounded to
+      fp32): within 2^-19 relatively, enough for P8 = e4m3(448 p) to round to
+      its exact value, but it enters l;
+    * the epilogue's v_scale product, reciprocal and product: 3 u.
+    Together gamma(n, u) + gamma(n, 2u) + 2^-19 + 3 u (relative to max|v|),
+    n = the keys one fp32 sum runs over."""
+    u = 2.0 ** -24
+    gamma = lambda uu: n * uu / (1.0 - n * uu)
+    return gamma(u) + gamma(2.0 * u) + 2.0 ** -19 + 3.0 * u
+
+
 def base2_attention(x, v, causal):
     """sum_j 2^x_ij v_j / sum_j 2^x_ij over visible j (j <= i when causal)."""
     x = x.astype(np.float64)
