@@ -290,13 +290,21 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
 
 
 def cpu_baseline(target_run_s=1.5):
-    """The oracle as it stands, on bounded samples: for video-DiT and
-    LLM-prefill, one (b, h) head is quantized and a seeded sample of its query
-    rows is run through the quantization-emulating oracle, and the same rows
-    through the exact fp64 oracle.  The sample is sized to ~target_run_s per
-    run; one warm-up run, then three timed runs, median.  Throughput uses the
-    metric's formula per query row, 4 Lk D ops (LLM-prefill is causal, so
-    that counts each row's masked keys too, as the metric's formula does)."""
+    """The oracle as it stands, both forms (the quantization-emulating one and
+    the exact fp64 one), on every configuration: one warm-up run, then three
+    timed runs, median.
+
+    Prefill (tiny, LLM-prefill, video-DiT, video-DiT MXFP4): one (b, h) head is
+    quantized and a seeded sample of its query rows is run, sized to
+    ~target_run_s per run (tiny: all rows); throughput uses the metric's formula
+    per query row, 4 Lk D ops (LLM-prefill is causal, so that counts each row's
+    masked keys too, as the metric's formula does).  The MXFP4 emulation
+    includes the Hadamard rotation of the head; its exact oracle is the same
+    computation as video-DiT's (same tensors).
+
+    Decode (FP8 and MXFP4 caches): the whole workload (16 sequences), the exact
+    form on the decoded cache values; throughput in GB/s of the workload's
+    algorithmic bytes, as the decode's GPU line."""
     import numpy as np
     sys.path.insert(0, ROOT)
     import oracle
@@ -307,7 +315,13 @@ def cpu_baseline(target_run_s=1.5):
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
     results = {}
-    for wname in (HEADLINE, "llm_prefill"):
+
+    def timed(run):
+        run()   # warm-up
+        ts = [run() for _ in range(3)]
+        return statistics.median(ts), ts
+
+    for wname in ("tiny", "llm_prefill", HEADLINE, "video_dit_mxfp4"):
         w = wl.WORKLOADS[wname]
         print(f"bench: cpu baseline on {wname} ({cores} threads)", file=sys.stderr, flush=True)
         inp = wl.make_prefill(w, B=1, H=1)
@@ -318,38 +332,85 @@ def cpu_baseline(target_run_s=1.5):
             rng = np.random.default_rng(11)
 
             def rows_of(n):
-                ri = np.sort(rng.integers(0, w.Lq, n))
+                ri = np.sort(rng.integers(0, w.Lq, n)) if n < w.Lq else np.arange(w.Lq)
                 return np.stack([np.zeros_like(ri), np.zeros_like(ri), ri], 1)
 
             def run(rows):
                 t0 = time.perf_counter()
-                if kind == "emulated":
+                if kind == "exact":
+                    oracle.attn_exact(q, k, v, w.causal, w.sm_scale, rows=rows, nthreads=cores)
+                elif w.qk_mode == "mxfp4":
+                    oracle.prefill_mxfp4_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale, BN=64,
+                                                  rows=rows, nthreads=cores)
+                else:
                     oracle.prefill_int8_pipeline(q, k, v, causal=w.causal, sm_scale=w.sm_scale,
                                                  BN=64, rows=rows, nthreads=cores)
-                else:
-                    oracle.attn_exact(q, k, v, w.causal, w.sm_scale, rows=rows, nthreads=cores)
                 return time.perf_counter() - t0
 
-            # a fixed cost (the head's quantization) plus a per-row cost: two
-            # probes give both, then the sample is sized to ~target_run_s
-            t1, t2 = run(rows_of(4 * cores)), run(rows_of(36 * cores))
-            per_row = max((t2 - t1) / (32 * cores), 1e-7)
-            nrows = int(max(8 * cores, min(2_000_000, (target_run_s - min(t1, t2) / 2) / per_row)))
+            if w.Lq <= 4096 and wname == "tiny":
+                nrows = w.Lq
+            else:
+                # a fixed cost (the head's quantization) plus a per-row cost: two
+                # probes give both, then the sample is sized to ~target_run_s
+                t1, t2 = run(rows_of(4 * cores)), run(rows_of(36 * cores))
+                per_row = max((t2 - t1) / (32 * cores), 1e-7)
+                nrows = int(max(8 * cores, min(2_000_000, (target_run_s - min(t1, t2) / 2) / per_row)))
             rows = rows_of(nrows)
-            run(rows)   # warm-up
-            ts = [run(rows) for _ in range(3)]
-            t = statistics.median(ts)
+            nrows = len(rows)
+            t, ts = timed(lambda: run(rows))
             results[f"{wname}_{kind}"] = {
                 "value": round(4.0 * nrows * w.Lk * w.D / t / 1e12, 6), "unit": "TOPS",
                 "seconds_median": round(t, 3), "seconds_runs": [round(x, 3) for x in ts],
-                "rows": nrows}
+                "rows": nrows, "of_rows": w.Lq * w.B * w.H}
+
+    w = wl.WORKLOADS["paged_decode"]
+    keys = min(w.ctx, w.window + w.mtp - 1)
+    for mx in (False, True):
+        name = "paged_decode_mxfp4" if mx else "paged_decode"
+        print(f"bench: cpu baseline on {name} ({cores} threads)", file=sys.stderr, flush=True)
+        per_key = (w.D + w.D // 16) if mx else (2 * w.D + 8)
+        alg_bytes = w.batch * w.hkv * keys * per_key + 2 * (w.batch * w.mtp * w.hq * w.D * 2)
+        common = dict(window=w.window, sm_scale=w.sm_scale, nthreads=cores)
+        if mx:
+            d = wl.make_decode_mx(w)
+            qf = d.q.float().numpy()
+            args = [d.k_codes.numpy(), d.k_e8.numpy(), d.v_codes.numpy(), d.v_e8.numpy(),
+                    d.page_table.numpy(), d.ctx_lens.numpy()]
+            # exact form: the decoded E2M1 x 2^(e - 127) values, V back to [P, Hkv, page, D]
+            e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+            kf = e2m1[args[0]] * np.repeat(np.ldexp(1.0, args[1].astype(np.int32) - 127), 32, -1)
+            vf = (e2m1[args[2]] * np.repeat(np.ldexp(1.0, args[3].astype(np.int32) - 127), 32, -1))
+            vf = np.ascontiguousarray(vf.transpose(0, 1, 3, 2)).astype(np.float32)
+            ones = np.ones(kf.shape[:3], np.float32)
+            emul = lambda: oracle.paged_decode_mx(qf, *args, **common)
+            exact = lambda: oracle.paged_decode(qf, kf.astype(np.float32), vf, ones, ones, args[4], args[5],
+                                                quant=False, **common)
+        else:
+            d = wl.make_decode(w)
+            qf = d.q.float().numpy()
+            kc, vc, ks, vs = d.k_cache.numpy(), d.v_cache.numpy(), d.k_scale.numpy(), d.v_scale.numpy()
+            pt, cl = d.page_table.numpy(), d.ctx_lens.numpy()
+            kf = oracle.e4m3_decode_array(kc).astype(np.float32)
+            vf = oracle.e4m3_decode_array(vc).astype(np.float32)
+            emul = lambda: oracle.paged_decode(qf, kc, vc, ks, vs, pt, cl, **common)
+            exact = lambda: oracle.paged_decode(qf, kf, vf, ks, vs, pt, cl, quant=False, **common)
+        for kind, fn in (("emulated", emul), ("exact", exact)):
+            def run():
+                t0 = time.perf_counter()
+                fn()
+                return time.perf_counter() - t0
+            t, ts = timed(run)
+            results[f"{name}_{kind}"] = {
+                "value": round(alg_bytes / t / 1e9, 3), "unit": "GB/s", "seconds_median": round(t, 4),
+                "seconds_runs": [round(x, 4) for x in ts], "sequences": w.batch}
     head = results[f"{HEADLINE}_emulated"]
     w = wl.WORKLOADS[HEADLINE]
     return {"value": head["value"], "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": (f"{head['rows']} seeded query rows of one (b,h) head of {HEADLINE} "
                        f"(Lk={w.Lk}, D={w.D}): K mean + INT8/e4m3 quantization of that head + "
                        f"step-by-step emulation of those rows, C++ threads={cores}; median of 3 "
-                       f"timed runs after 1 warm-up; 4 Lk D ops per row"),
+                       f"timed runs after 1 warm-up; 4 Lk D ops per row.  `runs` holds both oracles "
+                       f"on every configuration"),
             "runs": results}
 
 
