@@ -11,7 +11,7 @@ namespace sage {
 hipError_t launch_k_mean_partial(const HalfView&, int, int, int, int, double*, hipStream_t) {
     return hipErrorNoDevice;
 }
-hipError_t launch_k_mean_final(const double*, int, int, int, int, float*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_k_mean_final(double*, int, int, int, int, float*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_quant_qk_int8(const HalfView&, const HalfView&, int, int, int, int, int, int, bool, double*,
                                 uint64_t*, float*, int8_t*, float*, int8_t*, float*, hipStream_t) {
     return hipErrorNoDevice;

@@ -98,12 +98,48 @@ __global__ __launch_bounds__(kThreads) void k_mean_partial(HalfView k, int H, in
     }
 }
 
+// Finish of one head's channel statistics: thread d folds channel d of the
+// head's nchunk chunk partials in chunk order.  The loads go out kFinishBatch
+// at a time, all in flight together, ahead of the (ordered) folds: one at a
+// time, the loop waited one memory latency per chunk (128 chunks: ~36 us).
+constexpr int kFinishBatch = 16;
+
+// mu = fp32(sum / L) in binary64, chunk order.  Written to mu (if any) and,
+// as a binary64 value, over chunk 0's partial, where k_quant_int8 reads it.
 template <int D>
-__global__ void k_mean_final(const double* partial, int nchunk, int L, float* mu) {
+__global__ void k_mean_final(double* partial, int nchunk, int L, float* mu) {
     const int bh = blockIdx.x, d = threadIdx.x;
+    double* col = partial + (int64_t)bh * nchunk * D + d;
     double s = 0.0;
-    for (int c = 0; c < nchunk; ++c) s += partial[((int64_t)bh * nchunk + c) * D + d];
-    mu[(int64_t)bh * D + d] = L > 0 ? (float)(s / (double)L) : 0.0f;
+    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch) {
+        double v[kFinishBatch];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0;
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u)
+            if (c0 + u < nchunk) s += v[u];
+    }
+    const float m = L > 0 ? (float)(s / (double)L) : 0.0f;
+    if (mu) mu[(int64_t)bh * D + d] = m;
+    col[0] = (double)m;   // this thread has read every chunk of its own column above
+}
+
+// V: amax = max over the chunk partials (order-free), written over chunk 0's
+// partial, where k_v_quant reads it, and scale = amax / 448.
+template <int D>
+__global__ void k_v_amax_final(float* partial, int nchunk, float* v_scale) {
+    const int bh = blockIdx.x, d = threadIdx.x;
+    float* col = partial + (int64_t)bh * nchunk * D + d;
+    float a = 0.0f;
+    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch) {
+        float v[kFinishBatch];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u) a = fmaxf(a, v[u]);
+    }
+    v_scale[(int64_t)bh * D + d] = a / kFp8Max;
+    col[0] = a;
 }
 
 // ---- INT8 block quantization -------------------------------------------------
@@ -113,9 +149,9 @@ __global__ void k_mean_final(const double* partial, int nchunk, int L, float* mu
 // and its code stores are 16-byte accesses.  Per quantization block: amax over
 // the valid rows (K: of fp32(K - mu)), scale = amax / 127,
 // codes = clamp(rne(x * (127 / amax)), -127, 127); padded rows get code 0.
-// K blocks first finish the channel mean from the binary64 partial sums
-// (summed in chunk order, divided by L in binary64, rounded to fp32); the
-// first K block of each head also writes it out.
+// K blocks take the channel mean that k_mean_final left over chunk 0 of the
+// binary64 partials (summed in chunk order, divided by L in binary64, rounded
+// to fp32).
 template <int D>
 struct Rows16 {
     static constexpr int kLanesPerRow = D / 16;
@@ -135,9 +171,8 @@ __device__ __forceinline__ void unpack8(const uint4& u, bool bf16, float out[8])
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k, int H, int Lq,
                                                          int Lk, int k_block, int nqb,
-                                                         const double* mean_partial, int nchunk,
-                                                         float* mu_out, int8_t* q_out,
-                                                         float* q_scale, int8_t* k_out,
+                                                         const double* mean_final, int nchunk,
+                                                         int8_t* q_out, float* q_scale, int8_t* k_out,
                                                          float* k_scale) {
     using G = Rows16<D>;
     const bool isq = (int)blockIdx.y < nqb;
@@ -167,16 +202,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
 
     __shared__ float mu_s[D];
     __shared__ float red[kThreads / 64][2];
-    const bool smooth = !isq && mean_partial != nullptr;
+    const bool smooth = !isq && mean_final != nullptr;
     if (smooth) {
-        if (threadIdx.x < D) {
-            const int d = threadIdx.x;
-            double acc = 0.0;
-            for (int c = 0; c < nchunk; ++c) acc += mean_partial[((int64_t)bh * nchunk + c) * D + d];
-            const float m = L > 0 ? (float)(acc / (double)L) : 0.0f;
-            mu_s[d] = m;
-            if (blk == 0 && mu_out) mu_out[(int64_t)bh * D + d] = m;
-        }
+        if (threadIdx.x < D) mu_s[threadIdx.x] = (float)mean_final[(int64_t)bh * nchunk * D + threadIdx.x];
         __syncthreads();
     }
     float mu16[16];
@@ -286,16 +314,14 @@ __global__ __launch_bounds__(kThreads) void k_v_amax(HalfView v, int H, int L, i
     }
 }
 
-// Pass 2: one block per 128 keys of one (b, h).  amax[d] = max over the chunk
-// partials; codes = e4m3(v * (448 / amax[d])), scale = amax / 448 (written by
-// the first block of each head).  A thread converts 4 keys x 8 channels and
+// Pass 2: one block per 128 keys of one (b, h).  amax[d] from
+// k_v_amax_final (chunk 0 of the partials); codes = e4m3(v * (448 / amax[d])).  A thread converts 4 keys x 8 channels and
 // packs, per channel, the 4 keys' codes into one dword, stored into an LDS
 // tile [D][128 keys] whose 16-byte chunks are XOR-swizzled by row; the tile is
 // then written out as 128-byte V^T rows with 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, int nchunk,
-                                                      const float* partial, uint8_t* v_out,
-                                                      float* v_scale) {
+                                                      const float* partial, uint8_t* v_out) {
     constexpr int kKeys = 128;
     constexpr int kGroups = D / 8;                         // 8-channel groups (16 or 8)
     constexpr int kKeyGroups = kThreads / kGroups;         // 4-key groups per pass (16 or 32)
@@ -320,11 +346,8 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
     __shared__ float inv_s[D];
     __shared__ __attribute__((aligned(16))) uint32_t tile[D * kKeys / 4];
     if (threadIdx.x < D) {
-        const int d = threadIdx.x;
-        float a = 0.0f;
-        for (int c = 0; c < nchunk; ++c) a = fmaxf(a, partial[((int64_t)bh * nchunk + c) * D + d]);
-        inv_s[d] = a > 0.0f ? kFp8Max / a : 0.0f;
-        if (blockIdx.y == 0) v_scale[(int64_t)bh * D + d] = a / kFp8Max;
+        const float a = partial[(int64_t)bh * nchunk * D + threadIdx.x];   // k_v_amax_final's result
+        inv_s[threadIdx.x] = a > 0.0f ? kFp8Max / a : 0.0f;
     }
     __syncthreads();
     float inv8[8];
@@ -1024,7 +1047,7 @@ hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, 
     return hipGetLastError();
 }
 
-hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D, float* mu,
+hipError_t launch_k_mean_final(double* partial, int B, int H, int L, int D, float* mu,
                                hipStream_t stream) {
     const int nchunk = mean_chunks(L);
     if (D == 128)
@@ -1052,12 +1075,13 @@ hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int
         }
     }
     if (smooth) {
-        const hipError_t e = launch_k_mean_partial(k, B, H, Lk, D, mean_partial, stream);
+        hipError_t e = launch_k_mean_partial(k, B, H, Lk, D, mean_partial, stream);
+        if (e == hipSuccess) e = launch_k_mean_final(mean_partial, B, H, Lk, D, mu_out, stream);
         if (e != hipSuccess) return e;
     }
     auto quant = D == 128 ? k_quant_int8<128> : k_quant_int8<64>;
     quant<<<dim3(BH, nqb + nkb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb,
-                                                        smooth ? mean_partial : nullptr, nchunk, mu_out,
+                                                        smooth ? mean_partial : nullptr, nchunk,
                                                         q_out, q_scale, k_out, k_scale);
     return hipGetLastError();
 }
@@ -1076,10 +1100,12 @@ hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float*
     dim3 g1(BH, nchunk), g2(BH, pad128(Lk) / 128);
     if (D == 128) {
         k_v_amax<128><<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial);
-        k_v_quant<128><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out, v_scale);
+        k_v_amax_final<128><<<BH, 128, 0, stream>>>(amax_partial, nchunk, v_scale);
+        k_v_quant<128><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out);
     } else {
         k_v_amax<64><<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial);
-        k_v_quant<64><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out, v_scale);
+        k_v_amax_final<64><<<BH, 64, 0, stream>>>(amax_partial, nchunk, v_scale);
+        k_v_quant<64><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out);
     }
     return hipGetLastError();
 }

@@ -32,10 +32,11 @@ __host__ __device__ inline int pad128(int L) { return (L + 127) / 128 * 128; }
 inline int mean_chunks(int L) { return (L + kMeanChunk - 1) / kMeanChunk; }
 
 // K mean: partial binary64 sums [B*H, nchunk, D] (nchunk = mean_chunks(L));
-// the final mean mu fp32 [B*H, D] (sum in chunk order / L).
+// the final mean mu fp32 [B*H, D] (sum in chunk order / L; mu may be NULL),
+// also left, as binary64, over chunk 0 of the partials.
 hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, double* partial,
                                  hipStream_t stream);
-hipError_t launch_k_mean_final(const double* partial, int B, int H, int L, int D, float* mu,
+hipError_t launch_k_mean_final(double* partial, int B, int H, int L, int D, float* mu,
                                hipStream_t stream);
 
 // INT8 block quantization of Q (128-row blocks) and K (k_block rows, 64 or
