@@ -903,36 +903,47 @@ __global__ void k_hadamard_build(int R, uint16_t* hb, uint16_t* hf) {
     hf[i * R + j] = neg ? 0xBC00 : 0x3C00;   // fp16 -1 / +1
 }
 
-// One block = 4 waves x 32 tokens of one (b, h); blockIdx.x < nqb are Q blocks.
-// Rotation Y^T = H X^T on bf16/fp16 MFMA (H's +-1 entries and the half-precision
-// inputs are exact, accumulation in fp32), then times 1/sqrt(128).  Each lane
-// ends with token (l % 32) and channels 32 cb + 8 i + 4 (l / 32) + j, so one
-// MX block's amax needs a single cross-lane step and channel pairs (2t, 2t+1)
-// sit in the same lane for nibble packing.
+// One block = kMxRowBlocks consecutive 128-token row blocks of one (b, h),
+// 4 waves x 32 tokens each; row blocks < nqb are Q's, the rest K's.  Rotation
+// Y^T = H X^T on bf16/fp16 MFMA (H's +-1 entries and the half-precision inputs
+// are exact, accumulation in fp32), then times 1/sqrt(128).  Each lane ends
+// with token (l % 32) and channels 32 cb + 8 i + 4 (l / 32) + j, so one MX
+// block's amax needs a single cross-lane step and channel pairs (2t, 2t+1) sit
+// in the same lane for nibble packing.  The 32 KB Hadamard matrix is staged in
+// LDS once per block, for all its row blocks (staged per 128-token row block,
+// it moved as many bytes through L2 as K itself).
+constexpr int kMxRowBlocks = 4;
+
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
-    HalfView q, HalfView k, int H, int Lq, int Lk, int nqb, const float* mu,
+    HalfView q, HalfView k, int H, int Lq, int Lk, int nqb, int nrb, const float* mu,
     const uint16_t* hmat_bf16, const uint16_t* hmat_f16, float inv_sqrt_r, const float* mu_rot,
     uint8_t* q_out, uint8_t* q_e8, uint8_t* k_out, uint8_t* k_e8) {
     constexpr int D = 128;
-    const bool isq = (int)blockIdx.x < nqb;
-    const int blk = isq ? blockIdx.x : blockIdx.x - nqb;
-    const int L = isq ? Lq : Lk;
-    const int Lp = pad128(L);
-    const HalfView& src = isq ? q : k;
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 31, half = lane >> 5;
-    const int token = blk * 128 + wave * 32 + col;
-    const bool valid = token < L;
     const bool rotate = hmat_bf16 != nullptr;
 
-    __shared__ uint16_t hs[D * D];   // 32 KB: the Hadamard matrix for this block
+    // 32 KB: the Hadamard matrix in the inputs' half format (Q and K share it)
+    __shared__ uint16_t hs[D * D];
     if (rotate) {
-        const uint16_t* hm = src.bf16 ? hmat_bf16 : hmat_f16;
+        const uint16_t* hm = q.bf16 ? hmat_bf16 : hmat_f16;
         for (int c = threadIdx.x; c < D * D / 8; c += kThreads)
             *(uint4*)&hs[c * 8] = *(const uint4*)&hm[c * 8];
         __syncthreads();
     }
+
+#pragma unroll 1
+    for (int rb = 0; rb < kMxRowBlocks; ++rb) {
+    const int gblk = blockIdx.x * kMxRowBlocks + rb;
+    if (gblk >= nrb) break;   // block-uniform
+    const bool isq = gblk < nqb;
+    const int blk = isq ? gblk : gblk - nqb;
+    const int L = isq ? Lq : Lk;
+    const int Lp = pad128(L);
+    const HalfView& src = isq ? q : k;
+    const int token = blk * 128 + wave * 32 + col;
+    const bool valid = token < L;
 
     float y[4][16];   // [cb][e]: channel 32 cb + 8 (e / 4) + 4 half + (e % 4)
     if (rotate) {
@@ -970,14 +981,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     int ex[4];
     uint16_t pk[4][4];
     mx_quant_rows(y, ex, pk);
+    // Whole 16-byte stores: the token's 64 code bytes are split between the
+    // lane pair (l, l ^ 32), bytes 16 cb + 4 i + 2 h + {0, 1} in lane half h.
+    // Lane half h collects MX blocks 2 h and 2 h + 1 from both (the partner's
+    // halves of them through one exchange) and writes them as two 16-byte
+    // chunks; the four E8M0 bytes go out as one dword.  (Byte and 16-bit
+    // stores of the same data left the kernel write-bound on partial lines.)
+    uint32_t mine[2][4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        if (half == 0 && token < Lp) oe[((int64_t)bh * Lp + token) * (D / 32) + cb] = (uint8_t)(ex[cb] + 127);
+    for (int j = 0; j < 2; ++j) {
+        const int cb_keep = 2 * half + j, cb_send = 2 * (1 - half) + j;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (token < Lp)
-                *(uint16_t*)(out + ((int64_t)bh * Lp + token) * (D / 2) + 16 * cb + 4 * i + 2 * half) = pk[cb][i];
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)pk[cb_send][i], 32) & 0xFFFFu;
+            mine[j][i] = half == 0 ? (uint32_t)pk[cb_keep][i] | (other << 16)
+                                   : other | ((uint32_t)pk[cb_keep][i] << 16);
+        }
     }
+    if (token < Lp) {
+        uint8_t* orow = out + ((int64_t)bh * Lp + token) * (D / 2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *(uint4*)(orow + 16 * (2 * half + j)) = make_uint4(mine[j][0], mine[j][1], mine[j][2], mine[j][3]);
+        if (half == 0)
+            *(uint32_t*)(oe + ((int64_t)bh * Lp + token) * (D / 32)) =
+                (uint32_t)(ex[0] + 127) | ((uint32_t)(ex[1] + 127) << 8) | ((uint32_t)(ex[2] + 127) << 16) |
+                ((uint32_t)(ex[3] + 127) << 24);
+    }
+    }   // row blocks
 }
 
 }  // namespace
@@ -1122,8 +1153,9 @@ hipError_t launch_quant_qk_mxfp4(const HalfView& q, const HalfView& k, int B, in
         mrot = mu_rot_ws;
     }
     const int nqb = pad128(Lq) / 128, nkb = pad128(Lk) / 128;
-    dim3 grid(nqb + nkb, B * H);
-    k_quant_mxfp4<<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, nqb, mu,
+    const int nrb = nqb + nkb;   // K-only calls come with Lq = 0: no Q row blocks
+    dim3 grid((nrb + kMxRowBlocks - 1) / kMxRowBlocks, B * H);
+    k_quant_mxfp4<<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, nqb, nrb, mu,
                                                  (const uint16_t*)hadamard_bf16,
                                                  (const uint16_t*)hadamard_f16, inv_sqrt_r, mrot,
                                                  q_out, q_e8, k_out, k_e8);
