@@ -425,12 +425,16 @@ __device__ __forceinline__ void mx_fused_qfrag(QFrag<128, true>& qf, const AttnK
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
             xb[kc] = valid ? *(const uint4*)(row + 16 * kc + 8 * half) : make_uint4(0, 0, 0, 0);
-        // 32 KB of +-1 entries: 32 regions of 1 KB, eight per wave
+        // 32 KB of +-1 entries: 32 regions of 1 KB, eight per wave.  LDS chunk
+        // p holds chunk (p % 16) ^ (r % 16) of row r = p / 16 (the layout
+        // mx_rotate_rows reads), so each lane fetches the global chunk that
+        // belongs at its position.
         const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.hmat, D * D * 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int region = 4 * j + wave;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, ring + 1024 * region, 16, 1024 * region + 16 * lane, 0, 0, 0);
+            const int p = 64 * region + lane, r = p >> 4, c = (p & 15) ^ (r & 15);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, ring + 1024 * region, 16, 256 * r + 16 * c, 0, 0, 0);
         }
         wait_dma();
         __syncthreads();

@@ -929,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     if (rotate) {
         const uint16_t* hm = q.bf16 ? hmat_bf16 : hmat_f16;
         for (int c = threadIdx.x; c < D * D / 8; c += kThreads)
-            *(uint4*)&hs[c * 8] = *(const uint4*)&hm[c * 8];
+            *(uint4*)&hs[8 * (16 * (c / 16) + ((c % 16) ^ ((c / 16) & 15)))] = *(const uint4*)&hm[c * 8];
         __syncthreads();
     }
 

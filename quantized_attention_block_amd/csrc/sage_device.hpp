@@ -128,7 +128,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // Shared by the MXFP4 quantizer and the attention kernel's fused-Q prologue, so
 // that both give the same codes bit for bit.  Lane l holds token (l % 32):
 //   xb[kc]: its channels [16 kc + 8 (l / 32), +8) (half precision, bf16 or fp16)
-//   hs:     the 128 x 128 +-1 Hadamard matrix in LDS, row-major, same precision
+//   hs:     the 128 x 128 +-1 Hadamard matrix in LDS, row-major, same precision,
+//           16-byte chunk c of row r stored at chunk c ^ (r % 16) of the row (the
+//           256-byte rows are one full sweep of the LDS banks: unswizzled, the
+//           16 rows one read pass fetches at one column meet on the same banks)
 // Y^T = H X^T on MFMA (H's entries and the inputs are exact, fp32 accumulation
 // over kc ascending), then y = (Y - sub) * inv_sqrt_r, with y[cb][e] channel
 // 32 cb + 8 (e / 4) + 4 (l / 32) + (e % 4) of the token; sub (the rotated K
@@ -143,7 +146,8 @@ __device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (
         v16f acc = {0};
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) {
-            const uint4 ha = *(const uint4*)&hs[(32 * cb + col) * D + 16 * kc + 8 * half];
+            const int hr = 32 * cb + col, hc = (2 * kc + half) ^ (hr & 15);
+            const uint4 ha = *(const uint4*)&hs[hr * D + 8 * hc];
             if (bf16)
                 acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ha), __builtin_bit_cast(bf16x8, xb[kc]), acc);
             else
