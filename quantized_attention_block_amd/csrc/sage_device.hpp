@@ -75,23 +75,6 @@ __device__ __forceinline__ uint32_t cvt_pk_fp8(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
-// fp32 -> E2M1 nibble, round to nearest even, saturating at 6 (|x| < 8 on the
-// quantization path: x = value * 2^-e with amax * 2^-e in [4, 8)).
-__device__ __forceinline__ uint32_t e2m1_rne(float x) {
-    uint32_t s = (__float_as_uint(x) >> 31) << 3;
-    float a = fabsf(x);
-    uint32_t c;
-    if (a < 2.0f) {
-        c = (uint32_t)__builtin_rintf(a * 2.0f);           // 0, 0.5, 1, 1.5, 2
-    } else if (a < 4.0f) {
-        c = 4u + (uint32_t)__builtin_rintf(a - 2.0f);      // 2, 3, 4
-    } else {
-        float t = __builtin_rintf((a - 4.0f) * 0.5f);      // 4, 6 (ties to 4)
-        c = 6u + (uint32_t)fminf(t, 1.0f);
-    }
-    return s | c;
-}
-
 // MX shared exponent of a block: floor(log2(amax)) - 2 from the fp32 bits,
 // clamped to [-127, 127]; amax == 0 -> -127.
 __device__ __forceinline__ int mx_exponent(float amax) {
@@ -176,12 +159,19 @@ __device__ __forceinline__ void mx_quant_rows(const float (&y)[4][16], int (&ex)
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[cb][e]));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         ex[cb] = mx_exponent(amax);
+        // gfx950's scaled conversion divides by 2^(exponent field of the scale
+        // - 127) -- the E8M0 value of the scale's bits -- and rounds to the
+        // nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even
+        // code), saturating at 6: the E2M1 code of y * 2^-ex for every ex in
+        // [-127, 127] (checked against a software rounding over a grid of
+        // inputs and scales, exponent field 0 included).  Two values per
+        // instruction, the first in the low nibble, into byte `sel`.
+        const float sc = __builtin_bit_cast(float, (uint32_t)(ex[cb] + 127) << 23);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t n[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) n[j] = e2m1_rne(__builtin_ldexpf(y[cb][4 * i + j], -ex[cb]));
-            pk[cb][i] = (uint16_t)(n[0] | (n[1] << 4) | (n[2] << 8) | (n[3] << 12));
+            uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[cb][4 * i], y[cb][4 * i + 1], sc, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[cb][4 * i + 2], y[cb][4 * i + 3], sc, 1);
+            pk[cb][i] = (uint16_t)w;
         }
     }
 }
