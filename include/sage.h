@@ -261,6 +261,11 @@ typedef struct {
      * [B, MTP, Hq] (one per (token, head) row), contiguous; q's value is
      * code * scale */
     const sage_tensor* q_scale;
+    /* splits per sequence: 0 takes the plan, one split per 256-token tile
+     * (sage_decode_num_splits(window, MTP, max_ctx)); any other value must
+     * equal the plan's count (other split lengths are not built:
+     * SAGE_ERR_UNSUPPORTED; negative: SAGE_ERR_INVALID_ARG) */
+    int32_t num_splits;
 } sage_decode_params;
 
 sage_status sage_paged_decode_workspace_size(const sage_tensor* q, const sage_tensor* k_cache,

@@ -517,6 +517,11 @@ sage_status decode_query(const sage_tensor* q, const sage_tensor* page_table,
     if (p->max_ctx < 1) return fail(SAGE_ERR_INVALID_ARG, "params.max_ctx must be >= 1");
     if (p->window < 0) return fail(SAGE_ERR_INVALID_ARG, "params.window must be >= 0");
     s->splits = sage_decode_num_splits(p->window, s->MTP, p->max_ctx);
+    if (p->num_splits < 0) return fail(SAGE_ERR_INVALID_ARG, "params.num_splits must be >= 0");
+    if (p->num_splits != 0 && p->num_splits != s->splits)
+        return fail(SAGE_ERR_UNSUPPORTED,
+                    "params.num_splits %d: only the plan's %d splits (one per 256-token tile) are built",
+                    p->num_splits, s->splits);
     s->rows_pad = 64;
     return SAGE_OK;
 }

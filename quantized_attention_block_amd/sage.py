@@ -72,7 +72,7 @@ class AttnParams(ctypes.Structure):
 class DecodeParams(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("window", ctypes.c_int32),
                 ("v_transposed", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
-                ("q_scale", ctypes.POINTER(SageTensor))]
+                ("q_scale", ctypes.POINTER(SageTensor)), ("num_splits", ctypes.c_int32)]
 
 
 _lib = None
@@ -364,18 +364,18 @@ def sage_decode_num_splits(window: int, mtp: int, max_ctx: int) -> int:
     return int(lib().sage_decode_num_splits(window, mtp, max_ctx))
 
 
-def _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale):
+def _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale, num_splits=0):
     """DecodeParams plus the descriptor it points to (kept alive by the caller)."""
     qsd = desc(q_scale) if q_scale is not None else None
     prm = DecodeParams(float(sm_scale), int(window), int(v_transposed), int(max_ctx),
-                       ctypes.pointer(qsd) if qsd is not None else None)
+                       ctypes.pointer(qsd) if qsd is not None else None, int(num_splits))
     return prm, qsd
 
 
 def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, *, max_ctx: int,
                       window: int = 0, sm_scale: float = 0.0, v_transposed: bool = True,
                       q_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      workspace: Optional[torch.Tensor] = None, num_splits: int = 0) -> torch.Tensor:
     """q bf16 / fp16 [B, MTP, Hq, D], or e4m3 with fp32 `q_scale` ([1] or
     [B, MTP, Hq]); caches e4m3 [P, Hkv, page, D] (V transposed: [P, Hkv, D,
     page], or plain like K with v_transposed False) with fp32 scales
@@ -388,7 +388,7 @@ def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_len
     if out is None:
         odt = q.dtype if q.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
         out = torch.empty(q.shape, dtype=odt, device=q.device)
-    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale)
+    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale, num_splits)
     qd, ptd, kcd = desc(q), desc(page_table), desc(k_cache)
     if workspace is None:
         nbytes = ctypes.c_size_t()
@@ -407,12 +407,12 @@ def sage_paged_decode(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_len
 
 def sage_paged_decode_noalloc(q, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, out, *,
                               max_ctx: int, window: int = 0, sm_scale: float = 0.0,
-                              v_transposed: bool = True,
-                              q_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+                              v_transposed: bool = True, q_scale: Optional[torch.Tensor] = None,
+                              num_splits: int = 0) -> torch.Tensor:
     """sage_paged_decode without a workspace: the library's fixed per-device
     scratch holds the split partials (calls that overlap on one device race).
     `out` is required; nothing is allocated."""
-    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale)
+    prm, _keep = _decode_params(sm_scale, window, v_transposed, max_ctx, q_scale, num_splits)
     _check(lib().sage_paged_decode_noalloc(ctypes.byref(desc(q)), ctypes.byref(desc(k_cache)),
                                            ctypes.byref(desc(v_cache)), ctypes.byref(desc(k_scale)),
                                            ctypes.byref(desc(v_scale)), ctypes.byref(desc(page_table)),

@@ -208,6 +208,12 @@ def test_paged_decode_refusals(S):
     assert call(S.DecodeParams(0.0, 256, 1, 4096)) == S.ERR_SHAPE       # table too short
     assert call(S.DecodeParams(0.0, 256, 2, 512)) == S.ERR_INVALID_ARG  # layout flag is 0 or 1
     assert call(S.DecodeParams(0.0, -1, 1, 512)) == S.ERR_INVALID_ARG
+    # num_splits: 0 or the plan's count (window 256, MTP 4 within 512 keys: 2); others are not built
+    plan = S.lib().sage_decode_num_splits(256, MTP, 512)
+    assert plan == 2
+    assert call(S.DecodeParams(0.0, 256, 1, 512, None, plan)) == S.ERR_HIP   # valid: reaches the device check
+    assert call(S.DecodeParams(0.0, 256, 1, 512, None, plan + 1)) == S.ERR_UNSUPPORTED
+    assert call(S.DecodeParams(0.0, 256, 1, 512, None, -1)) == S.ERR_INVALID_ARG
     # plain V [P, Hkv, page, D]: a transposed-shaped cache is refused (page 64 != D)
     kc64, vt64 = T(S.FP8_E4M3FN, (P_, Hkv, 64, D)), T(S.FP8_E4M3FN, (P_, Hkv, D, 64))
     sc64 = T(S.F32, (P_, Hkv, 64))

@@ -180,3 +180,23 @@ def test_paged_decode_context_above_max_ctx(dev, orc):
     clamped = wl.DecodeInputs(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale, inp.page_table,
                               torch.clamp(inp.ctx_lens, max=max_ctx))
     _check(g, _oracle(orc, clamped, 0, base.sm_scale), _oracle(orc, clamped, 0, base.sm_scale, False))
+
+
+def test_paged_decode_explicit_num_splits(dev):
+    """num_splits given as the plan's count runs the same plan (bit-identical
+    output); any other count is refused before anything is enqueued."""
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=2, ctx=3000)
+    say("paged decode explicit num_splits")
+    args = (inp.q.to(dev), inp.k_cache.to(dev).view(torch.float8_e4m3fn),
+            inp.v_cache.transpose(2, 3).contiguous().to(dev).view(torch.float8_e4m3fn),
+            inp.k_scale.to(dev), inp.v_scale.to(dev), inp.page_table.to(dev), inp.ctx_lens.to(dev))
+    kw = dict(max_ctx=3000, window=w.window, sm_scale=w.sm_scale)
+    plan = sage.sage_decode_num_splits(w.window, w.mtp, 3000)
+    a = sage.sage_paged_decode(*args, **kw)
+    b = sage.sage_paged_decode(*args, num_splits=plan, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(sage.SageError) as err:
+        sage.sage_paged_decode(*args, num_splits=plan + 1, **kw)
+    assert err.value.status == sage.ERR_UNSUPPORTED
