@@ -212,13 +212,15 @@ def test_single_read_wait_bound(dev, name, kw):
         sage.sage_set_quant_wait_us(-1)
 
 
-def test_two_pass_path_bit_exact(dev, orc):
+@pytest.mark.parametrize("name,H", [("tiny", 9), ("llm_prefill", 9)])
+def test_two_pass_path_bit_exact(dev, orc, name, H):
     """More chunks than the device holds at once (9 heads x 258 chunks of 256
-    tokens): the quantizers take the two-pass kernels, whose results must be
+    tokens, D 64 and D 128): the quantizers take the two-pass kernels (chunk
+    statistics, their per-head finish, then the codes), whose results must be
     the oracle's too."""
-    w = wl.WORKLOADS["tiny"]
-    inp = wl.make_prefill(w, device=dev, Lq=66000, Lk=66000, B=1, H=9)
-    say("two-pass quantizers", "tiny distribution, 9 heads x 66000 tokens, D 64")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, Lq=66000, Lk=66000, B=1, H=H)
+    say("two-pass quantizers", f"{name} distribution, {H} heads x 66000 tokens, D {w.D}")
     qk = sage.sage_quantize_qk(inp.q, inp.k)
     v_q, v_s = sage.sage_quantize_v(inp.v)
     torch.cuda.synchronize()
