@@ -438,7 +438,7 @@ __device__ __forceinline__ void mx_fused_qfrag(QFrag<128, true>& qf, const AttnK
         }
         wait_dma();
         __syncthreads();
-        mx_rotate_rows((const uint16_t*)ring, xb, qh.bf16, a.inv_sqrt_r, nullptr, valid, y);
+        mx_rotate_rows((const uint16_t*)ring, xb, qh.bf16, a.inv_sqrt_r, valid, y);
     } else {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -458,18 +458,24 @@ __device__ __forceinline__ void mx_fused_qfrag(QFrag<128, true>& qf, const AttnK
     int ex[4];
     uint16_t pk[4][4];
     mx_quant_rows(y, ex, pk);
+    // (blocks picked with selects and shifts on the lane half, not an array
+    // index that depends on the lane: that compiles to compare-and-select
+    // chains or a scratch array)
+    const uint32_t e8 = (uint32_t)(ex[0] + 127) | ((uint32_t)(ex[1] + 127) << 8) |
+                        ((uint32_t)(ex[2] + 127) << 16) | ((uint32_t)(ex[3] + 127) << 24);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const int mine = 2 * c + half, theirs = 2 * c + (1 - half);
         uint32_t wd[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // bytes 4 i + {0, 1} of a block come from half 0, 4 i + {2, 3} from half 1
-            const uint32_t other = (uint32_t)__shfl_xor((int)pk[theirs][i], 32) & 0xFFFFu;
-            wd[i] = half == 0 ? (uint32_t)pk[mine][i] | (other << 16) : other | ((uint32_t)pk[mine][i] << 16);
+            const uint32_t lo = pk[2 * c][i], hi = pk[2 * c + 1][i];   // blocks 2 c and 2 c + 1
+            const uint32_t mine = half ? hi : lo, theirs = half ? lo : hi;
+            const uint32_t other = (uint32_t)__shfl_xor((int)theirs, 32) & 0xFFFFu;
+            wd[i] = half == 0 ? mine | (other << 16) : other | (mine << 16);
         }
         qf.f[c] = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
-        qf.s[c] = ex[mine] + 127;
+        qf.s[c] = (int)((e8 >> (8 * (2 * c + half))) & 0xFFu);
     }
     __syncthreads();   // every wave is done reading the Hadamard matrix from the ring
 }

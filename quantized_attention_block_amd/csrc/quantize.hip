@@ -914,6 +914,7 @@ __global__ void k_hadamard_build(int R, uint16_t* hb, uint16_t* hf) {
 // it moved as many bytes through L2 as K itself).
 constexpr int kMxRowBlocks = 4;
 
+template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     HalfView q, HalfView k, int H, int Lq, int Lk, int nqb, int nrb, const float* mu,
     const uint16_t* hmat_bf16, const uint16_t* hmat_f16, float inv_sqrt_r, const float* mu_rot,
@@ -924,14 +925,23 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     const int col = lane & 31, half = lane >> 5;
     const bool rotate = hmat_bf16 != nullptr;
 
-    // 32 KB: the Hadamard matrix in the inputs' half format (Q and K share it)
+    // 32 KB: the Hadamard matrix in the inputs' half format (Q and K share it);
+    // what the rows lose before quantization, per channel: nothing for Q rows
+    // (zeros), the K mean for K rows (rotated when rotating; zeros without
+    // smoothing)
     __shared__ uint16_t hs[D * D];
+    __shared__ __attribute__((aligned(16))) float sub_s[2][D];
     if (rotate) {
-        const uint16_t* hm = q.bf16 ? hmat_bf16 : hmat_f16;
+        const uint16_t* hm = BF16 ? hmat_bf16 : hmat_f16;
         for (int c = threadIdx.x; c < D * D / 8; c += kThreads)
             *(uint4*)&hs[8 * (16 * (c / 16) + ((c % 16) ^ ((c / 16) & 15)))] = *(const uint4*)&hm[c * 8];
-        __syncthreads();
     }
+    const float* ksub = rotate ? mu_rot : mu;
+    if (threadIdx.x < D) {
+        sub_s[0][threadIdx.x] = 0.0f;
+        sub_s[1][threadIdx.x] = ksub ? ksub[(int64_t)bh * D + threadIdx.x] : 0.0f;
+    }
+    __syncthreads();
 
 #pragma unroll 1
     for (int rb = 0; rb < kMxRowBlocks; ++rb) {
@@ -944,6 +954,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     const HalfView& src = isq ? q : k;
     const int token = blk * 128 + wave * 32 + col;
     const bool valid = token < L;
+    const float* sub = sub_s[isq ? 0 : 1];
 
     float y[4][16];   // [cb][e]: channel 32 cb + 8 (e / 4) + 4 half + (e % 4)
     if (rotate) {
@@ -951,11 +962,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
         uint4 xb[8];
         const uint16_t* row = (const uint16_t*)src.ptr + (int64_t)b * src.sB +
                               (int64_t)(valid ? token : 0) * src.sL + (int64_t)h * src.sH;
+        // loaded unconditionally (row 0 stands in for tokens past L; the
+        // rotation zeroes their outputs)
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-            xb[kc] = valid ? *(const uint4*)(row + 16 * kc + 8 * half) : make_uint4(0, 0, 0, 0);
-        mx_rotate_rows(hs, xb, src.bf16, inv_sqrt_r, (!isq && mu_rot) ? mu_rot + (int64_t)bh * D : nullptr,
-                       valid, y);
+        for (int kc = 0; kc < 8; ++kc) xb[kc] = *(const uint4*)(row + 16 * kc + 8 * half);
+        mx_rotate_rows<BF16>(hs, xb, inv_sqrt_r, sub, valid, y);
     } else {
         const uint16_t* row = (const uint16_t*)src.ptr + (int64_t)b * src.sB +
                               (int64_t)(valid ? token : 0) * src.sL + (int64_t)h * src.sH;
@@ -964,13 +975,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ch0 = 32 * cb + 8 * i + 4 * half;
-                uint2 u = valid ? *(const uint2*)(row + ch0) : make_uint2(0, 0);
-                uint32_t w[2] = {u.x, u.y};
+                const uint2 u = *(const uint2*)(row + ch0);   // row 0 for tokens past L
+                const float4 sv = *(const float4*)&sub[ch0];
+                const uint32_t w[2] = {u.x, u.y};
+                const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t bits = (w[j / 2] >> (16 * (j % 2))) & 0xFFFF;
-                    float t = src.bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-                    if (!isq && mu) t = t - mu[(int64_t)bh * D + ch0 + j];
+                    const float t = (BF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits)) - sc[j];
                     y[cb][4 * i + j] = valid ? t : 0.0f;
                 }
             }
@@ -987,15 +999,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     // halves of them through one exchange) and writes them as two 16-byte
     // chunks; the four E8M0 bytes go out as one dword.  (Byte and 16-bit
     // stores of the same data left the kernel write-bound on partial lines.)
+    // (The blocks are picked with selects on the lane half: an array index
+    // that depends on the lane compiles to compare-and-select chains and
+    // divergent branches.)
     uint32_t mine[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int cb_keep = 2 * half + j, cb_send = 2 * (1 - half) + j;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t other = (uint32_t)__shfl_xor((int)pk[cb_send][i], 32) & 0xFFFFu;
-            mine[j][i] = half == 0 ? (uint32_t)pk[cb_keep][i] | (other << 16)
-                                   : other | ((uint32_t)pk[cb_keep][i] << 16);
+            const uint32_t lo = pk[j][i], hi = pk[2 + j][i];   // blocks j and 2 + j
+            const uint32_t keep = half ? hi : lo, send = half ? lo : hi;
+            const uint32_t other = (uint32_t)__shfl_xor((int)send, 32) & 0xFFFFu;
+            mine[j][i] = half == 0 ? keep | (other << 16) : other | (keep << 16);
         }
     }
     if (token < Lp) {
@@ -1155,10 +1170,10 @@ hipError_t launch_quant_qk_mxfp4(const HalfView& q, const HalfView& k, int B, in
     const int nqb = pad128(Lq) / 128, nkb = pad128(Lk) / 128;
     const int nrb = nqb + nkb;   // K-only calls come with Lq = 0: no Q row blocks
     dim3 grid((nrb + kMxRowBlocks - 1) / kMxRowBlocks, B * H);
-    k_quant_mxfp4<<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, nqb, nrb, mu,
-                                                 (const uint16_t*)hadamard_bf16,
-                                                 (const uint16_t*)hadamard_f16, inv_sqrt_r, mrot,
-                                                 q_out, q_e8, k_out, k_e8);
+    auto kern = k.bf16 ? k_quant_mxfp4<true> : k_quant_mxfp4<false>;   // Q shares K's precision
+    kern<<<grid, kThreads, 0, stream>>>(q, k, H, Lq, Lk, nqb, nrb, mu, (const uint16_t*)hadamard_bf16,
+                                        (const uint16_t*)hadamard_f16, inv_sqrt_r, mrot, q_out, q_e8, k_out,
+                                        k_e8);
     return hipGetLastError();
 }
 

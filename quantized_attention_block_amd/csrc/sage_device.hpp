@@ -117,32 +117,60 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 //           16 rows one read pass fetches at one column meet on the same banks)
 // Y^T = H X^T on MFMA (H's entries and the inputs are exact, fp32 accumulation
 // over kc ascending), then y = (Y - sub) * inv_sqrt_r, with y[cb][e] channel
-// 32 cb + 8 (e / 4) + 4 (l / 32) + (e % 4) of the token; sub (the rotated K
-// mean, per channel) may be NULL.  Invalid tokens give 0.
-__device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (&xb)[8], bool bf16,
-                                               float inv_sqrt_r, const float* sub, bool valid,
-                                               float (&y)[4][16]) {
+// 32 cb + 8 (e / 4) + 4 (l / 32) + (e % 4) of the token.  Invalid tokens give 0.
+
+// The MFMA chain of output channels [32 cb, +32).
+template <bool BF16>
+__device__ __forceinline__ v16f mx_rotate_block(const uint16_t* hs, const uint4 (&xb)[8], int cb) {
     constexpr int D = 128;
     const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+    v16f acc = {0};
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+        const int hr = 32 * cb + col, hc = (2 * kc + half) ^ (hr & 15);
+        const uint4 ha = *(const uint4*)&hs[hr * D + 8 * hc];
+        if constexpr (BF16)
+            acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ha), __builtin_bit_cast(bf16x8, xb[kc]), acc);
+        else
+            acc = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, ha), __builtin_bit_cast(f16x8, xb[kc]), acc);
+    }
+    return acc;
+}
+
+// Input precision fixed at compile time; sub (per channel, e.g. the rotated K
+// mean, zeros for none; 16-byte aligned) is never NULL.  Subtracting +0 leaves every value,
+// -0 included, as it is, so rows with a zero sub get the codes of the form
+// below.
+template <bool BF16>
+__device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (&xb)[8], float inv_sqrt_r,
+                                               const float* sub, bool valid, float (&y)[4][16]) {
+    const int half = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        v16f acc = {0};
+        const v16f acc = mx_rotate_block<BF16>(hs, xb, cb);
+        // (sub is read unconditionally: a read inside the selection becomes a
+        // branch around each load)
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
-            const int hr = 32 * cb + col, hc = (2 * kc + half) ^ (hr & 15);
-            const uint4 ha = *(const uint4*)&hs[hr * D + 8 * hc];
-            if (bf16)
-                acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ha), __builtin_bit_cast(bf16x8, xb[kc]), acc);
-            else
-                acc = mfma_f16_32x32x16(__builtin_bit_cast(f16x8, ha), __builtin_bit_cast(f16x8, xb[kc]), acc);
-        }
+        for (int i = 0; i < 4; ++i) {
+            const float4 sv = *(const float4*)&sub[32 * cb + 8 * i + 4 * half];
+            const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int ch = 32 * cb + 8 * (e / 4) + 4 * half + (e % 4);
-            float t = acc[e];
-            if (sub) t = t - sub[ch];
-            y[cb][e] = valid ? t * inv_sqrt_r : 0.0f;
+            for (int j = 0; j < 4; ++j) {
+                const float r = (acc[4 * i + j] - sc[j]) * inv_sqrt_r;
+                y[cb][4 * i + j] = valid ? r : 0.0f;
+            }
         }
+    }
+}
+
+// Precision chosen at run time, nothing subtracted (the fused Q of attention).
+__device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (&xb)[8], bool bf16,
+                                               float inv_sqrt_r, bool valid, float (&y)[4][16]) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const v16f acc = bf16 ? mx_rotate_block<true>(hs, xb, cb) : mx_rotate_block<false>(hs, xb, cb);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) y[cb][e] = valid ? acc[e] * inv_sqrt_r : 0.0f;
     }
 }
 
