@@ -34,23 +34,32 @@ struct Rows {
     static constexpr int kRowsPerPass = kThreads / kLanesPerRow;
 };
 
-// Loads 8 consecutive channels [8 c8, 8 c8 + 8) of token l of head h, batch b.
-__device__ __forceinline__ void load8(const HalfView& v, int b, int l, int h, int c8, float out[8]) {
-    const uint16_t* p = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)l * v.sL +
-                        (int64_t)h * v.sH + c8 * 8;
-    uint4 u = *(const uint4*)p;
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+template <bool BF16>
+__device__ __forceinline__ void unpack8t(const uint4& u, float out[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (v.bf16) {
-            out[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFF);
-            out[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-        } else {
-            out[2 * i] = f16_bits_to_f32(w[i] & 0xFFFF);
-            out[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
-        }
+        out[2 * i] = BF16 ? bf16_bits_to_f32(w[i] & 0xFFFF) : f16_bits_to_f32(w[i] & 0xFFFF);
+        out[2 * i + 1] = BF16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
     }
 }
+
+// The rows of one kMeanChunk-token chunk [lo, lo + kMeanChunk) that a thread
+// of the chunk kernels reads: rows lo + r0 + kRowsPerPass i, channels
+// [8 c8, +8), all loads issued before any is used (one memory round trip per
+// chunk instead of one per row).  Rows at or past L (L >= 1) are read at row
+// L - 1, in bounds, and must be skipped by the caller.
+template <int D>
+struct ChunkRows {
+    static constexpr int kN = kMeanChunk / Rows<D>::kRowsPerPass;
+    uint4 raw[kN];
+    __device__ __forceinline__ void load(const HalfView& v, int b, int h, int L, int lo, int r0, int c8) {
+        const uint16_t* base = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)h * v.sH + 8 * c8;
+#pragma unroll
+        for (int i = 0; i < kN; ++i)
+            raw[i] = *(const uint4*)(base + (int64_t)min(lo + r0 + Rows<D>::kRowsPerPass * i, L - 1) * v.sL);
+    }
+};
 
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
@@ -72,17 +81,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // Partial binary64 channel sums over chunks of kMeanChunk tokens; fixed
 // summation order (per thread ascending rows, then ascending row groups), so
 // the result is deterministic.
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_mean_partial(HalfView k, int H, int L, int nchunk,
                                                            double* partial) {
     using G = Rows<D>;
     const int bh = blockIdx.x, b = bh / H, h = bh % H, chunk = blockIdx.y;
     const int c8 = threadIdx.x % G::kLanesPerRow, r0 = threadIdx.x / G::kLanesPerRow;
+    const int lo = chunk * kMeanChunk;
+    ChunkRows<D> rows;
+    rows.load(k, b, h, L, lo, r0, c8);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int lo = chunk * kMeanChunk, hi = min(L, lo + kMeanChunk);
-    for (int l = lo + r0; l < hi; l += G::kRowsPerPass) {
+#pragma unroll
+    for (int j = 0; j < ChunkRows<D>::kN; ++j) {
+        if (lo + r0 + G::kRowsPerPass * j >= L) continue;
         float x[8];
-        load8(k, b, l, h, c8, x);
+        unpack8t<BF16>(rows.raw[j], x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
     }
@@ -159,16 +172,7 @@ struct Rows16 {
     static constexpr int kPasses = 128 / kRowsPass;              // 4 or 2
 };
 
-__device__ __forceinline__ void unpack8(const uint4& u, bool bf16, float out[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[2 * i] = bf16 ? bf16_bits_to_f32(w[i] & 0xFFFF) : f16_bits_to_f32(w[i] & 0xFFFF);
-        out[2 * i + 1] = bf16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
-    }
-}
-
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k, int H, int Lq,
                                                          int Lk, int k_block, int nqb,
                                                          const double* mean_final, int nchunk,
@@ -200,22 +204,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
             if (row0 + p * G::kRowsPass + r0 >= L) raw[p][0] = raw[p][1] = make_uint4(0, 0, 0, 0);
     }
 
-    __shared__ float mu_s[D];
+    // the subtracted mean: K's (zeros without smoothing), zeros for Q; read
+    // unconditionally (a read under the condition becomes a branch per read)
+    __shared__ __attribute__((aligned(16))) float mu_s[D];
     __shared__ float red[kThreads / 64][2];
     const bool smooth = !isq && mean_final != nullptr;
-    if (smooth) {
-        if (threadIdx.x < D) mu_s[threadIdx.x] = (float)mean_final[(int64_t)bh * nchunk * D + threadIdx.x];
-        __syncthreads();
-    }
+    if (threadIdx.x < D) mu_s[threadIdx.x] = smooth ? (float)mean_final[(int64_t)bh * nchunk * D + threadIdx.x] : 0.0f;
+    __syncthreads();
     float mu16[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mu16[i] = smooth ? mu_s[16 * c16 + i] : 0.0f;
+    for (int i = 0; i < 16; ++i) mu16[i] = mu_s[16 * c16 + i];
 
     // x = fp32(value - mu); amax per quantization block.  Passes [0, kPasses/2)
     // hold rows 0..63 of the 128, the rest rows 64..127.
     auto xval = [&](int p, float x[16]) {
-        unpack8(raw[p][0], src.bf16, x);
-        unpack8(raw[p][1], src.bf16, x + 8);
+        unpack8t<BF16>(raw[p][0], x);
+        unpack8t<BF16>(raw[p][1], x + 8);
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = x[i] - mu16[i];
     };
@@ -288,17 +292,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
 // ---- V: per-channel amax, then e4m3 codes written transposed ----------------
 // Pass 1: per chunk of kMeanChunk tokens, the channel amax of |v| (no atomics:
 // one partial row per chunk); head-fastest grid like the K mean.
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_v_amax(HalfView v, int H, int L, int nchunk,
                                                      float* partial) {
     using G = Rows<D>;
     const int bh = blockIdx.x, b = bh / H, h = bh % H, chunk = blockIdx.y;
     const int c8 = threadIdx.x % G::kLanesPerRow, r0 = threadIdx.x / G::kLanesPerRow;
+    const int lo = chunk * kMeanChunk;
+    ChunkRows<D> rows;
+    rows.load(v, b, h, L, lo, r0, c8);
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int lo = chunk * kMeanChunk, hi = min(L, lo + kMeanChunk);
-    for (int l = lo + r0; l < hi; l += G::kRowsPerPass) {
+#pragma unroll
+    for (int j = 0; j < ChunkRows<D>::kN; ++j) {
+        if (lo + r0 + G::kRowsPerPass * j >= L) continue;
         float x[8];
-        load8(v, b, l, h, c8, x);
+        unpack8t<BF16>(rows.raw[j], x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(x[i]));
     }
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_v_amax(HalfView v, int H, int L, i
 // packs, per channel, the 4 keys' codes into one dword, stored into an LDS
 // tile [D][128 keys] whose 16-byte chunks are XOR-swizzled by row; the tile is
 // then written out as 128-byte V^T rows with 16-byte stores.
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, int nchunk,
                                                       const float* partial, uint8_t* v_out) {
     constexpr int kKeys = 128;
@@ -331,17 +339,22 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
     const int Lp = pad128(L);
     const int c8 = threadIdx.x % kGroups, kg0 = threadIdx.x / kGroups;
 
-    // row loads first: keys k0 + 4 kg + j, channels [8 c8, +8)
+    // row loads first: keys k0 + 4 kg + j, channels [8 c8, +8); keys past L
+    // read key L - 1 (in bounds, unconditional) and are zeroed afterwards
     uint4 raw[kPasses][4];
+    const uint16_t* vbase = (const uint16_t*)v.ptr + (int64_t)b * v.sB + (int64_t)h * v.sH + 8 * c8;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = k0 + 4 * (p * kKeyGroups + kg0) + j;
-            raw[p][j] = key < L ? *(const uint4*)((const uint16_t*)v.ptr + (int64_t)b * v.sB +
-                                                  (int64_t)key * v.sL + (int64_t)h * v.sH + 8 * c8)
-                                : make_uint4(0, 0, 0, 0);
+            raw[p][j] = *(const uint4*)(vbase + (int64_t)min(key, L - 1) * v.sL);
         }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (k0 + 4 * (p * kKeyGroups + kg0) + j >= L) raw[p][j] = make_uint4(0, 0, 0, 0);
 
     __shared__ float inv_s[D];
     __shared__ __attribute__((aligned(16))) uint32_t tile[D * kKeys / 4];
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
         const int kg = p * kKeyGroups + kg0;
         float x[4][8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) unpack8(raw[p][j], v.bf16, x[j]);
+        for (int j = 0; j < 4; ++j) unpack8t<BF16>(raw[p][j], x[j]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t c = cvt_pk_fp8<false>(x[0][i] * inv8[i], x[1][i] * inv8[i], 0);
@@ -499,16 +512,6 @@ __device__ __forceinline__ bool head_wait(const HeadSync& hs, int bh, int chunk,
     }
     __syncthreads();
     return *met_lds != 0;
-}
-
-template <bool BF16>
-__device__ __forceinline__ void unpack8t(const uint4& u, float out[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[2 * i] = BF16 ? bf16_bits_to_f32(w[i] & 0xFFFF) : f16_bits_to_f32(w[i] & 0xFFFF);
-        out[2 * i + 1] = BF16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
-    }
 }
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int off) {
@@ -1086,10 +1089,9 @@ hipError_t launch_k_mean_partial(const HalfView& k, int B, int H, int L, int D, 
                                  hipStream_t stream) {
     const int nchunk = mean_chunks(L);
     dim3 grid(B * H, nchunk);
-    if (D == 128)
-        k_mean_partial<128><<<grid, kThreads, 0, stream>>>(k, H, L, nchunk, partial);
-    else
-        k_mean_partial<64><<<grid, kThreads, 0, stream>>>(k, H, L, nchunk, partial);
+    auto kern = D == 128 ? (k.bf16 ? k_mean_partial<128, true> : k_mean_partial<128, false>)
+                         : (k.bf16 ? k_mean_partial<64, true> : k_mean_partial<64, false>);
+    kern<<<grid, kThreads, 0, stream>>>(k, H, L, nchunk, partial);
     return hipGetLastError();
 }
 
@@ -1125,7 +1127,9 @@ hipError_t launch_quant_qk_int8(const HalfView& q, const HalfView& k, int B, int
         if (e == hipSuccess) e = launch_k_mean_final(mean_partial, B, H, Lk, D, mu_out, stream);
         if (e != hipSuccess) return e;
     }
-    auto quant = D == 128 ? k_quant_int8<128> : k_quant_int8<64>;
+    // Q shares K's precision when both are given (the ABI refuses a mix)
+    auto quant = D == 128 ? (k.bf16 ? k_quant_int8<128, true> : k_quant_int8<128, false>)
+                          : (k.bf16 ? k_quant_int8<64, true> : k_quant_int8<64, false>);
     quant<<<dim3(BH, nqb + nkb), kThreads, 0, stream>>>(q, k, H, Lq, Lk, k_block, nqb,
                                                         smooth ? mean_partial : nullptr, nchunk,
                                                         q_out, q_scale, k_out, k_scale);
@@ -1145,13 +1149,17 @@ hipError_t launch_quant_v(const HalfView& v, int B, int H, int Lk, int D, float*
     }
     dim3 g1(BH, nchunk), g2(BH, pad128(Lk) / 128);
     if (D == 128) {
-        k_v_amax<128><<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial);
+        (v.bf16 ? k_v_amax<128, true> : k_v_amax<128, false>)<<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk,
+                                                                                         amax_partial);
         k_v_amax_final<128><<<BH, 128, 0, stream>>>(amax_partial, nchunk, v_scale);
-        k_v_quant<128><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out);
+        (v.bf16 ? k_v_quant<128, true> : k_v_quant<128, false>)<<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk,
+                                                                                           amax_partial, v_out);
     } else {
-        k_v_amax<64><<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial);
+        (v.bf16 ? k_v_amax<64, true> : k_v_amax<64, false>)<<<g1, kThreads, 0, stream>>>(v, H, Lk, nchunk,
+                                                                                       amax_partial);
         k_v_amax_final<64><<<BH, 64, 0, stream>>>(amax_partial, nchunk, v_scale);
-        k_v_quant<64><<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk, amax_partial, v_out);
+        (v.bf16 ? k_v_quant<64, true> : k_v_quant<64, false>)<<<g2, kThreads, 0, stream>>>(v, H, Lk, nchunk,
+                                                                                         amax_partial, v_out);
     }
     return hipGetLastError();
 }
