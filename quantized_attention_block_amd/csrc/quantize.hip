@@ -156,11 +156,11 @@ __global__ void k_v_amax_final(float* partial, int nchunk, float* v_scale) {
 }
 
 // ---- INT8 block quantization -------------------------------------------------
-// One block per (b*h, 128 token rows), Q blocks first, then K blocks; a Q
-// block is one q_block (128 rows), a K block holds 128 / k_block k_blocks.  A
-// thread owns 16 channels [16 c16, +16) of rows r0 + kRowsPass p: its loads
-// and its code stores are 16-byte accesses.  Per quantization block: amax over
-// the valid rows (K: of fp32(K - mu)), scale = amax / 127,
+// One block per (b*h, 128 token rows), block index y: Q's row blocks, then
+// K's (dispatched last-first, see below); a Q block is one q_block (128
+// rows), a K block holds 128 / k_block k_blocks.  A thread owns 16 channels
+// [16 c16, +16) of rows r0 + kRowsPass p: its loads and its code stores are
+// 16-byte accesses.  Per quantization block: amax over the valid rows (K: of fp32(K - mu)), scale = amax / 127,
 // codes = clamp(rne(x * (127 / amax)), -127, 127); padded rows get code 0.
 // K blocks take the channel mean that k_mean_final left over chunk 0 of the
 // binary64 partials (summed in chunk order, divided by L in binary64, rounded
@@ -179,8 +179,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
                                                          int8_t* q_out, float* q_scale, int8_t* k_out,
                                                          float* k_scale) {
     using G = Rows16<D>;
-    const bool isq = (int)blockIdx.y < nqb;
-    const int blk = isq ? blockIdx.y : blockIdx.y - nqb;   // 128-row block
+    // Row blocks run last-first: the statistics pass before this one read the
+    // tokens first-first, so its last ~256 MB (the size of the GPU's
+    // memory-side cache) are still cached when this pass starts on them
+    // (32760 tokens x 40 heads: quantize_qk step 176 -> 154 us; the same
+    // order measured no gain for the MXFP4 quantizer, which is not bound by
+    // its reads)
+    const int yy = (int)gridDim.y - 1 - (int)blockIdx.y;
+    const bool isq = yy < nqb;
+    const int blk = isq ? yy : yy - nqb;   // 128-row block
     const int L = isq ? Lq : Lk;
     const int Lp = pad128(L);
     const HalfView& src = isq ? q : k;
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void k_v_quant(HalfView v, int H, int L, 
     constexpr int kKeyGroups = kThreads / kGroups;         // 4-key groups per pass (16 or 32)
     constexpr int kPasses = kKeys / (4 * kKeyGroups);      // 2 or 1
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
-    const int k0 = blockIdx.y * kKeys;
+    const int k0 = ((int)gridDim.y - 1 - (int)blockIdx.y) * kKeys;   // last-first, as in k_quant_int8
     const int Lp = pad128(L);
     const int c8 = threadIdx.x % kGroups, kg0 = threadIdx.x / kGroups;
 
