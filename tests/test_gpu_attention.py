@@ -378,6 +378,7 @@ def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
     (333, 333, 2, torch.bfloat16, False),       # no rotation
     (700, 1500, 2, torch.bfloat16, True),       # Lq != Lk
     (256, 256, 3, torch.float16, True),         # fp16 inputs: the fp16 Hadamard matrix
+    (300, 300, 2, torch.float16, False),        # fp16 inputs, no rotation
     (32760, 32760, 1, torch.bfloat16, True),    # the full video-DiT length, one head
 ])
 def test_fused_mxfp4_q_equals_unfused(dev, Lq, Lk, H, dtype, rotate):

@@ -62,14 +62,26 @@ def test_v_fp8_bit_exact(dev, orc, name, kw):
     assert np.array_equal(v_s.cpu().numpy(), vs)
 
 
-@pytest.mark.parametrize("name,kw", CASES[1:])
-def test_mxfp4_without_rotation_bit_exact(dev, orc, name, kw):
-    w = wl.WORKLOADS[name]
-    inp = wl.make_prefill(w, device=dev, **kw)
-    say("mxfp4 quantize (no rotation)", name, kw)
-    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4)
+# MXFP4 needs D = 128: the D-128 cases in their own precision, and the ragged
+# LLM-prefill case cast to fp16 (the quantizer's fp16 instantiation)
+MX_CASES = [(name, kw, None) for name, kw in CASES[1:]] + [("llm_prefill", CASES[1][1], torch.float16)]
+
+
+def _mx_inputs(dev, name, kw, dtype):
+    inp = wl.make_prefill(wl.WORKLOADS[name], device=dev, **kw)
+    q, k = inp.q, inp.k
+    if dtype is not None:
+        q, k = q.to(dtype), k.to(dtype)
+    return q, k
+
+
+@pytest.mark.parametrize("name,kw,dtype", MX_CASES)
+def test_mxfp4_without_rotation_bit_exact(dev, orc, name, kw, dtype):
+    q, k = _mx_inputs(dev, name, kw, dtype)
+    say("mxfp4 quantize (no rotation)", name, kw, q.dtype)
+    qk = sage.sage_quantize_qk(q, k, mode=sage.QK_MXFP4)
     torch.cuda.synchronize()
-    qc, kc = canon(inp.q), canon(inp.k)
+    qc, kc = canon(q), canon(k)
     Lq, Lk = qc.shape[2], kc.shape[2]
     mu_g = qk.k_mean.cpu().numpy()
     assert np.array_equal(mu_g, orc.k_mean(kc))
@@ -83,19 +95,18 @@ def test_mxfp4_without_rotation_bit_exact(dev, orc, name, kw):
     assert np.array_equal(qk.k_scale.cpu().numpy()[:, :, :Lk], ke)
 
 
-@pytest.mark.parametrize("name,kw", CASES[1:])
-def test_mxfp4_with_hadamard(dev, orc, name, kw):
+@pytest.mark.parametrize("name,kw,dtype", MX_CASES)
+def test_mxfp4_with_hadamard(dev, orc, name, kw, dtype):
     """The rotation sums 128 products in fp32 on MFMA, so a value that sits on
     an E2M1 rounding boundary can round the other way than the oracle's
     correctly rounded sum: codes agree except on such boundary cases, and the
     dequantized values agree to within one code step."""
-    w = wl.WORKLOADS[name]
-    inp = wl.make_prefill(w, device=dev, **kw)
+    q, k = _mx_inputs(dev, name, kw, dtype)
     had = sage.Hadamard(0)
-    say("mxfp4 quantize (hadamard)", name, kw)
-    qk = sage.sage_quantize_qk(inp.q, inp.k, mode=sage.QK_MXFP4, hadamard=had)
+    say("mxfp4 quantize (hadamard)", name, kw, q.dtype)
+    qk = sage.sage_quantize_qk(q, k, mode=sage.QK_MXFP4, hadamard=had)
     torch.cuda.synchronize()
-    qc, kc = canon(inp.q), canon(inp.k)
+    qc, kc = canon(q), canon(k)
     mu = qk.k_mean.cpu().numpy()
     vals = np.array([orc.e2m1_decode(c) for c in range(16)], np.float32)
     for x, codes, e8 in ((orc.rotate(qc), qk.q, qk.q_scale),
