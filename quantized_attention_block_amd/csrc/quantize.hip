@@ -112,10 +112,12 @@ __global__ __launch_bounds__(kThreads) void k_mean_partial(HalfView k, int H, in
 }
 
 // Finish of one head's channel statistics: thread d folds channel d of the
-// head's nchunk chunk partials in chunk order.  The loads go out kFinishBatch
-// at a time, all in flight together, ahead of the (ordered) folds: one at a
-// time, the loop waited one memory latency per chunk (128 chunks: ~36 us).
-constexpr int kFinishBatch = 16;
+// head's nchunk chunk partials in chunk order.  The loads go out a batch at a
+// time (32 binary64 or 64 fp32 values, as many as fit in registers), all in
+// flight together, ahead of the (ordered) folds: one at a time, the loop
+// waited one memory latency per chunk (128 chunks: ~36 us).
+template <typename T>
+constexpr int kFinishBatch = sizeof(T) == 8 ? 32 : 64;
 
 // mu = fp32(sum / L) in binary64, chunk order.  Written to mu (if any) and,
 // as a binary64 value, over chunk 0's partial, where k_quant_int8 reads it.
@@ -124,12 +126,12 @@ __global__ void k_mean_final(double* partial, int nchunk, int L, float* mu) {
     const int bh = blockIdx.x, d = threadIdx.x;
     double* col = partial + (int64_t)bh * nchunk * D + d;
     double s = 0.0;
-    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch) {
-        double v[kFinishBatch];
+    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch<double>) {
+        double v[kFinishBatch<double>];
 #pragma unroll
-        for (int u = 0; u < kFinishBatch; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0;
+        for (int u = 0; u < kFinishBatch<double>; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0;
 #pragma unroll
-        for (int u = 0; u < kFinishBatch; ++u)
+        for (int u = 0; u < kFinishBatch<double>; ++u)
             if (c0 + u < nchunk) s += v[u];
     }
     const float m = L > 0 ? (float)(s / (double)L) : 0.0f;
@@ -144,12 +146,12 @@ __global__ void k_v_amax_final(float* partial, int nchunk, float* v_scale) {
     const int bh = blockIdx.x, d = threadIdx.x;
     float* col = partial + (int64_t)bh * nchunk * D + d;
     float a = 0.0f;
-    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch) {
-        float v[kFinishBatch];
+    for (int c0 = 0; c0 < nchunk; c0 += kFinishBatch<float>) {
+        float v[kFinishBatch<float>];
 #pragma unroll
-        for (int u = 0; u < kFinishBatch; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0f;
+        for (int u = 0; u < kFinishBatch<float>; ++u) v[u] = c0 + u < nchunk ? col[(int64_t)(c0 + u) * D] : 0.0f;
 #pragma unroll
-        for (int u = 0; u < kFinishBatch; ++u) a = fmaxf(a, v[u]);
+        for (int u = 0; u < kFinishBatch<float>; ++u) a = fmaxf(a, v[u]);
     }
     v_scale[(int64_t)bh * D + d] = a / kFp8Max;
     col[0] = a;
