@@ -209,6 +209,21 @@ def prefill_bench(wname, steps, warmup, dev, time_unfused=False, fused_q=True):
            "roofline": roof}
     if t_step_unfused is not None:
         res["ms_per_step_unfused_q"] = round(t_step_unfused * 1e3, 4)
+    if mode == sage.QK_INT8 and w.D == 128:
+        # the same attention under the wave-pair ping-pong schedule (same
+        # output bits, checked here before timing)
+        ref = out.clone()
+
+        def attn_pp():
+            sage.sage_attn_fwd(qk, v_q, v_s, causal=w.causal, sm_scale=w.sm_scale, out=out,
+                               q=inp.q if fused_q else None, schedule=sage.SCHED_PINGPONG)
+        attn_pp()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError(f"{wname}: the ping-pong schedule differs from the interleaved one")
+        t_pp = min(_events_time(attn_pp, max(3, reps // 2), stream) for _ in range(2))
+        res["pingpong_schedule"] = {"attn_kernel_us": round(t_pp * 1e6, 2),
+                                    "frac": round(ops_alg / t_pp / 1e12 / peak, 4)}
     del inp, qk, v_q, v_s, out, ws_qk, ws_v
     torch.cuda.empty_cache()
     return w, res

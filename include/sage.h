@@ -187,6 +187,19 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
  * num_kv_heads: K/V heads (H % num_kv_heads == 0; query head h reads KV head
  * h / (H / num_kv_heads)); 0 means H.  No workspace is needed (pass NULL, 0).
  */
+/* How the attention kernel's waves share a SIMD.  Both give the same output
+ * bits; they differ in speed only.
+ *   SAGE_SCHED_INTERLEAVED  workgroups of 4 waves (128 query rows), three per
+ *     CU: the hardware interleaves the waves' MFMA and softmax phases.
+ *   SAGE_SCHED_PINGPONG  workgroups of 8 waves (two 128-row query blocks of
+ *     one head, sharing every K/V tile), two waves per SIMD alternating an
+ *     MFMA phase (PV of the previous tile, QK of this one) and a softmax phase
+ *     between workgroup barriers, the two groups offset by one phase: the
+ *     wave-pair schedule of the "Sage2 SM89 Temporal Pair Experiment" README
+ *     (Candidate section).  INT8 QK with head dim 128 only
+ *     (SAGE_ERR_UNSUPPORTED otherwise). */
+typedef enum { SAGE_SCHED_INTERLEAVED = 0, SAGE_SCHED_PINGPONG = 1 } sage_attn_schedule;
+
 typedef struct {
     float sm_scale;        /* <= 0: 1/sqrt(D)                                  */
     int32_t causal;
@@ -197,6 +210,7 @@ typedef struct {
     /* SAGE_QK_MXFP4 with q_scale NULL only (else NULL): the rotation applied to
      * Q in the prologue; NULL there means no rotation */
     const sage_hadamard* hadamard;
+    int32_t schedule;      /* sage_attn_schedule (0: interleaved)              */
 } sage_attn_params;
 
 sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale,

@@ -398,6 +398,10 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
         return fail(SAGE_ERR_SHAPE, "MXFP4 attention needs head dim 128");
     if (D != 64 && D != 128) return fail(SAGE_ERR_SHAPE, "head dim %d not in {64, 128}", D);
     if (!std::isfinite(p->sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (p->schedule != SAGE_SCHED_INTERLEAVED && p->schedule != SAGE_SCHED_PINGPONG)
+        return fail(SAGE_ERR_INVALID_ARG, "params.schedule: unknown schedule %d", p->schedule);
+    if (p->schedule == SAGE_SCHED_PINGPONG && (p->qk_mode != SAGE_QK_INT8 || D != 128))
+        return fail(SAGE_ERR_UNSUPPORTED, "the ping-pong schedule needs INT8 QK and head dim 128");
     const int64_t Lqp = sage::pad128(Lq), Lkp = sage::pad128(Lk);
     sage_status st;
     // q_scale NULL: q_q is the fp16/bf16 Q itself, quantized in the kernel's
@@ -482,6 +486,7 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
     a.k_block = p->k_block;
     a.causal = p->causal;
     a.mxfp4 = p->qk_mode == SAGE_QK_MXFP4;
+    a.pingpong = p->schedule == SAGE_SCHED_PINGPONG;
     a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : (float)(1.0 / std::sqrt((double)D));
     return launch_status(sage::launch_attn_fwd(a, (hipStream_t)stream), "attention");
 }

@@ -353,17 +353,19 @@ __device__ __forceinline__ void load_q_rows(uint4 (&raw)[D / 16], const HalfView
     }
 }
 
-// The 128 rows of the block are one INT8 quantization block of Q: amax over
+// The 128 rows of four waves are one INT8 quantization block of Q: amax over
 // the block (rows past Lq are zeros), codes clamp(rne(x * (127 / amax)),
 // -127, 127), scale amax / 127 (returned) -- the arithmetic of the Q blocks of
 // the quantize kernels, so the codes and the scale are theirs bit for bit.
 // The clamp comes before the rounding (the bounds are integers, and a NaN
 // product still gives -127), and the rounding is the addition of 1.5 * 2^23,
 // whose result has spacing 1 and holds the code in its low byte.
-// red: 4 floats of LDS for the waves' amax.
+// red: LDS floats for the waves' amax; wave w writes red[w], the block's four
+// waves are red[red_base + 0..3]; one workgroup barrier between the writes
+// and the reads, so every wave of the workgroup calls this once.
 template <int D, bool BF16>
 __device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&raw)[D / 16], float* red,
-                                             int wave) {
+                                             int wave, int red_base = 0) {
     auto lo = [](uint32_t w) { return BF16 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu); };
     auto hi = [](uint32_t w) { return BF16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16); };
     float am = 0.0f;
@@ -376,9 +378,9 @@ __device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&
     am = wave_max(am);
     if ((threadIdx.x & 63) == 0) red[wave] = am;
     lds_barrier();
-    float amax = red[0];
+    float amax = red[red_base];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+    for (int w = 1; w < 4; ++w) amax = fmaxf(amax, red[red_base + w]);   // the block's four waves
     amax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax)));   // uniform
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
     // adding 1.5 * 2^23 rounds to the nearest integer (ties to even) and leaves
@@ -478,6 +480,132 @@ __device__ __forceinline__ void mx_fused_qfrag(QFrag<128, true>& qf, const AttnK
         qf.s[c] = (int)((e8 >> (8 * (2 * c + half))) & 0xFFu);
     }
     __syncthreads();   // every wave is done reading the Hadamard matrix from the ring
+}
+
+// Sub-tile states of the 64-key tile starting at key0 for one wave's query
+// rows [q0w, +32): 0 no key visible to any of the rows, 2 every key visible to
+// every row, 1 crossing (keys tested one by one).  FULL: all 2, no tests.
+template <bool FULL>
+__device__ __forceinline__ void tile_states(int (&st)[kNT], int key0, int Lk, bool causal, int q0w) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+        if constexpr (FULL) {
+            st[t] = 2;
+        } else {
+            const int lo = key0 + 32 * t, hi = lo + 31;
+            const bool empty = lo >= Lk || (causal && lo > q0w + 31);
+            const bool whole = hi < Lk && (!causal || hi <= q0w);
+            st[t] = empty ? 0 : (whole ? 2 : 1);
+        }
+    }
+}
+
+// The online-softmax step of one staged tile for this lane's query row qrow
+// (S: element (t, e) is key key0 + 32 t + 16 half + e; c the tile's score
+// scale): row max, the O / l rescale when some row's max grew, and
+// q = 448 * 2^(x - m) packed as the PV B operand into pf.  Returns the
+// tile's sum of q for l (added by the caller).
+template <int D, bool MX, bool FULL>
+__device__ __forceinline__ float tile_softmax(const SAccT<D, MX> (&S)[kNT], const int (&st)[kNT], int key0,
+                                              int half, int Lk, bool causal, int qrow, float c, float& m,
+                                              float& l, v16f (&O)[D / 32], v8i& pf) {
+    auto visible = [&](int t, int e) {
+        const int key = key0 + 32 * t + 16 * half + e;
+        return key < Lk && (!causal || key <= qrow);
+    };
+    // row max (on the integer scores for INT8: rounding is monotone)
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+        if (st[t] == 2) {
+            auto mx = S[t][0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = vmax(mx, S[t][e]);
+            tmax = fmaxf(tmax, score_f(mx) * c);
+        } else if (st[t] == 1) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c : -INFINITY);
+        }
+    }
+    const float m_new = fmaxf(m, half_pair_max(tmax));
+    // online-softmax rescale, skipped when no row's max moved; a row that
+    // has seen no key yet (m = -inf) holds O = 0 and l = 0, which the
+    // rescale by 0 leaves as they are, so its first max does not count
+    if (__any(m_new > m && m != -INFINITY)) {
+        const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+        l *= sc;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) O[i] *= sc;
+    }
+    m = m_new;
+    const float mb = (FULL || m_new != -INFINITY ? m_new : 0.0f) - kLog2Fp8Max;
+
+    // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
+    // accumulates q (so l = 448 * sum p).  Packed as the PV B operand:
+    // byte 16 t + e = key 32 t + 16 half + e of the tile.  The low-word
+    // conversion keeps the high word of its third operand, which the
+    // high-word conversion overwrites: the word's stale value is passed, so
+    // no register has to be zeroed first.
+    float ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const int t = w / 4, e0 = 4 * (w % 4);
+        if (st[t] == 0) {
+            pf[w] = 0;
+            continue;
+        }
+        float p[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            float xv = __builtin_fmaf(score_f(S[t][e0 + jj]), c, -mb);
+            if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
+            p[jj] = __builtin_amdgcn_exp2f(xv);
+        }
+        ls += (p[0] + p[1]) + (p[2] + p[3]);
+        uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], (uint32_t)pf[w]);
+        pk = cvt_pk_fp8<true>(p[2], p[3], pk);
+        pf[w] = (int)pk;
+    }
+    return ls;
+}
+
+// Epilogue: out = (O * v_scale) / l (times the reciprocal of l, one division
+// per row) for this lane's query row, written with the caller's strides.  vs:
+// the KV head's V scales in LDS.
+template <int D>
+__device__ __forceinline__ void store_rows(const AttnKernelArgs& a, const v16f (&O)[D / 32], float l,
+                                           const float* vs, int b, int h, int qrow, int half) {
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (qrow >= a.Lq) return;
+    const int64_t ooff = (int64_t)b * a.out.sB + (int64_t)qrow * a.out.sL + (int64_t)h * a.out.sH;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            float o[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o[jj] = (O[db][4 * i + jj] * vs[d0 + jj]) * inv_l;
+            if (a.out.dtype == kOutF32) {
+                *(float4*)((float*)a.out.ptr + ooff + d0) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+                uint32_t w[2];
+#pragma unroll
+                for (int jj = 0; jj < 4; jj += 2) {
+                    uint32_t h0, h1;
+                    if (a.out.dtype == kOutBF16) {
+                        h0 = __builtin_bit_cast(uint16_t, (__bf16)o[jj]);
+                        h1 = __builtin_bit_cast(uint16_t, (__bf16)o[jj + 1]);
+                    } else {
+                        h0 = __builtin_bit_cast(uint16_t, (_Float16)o[jj]);
+                        h1 = __builtin_bit_cast(uint16_t, (_Float16)o[jj + 1]);
+                    }
+                    w[jj / 2] = h0 | (h1 << 16);
+                }
+                *(uint2*)((uint16_t*)a.out.ptr + ooff + d0) = make_uint2(w[0], w[1]);
+            }
+        }
 }
 
 // QF: Q quantized in the prologue from the fp16/bf16 view qh (INT8 per
@@ -612,82 +740,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const float c = tile_c(j);
         const int key0 = j * kBN;
 
-        int st[kNT];   // 0 empty, 1 crossing, 2 full
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            if constexpr (FULL) {
-                st[t] = 2;
-            } else {
-                const int lo = key0 + 32 * t, hi = lo + 31;
-                const bool empty = lo >= a.Lk || (a.causal && lo > q0w + 31);
-                const bool whole = hi < a.Lk && (!a.causal || hi <= q0w);
-                st[t] = empty ? 0 : (whole ? 2 : 1);
-            }
-        }
-        auto visible = [&](int t, int e) {
-            const int key = key0 + 32 * t + 16 * half + e;
-            return key < a.Lk && (!a.causal || key <= qrow);
-        };
-
+        int st[kNT];
+        tile_states<FULL>(st, key0, a.Lk, a.causal, q0w);
         // S: element (t, e) is key key0 + 32 t + 16 half + e of query qrow
         SAcc S[kNT];
 #pragma unroll
         for (int t = 0; t < kNT; ++t) S[t] = qk_subtile<D, MX>(stage, qf, t, lane);
-
-        // row max (on the integer scores for INT8: rounding is monotone)
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            if (st[t] == 2) {
-                auto mx = S[t][0];
-#pragma unroll
-                for (int e = 1; e < 16; ++e) mx = vmax(mx, S[t][e]);
-                tmax = fmaxf(tmax, score_f(mx) * c);
-            } else if (st[t] == 1) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c : -INFINITY);
-            }
-        }
-        const float m_new = fmaxf(m, half_pair_max(tmax));
-        // online-softmax rescale, skipped when no row's max moved; a row that
-        // has seen no key yet (m = -inf) holds O = 0 and l = 0, which the
-        // rescale by 0 leaves as they are, so its first max does not count
-        if (__any(m_new > m && m != -INFINITY)) {
-            const float sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-            l *= sc;
-#pragma unroll
-            for (int i = 0; i < kDB; ++i) O[i] *= sc;
-        }
-        m = m_new;
-        const float mb = (FULL || m_new != -INFINITY ? m_new : 0.0f) - kLog2Fp8Max;
-
-        // q = 448 * 2^(x - m) evaluated as 2^(fma(S, c, -(m - log2 448))); l
-        // accumulates q (so l = 448 * sum p).  Packed as the PV B operand:
-        // byte 16 t + e = key 32 t + 16 half + e of the tile.  The low-word
-        // conversion keeps the high word of its third operand, which the
-        // high-word conversion overwrites: the word's stale value is passed, so
-        // no register has to be zeroed first.
-        float ls = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const int t = w / 4, e0 = 4 * (w % 4);
-            if (st[t] == 0) {
-                pf[w] = 0;
-                continue;
-            }
-            float p[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                float xv = __builtin_fmaf(score_f(S[t][e0 + jj]), c, -mb);
-                if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
-                p[jj] = __builtin_amdgcn_exp2f(xv);
-            }
-            ls += (p[0] + p[1]) + (p[2] + p[3]);
-            uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], (uint32_t)pf[w]);
-            pk = cvt_pk_fp8<true>(p[2], p[3], pk);
-            pf[w] = (int)pk;
-        }
+        const float ls = tile_softmax<D, MX, FULL>(S, st, key0, half, a.Lk, a.causal, qrow, c, m, l, O, pf);
         pv_tile<D, MX>(stage, pf, lane, O);
         l += ls;
     };
@@ -710,42 +769,172 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (; j < n_full; ++j) step(j, std::true_type{}, SR{});
     for (; j < ntiles; ++j) step(j, std::false_type{}, SR{});
 
-    // ---- epilogue: out = (O * v_scale) / l (times the reciprocal of l), written
-    // with the caller's strides
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;   // one division per row
-    if (qrow < a.Lq) {
-        const float* vs = (const float*)vs_lds;
-        const int64_t ooff = (int64_t)b * a.out.sB + (int64_t)qrow * a.out.sL + (int64_t)h * a.out.sH;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * half;
-                float o[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    o[jj] = (O[db][4 * i + jj] * vs[d0 + jj]) * inv_l;
-                if (a.out.dtype == kOutF32) {
-                    *(float4*)((float*)a.out.ptr + ooff + d0) = make_float4(o[0], o[1], o[2], o[3]);
-                } else {
-                    uint32_t w[2];
-#pragma unroll
-                    for (int jj = 0; jj < 4; jj += 2) {
-                        uint32_t h0, h1;
-                        if (a.out.dtype == kOutBF16) {
-                            h0 = __builtin_bit_cast(uint16_t, (__bf16)o[jj]);
-                            h1 = __builtin_bit_cast(uint16_t, (__bf16)o[jj + 1]);
-                        } else {
-                            h0 = __builtin_bit_cast(uint16_t, (_Float16)o[jj]);
-                            h1 = __builtin_bit_cast(uint16_t, (_Float16)o[jj + 1]);
-                        }
-                        w[jj / 2] = h0 | (h1 << 16);
-                    }
-                    *(uint2*)((uint16_t*)a.out.ptr + ooff + d0) = make_uint2(w[0], w[1]);
-                }
-            }
+    store_rows<D>(a, O, l, (const float*)vs_lds, b, h, qrow, half);
+}
+
+// ---- Wave-pair ping-pong schedule -------------------------------------------
+// The "Sage2 SM89 Temporal Pair Experiment" README (Candidate section) pairs
+// warps so that one pair runs QK and the softmax while the other runs PV of
+// the previous tile, then they swap.  Here: a workgroup of 8 waves = two
+// groups of four, each owning one 128-row Q block (two consecutive Q blocks of
+// one head), so every SIMD holds one wave of each group.  A wave alternates
+// two phases separated by workgroup barriers: X(j) = PV of tile j - 1 and QK
+// of tile j (MFMA work), Y(j) = the softmax of tile j (VALU work).  Group 1
+// passes one barrier more at the start, so whenever one group is in X the
+// other is in Y.  The K/V tiles are shared by the two groups (copied once per
+// 256 query rows) in a ring of four stages: tile j is read until X(j + 1) of
+// group 1, which ends at the barrier after which tile j + 4 is issued.  Per
+// row the arithmetic is the interleaved kernel's (the same helpers in the
+// same order), so the outputs are equal bit for bit.  INT8 QK, D = 128.
+constexpr int kPPWaves = 8;
+constexpr int kPPStages = 4;
+
+template <bool QF>
+__device__ __forceinline__ void attn_fwd_pp(const AttnKernelArgs& a, float alpha, const HalfView& qh) {
+    constexpr int D = 128;
+    constexpr bool MX = false;
+    using G = Geo<D, MX>;
+    using Dma = TileDma<D, MX, kPPWaves>;
+    using SAcc = SAccT<D, MX>;
+    constexpr int kDB = D / 32;
+    // DMA instructions one tile costs every wave
+    constexpr int kDma = Dma::kKRegions / kPPWaves + Dma::kVRegions / kPPWaves;
+    // the KV ring, the KV head's V scales (fp32 [D]), the waves' Q amax (QF)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kPPStages * G::kStageBytes + 512 + (QF ? 4 * kPPWaves : 0)];
+
+    const int Lqp = pad128(a.Lq), Lkp = pad128(a.Lk);
+    const int nqb = Lqp / kBM, npr = (nqb + 1) / 2;   // Q blocks, pairs of them
+    const int BH = a.B * a.H;
+    // causal: longest pairs first, heads fastest; otherwise head-major
+    int pr, bh;
+    if (a.causal) {
+        pr = npr - 1 - (int)(blockIdx.x / BH);
+        bh = (int)(blockIdx.x % BH);
+    } else {
+        bh = (int)(blockIdx.x / npr);
+        pr = (int)(blockIdx.x % npr);
     }
+    const int b = bh / a.H, h = bh % a.H;
+    const int hk = h / (a.H / a.Hkv);
+    const int bhk = b * a.Hkv + hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
+    const int half = lane >> 5, col = lane & 31;
+    // this group's Q block; qb == nqb (no rows) for the second group of the
+    // last pair when nqb is odd
+    const int qb = 2 * pr + grp;
+    const bool live = qb < nqb;
+    const int q0w = qb * kBM + wq * 32;
+    const int qrow = q0w + col;
+
+    // tiles this group visits, and the workgroup's (the later block's)
+    const int nkt = (a.Lk + kBN - 1) / kBN;
+    int my_nt = live ? nkt : 0;
+    if (a.causal && live) my_nt = min(my_nt, (qb * kBM + kBM - 1) / kBN + 1);
+    int nt = nkt;
+    if (a.causal) nt = min(nt, (min(2 * pr + 1, nqb - 1) * kBM + kBM - 1) / kBN + 1);
+    // tiles [0, n_full) are full for every row of this group
+    int n_full = a.Lk / kBN;
+    if (a.causal) n_full = min(n_full, qb * (kBM / kBN));
+
+    const uint8_t* kbase = (const uint8_t*)a.k + (int64_t)bhk * Lkp * G::kRowBytes;
+    const uint8_t* vbase = a.v + (int64_t)bhk * D * Lkp;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (int64_t)Lkp * G::kRowBytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (int64_t)D * Lkp);
+    auto stage_of = [&](int kt) { return smem + (kt % kPPStages) * G::kStageBytes; };
+
+    uint8_t* const vs_lds = smem + kPPStages * G::kStageBytes;
+    uint4 qraw[QF ? D / 16 : 1];
+    if constexpr (QF) load_q_rows<D>(qraw, qh, b, h, a.Lq, qrow, half);   // rows past Lq read as zeros
+    if (wave == 0 && lane < D / 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.v_scale + (int64_t)bhk * D, D * 4), vs_lds, 16,
+                                                 16 * lane, 0, 0, 0);
+    Dma::issue(stage_of(0), krs, krs, vrs, Lkp, 0, wave, lane);
+    if (nt > 1) Dma::issue(stage_of(1), krs, krs, vrs, Lkp, 1, wave, lane);
+
+    QFrag<D, MX> qf;
+    float q_s;
+    if constexpr (QF) {
+        float* red = (float*)(vs_lds + 512);
+        q_s = qh.bf16 ? quant_qfrag<D, true>(qf, qraw, red, wave, 4 * grp)
+                      : quant_qfrag<D, false>(qf, qraw, red, wave, 4 * grp);
+        q_s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, q_s)));
+    } else {
+        // a group without rows reads row 0 (in bounds) and computes nothing
+        const uint8_t* qbase = (const uint8_t*)a.q + (int64_t)bh * Lqp * G::kRowBytes;
+        load_qfrag<D, MX>(qf, qbase, nullptr, live ? qrow : 0, lane);
+        q_s = ((const float*)a.q_scale)[(int64_t)bh * (Lqp / a.q_block) + (live ? qb : 0) * kBM / a.q_block];
+    }
+    const __attribute__((address_space(4))) float* kscale_c =
+        (const __attribute__((address_space(4))) float*)((const float*)a.k_scale + (int64_t)bhk * (Lkp / a.k_block));
+    const int kshift = __builtin_amdgcn_readfirstlane(a.k_block == 2 * kBN ? 1 : 0);
+
+    v16f O[kDB];
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) O[i] = v16f{0};
+    float m = -INFINITY, l = 0.0f;
+    v8i pf = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // Tile j is first read in X(j) of group 0, so before the barrier that
+    // starts it every wave waits for its own copies of tile j: group 0 at its
+    // X(j) barrier, group 1 at the same barrier, which for it starts Y(j - 1)
+    // (or is its extra first barrier).  At either point a wave's most recent
+    // copies (tile j + 1) may still be in flight.
+    auto dma_wait_barrier = [&](int t) {   // every tile up to t landed
+        if (t + 1 < nt)
+            dma_barrier<kDma>();
+        else
+            dma_barrier<0>();
+    };
+    if (grp == 1) dma_wait_barrier(0);   // the second group runs one phase behind
+    for (int j = 0; j <= nt; ++j) {
+        // ---- X(j).  Every wave has finished X(j - 1), the last reader of the
+        // stage tile j + 2 reuses.
+        if (grp == 0)
+            dma_wait_barrier(j);
+        else
+            lds_barrier();
+        if (j + 2 < nt) Dma::issue(stage_of(j + 2), krs, krs, vrs, Lkp, j + 2, wave, lane);
+        if (j >= 1 && j - 1 < my_nt) pv_tile<D, MX>(stage_of(j - 1), pf, lane, O);
+        const bool qk = j < my_nt;
+        SAcc S[kNT];
+        if (qk) {
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) S[t] = qk_subtile<D, MX>(stage_of(j), qf, t, lane);
+        }
+        // ---- Y(j): the softmax of tile j (for group 1 this barrier starts X(j + 1) of group 0)
+        if (grp == 1)
+            dma_wait_barrier(j + 1);
+        else
+            lds_barrier();
+        if (qk) {
+            const float c = (q_s * kscale_c[j >> kshift]) * alpha;
+            const int key0 = j * kBN;
+            int st[kNT];
+            float ls;
+            if (j < n_full) {
+                tile_states<true>(st, key0, a.Lk, a.causal, q0w);
+                ls = tile_softmax<D, MX, true>(S, st, key0, half, a.Lk, a.causal, qrow, c, m, l, O, pf);
+            } else {
+                tile_states<false>(st, key0, a.Lk, a.causal, q0w);
+                ls = tile_softmax<D, MX, false>(S, st, key0, half, a.Lk, a.causal, qrow, c, m, l, O, pf);
+            }
+            l += ls;
+        }
+    }
+    if (grp == 0) lds_barrier();   // both groups pass the same number of barriers
+
+    if (live) store_rows<D>(a, O, l, (const float*)vs_lds, b, h, qrow, half);
+}
+
+// (Two kernels around one template body: with a kernel template here this
+// compiler emitted the host launch stub of only the first instantiation.)
+__global__ __launch_bounds__(64 * kPPWaves) void k_attn_fwd_pp_fused_q(AttnKernelArgs a, float alpha, HalfView qh) {
+    attn_fwd_pp<true>(a, alpha, qh);
+}
+__global__ __launch_bounds__(64 * kPPWaves) void k_attn_fwd_pp(AttnKernelArgs a, float alpha, HalfView qh) {
+    attn_fwd_pp<false>(a, alpha, qh);
 }
 
 // Test hook: int32 S = Q8 K8^T through the same staging and qk_subtile_i8 as
@@ -821,6 +1010,14 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     const AttnKernelArgs k{a.q, a.q_scale, a.k, a.k_scale, a.v, a.v_scale, a.out, a.B, a.H, a.Hkv,
                            a.Lq, a.Lk, a.D, a.q_block, a.k_block, a.causal,
                            a.q_fused ? (a.qh.bf16 ? a.hmat_bf16 : a.hmat_f16) : nullptr, a.inv_sqrt_r};
+    if (a.pingpong) {   // INT8, D 128 (checked by the caller)
+        dim3 pgrid((unsigned)((nqb + 1) / 2 * a.B * a.H));
+        if (a.q_fused)
+            k_attn_fwd_pp_fused_q<<<pgrid, 64 * kPPWaves, 0, stream>>>(k, alpha, a.qh);
+        else
+            k_attn_fwd_pp<<<pgrid, 64 * kPPWaves, 0, stream>>>(k, alpha, a.qh);
+        return hipGetLastError();
+    }
     if (a.mxfp4) {
         if (a.q_fused)
             k_attn_fwd<128, true, true><<<grid, kThreads, 0, stream>>>(k, alpha, a.qh);

@@ -84,6 +84,7 @@ struct AttnArgs {
     int q_block, k_block;
     int causal;
     int mxfp4;
+    int pingpong;         // the wave-pair schedule (INT8, D 128): 8-wave workgroups
     float sm_scale;
     // q_fused: Q is the caller's fp16/bf16 [B, Lq, H, D] view qh (q and
     // q_scale unused), quantized in the prologue: INT8 per 128-row block, or

@@ -30,6 +30,7 @@ STATUS_NAMES = ["SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_DTYPE", "SAGE_ERR_S
 # sage_dtype
 F16, BF16, F32, I8, I32, U8, FP8_E4M3FN, FP8_E4M3FNUZ, FP4X2_E2M1, E8M0 = range(1, 11)
 QK_INT8, QK_MXFP4 = 0, 1
+SCHED_INTERLEAVED, SCHED_PINGPONG = 0, 1   # sage_attn_schedule
 DECODE_SCRATCH_BYTES = 32 << 20   # SAGE_DECODE_SCRATCH_BYTES: scratch of sage_paged_decode_noalloc
 
 _TORCH_DTYPES = {
@@ -66,7 +67,7 @@ class AttnParams(ctypes.Structure):
                 ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("q_block", ctypes.c_int32), ("k_block", ctypes.c_int32),
-                ("hadamard", ctypes.c_void_p)]
+                ("hadamard", ctypes.c_void_p), ("schedule", ctypes.c_int32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -308,12 +309,14 @@ def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, 
                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                   out_dtype: torch.dtype = torch.bfloat16, num_kv_heads: int = 0,
                   q: Optional[torch.Tensor] = None,
-                  hadamard: Optional[Hadamard] = None) -> torch.Tensor:
+                  hadamard: Optional[Hadamard] = None,
+                  schedule: int = SCHED_INTERLEAVED) -> torch.Tensor:
     """Quantized attention; `out` is a logical [B, Lq, H, D] fp16/bf16 tensor
     with any B/L/H strides (allocated contiguous when None).  When qk holds K
     alone (sage_quantize_qk(None, k)), `q` is the fp16/bf16 [B, Lq, H, D] Q,
     quantized in the kernel's prologue to the same codes and scales as
-    sage_quantize_qk's (MXFP4: rotated by `hadamard`, None for no rotation)."""
+    sage_quantize_qk's (MXFP4: rotated by `hadamard`, None for no rotation).
+    `schedule`: SCHED_INTERLEAVED or SCHED_PINGPONG (same output bits)."""
     if (qk.q is None) != (q is not None):
         raise ValueError("pass q exactly when qk was quantized without Q")
     if q is not None:
@@ -327,7 +330,7 @@ def sage_attn_fwd(qk: QuantizedQK, v_q: torch.Tensor, v_scale: torch.Tensor, *, 
         out = torch.empty((B, Lq, H, D), dtype=out_dtype, device=dev)
     prm = AttnParams(float(sm_scale), int(causal), qk.mode, B, H, Lq, qk.Lk, D,
                      num_kv_heads, qk.q_block, qk.k_block,
-                     hadamard.handle if hadamard is not None else None)
+                     hadamard.handle if hadamard is not None else None, int(schedule))
     mx = qk.mode == QK_MXFP4
     kd = desc(qk.k, FP4X2_E2M1) if mx else desc(qk.k)
     ksd = desc(qk.k_scale, E8M0) if mx else desc(qk.k_scale)

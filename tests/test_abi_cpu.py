@@ -167,6 +167,11 @@ def test_attn_fwd_refusals(S):
     assert call(P(), out_=T(S.F32, (B, L, H, D), stride=(L * H * D, H * D, 2 * D + 2, 1))) == S.ERR_ALIGNMENT
     assert call(P(seqlen_q=300)) == S.ERR_SHAPE          # q_q padded length no longer matches
     assert call(P(sm_scale=float("nan"))) == S.ERR_INVALID_ARG
+    # the ping-pong schedule: INT8 QK, head dim 128 only; unknown schedules refused
+    assert call(P(schedule=2)) == S.ERR_INVALID_ARG
+    assert call(P(schedule=S.SCHED_PINGPONG, head_dim=64)) == S.ERR_UNSUPPORTED
+    assert call(P(schedule=S.SCHED_PINGPONG, qk_mode=S.QK_MXFP4)) == S.ERR_UNSUPPORTED
+    assert "ping-pong" in S.lib().sage_last_error().decode()
 
 
 def test_paged_decode_refusals(S):

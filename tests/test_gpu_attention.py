@@ -373,6 +373,37 @@ def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
     assert torch.equal(bf, ref.to(dtype))
 
 
+@pytest.mark.parametrize("name,Lq,Lk,H,Hkv,causal,fused,out_dtype", [
+    ("llm_prefill", 1100, 1100, 3, 3, True, True, torch.bfloat16),     # 9 Q blocks: the last pair has one
+    ("llm_prefill", 4096, 4096, 2, 2, True, True, torch.bfloat16),     # the benchmark's rows, two heads
+    ("video_dit", 1000, 1000, 3, 3, False, True, torch.bfloat16),      # ragged tail, strided views
+    ("video_dit", 700, 1500, 2, 2, False, False, torch.float32),       # Lq != Lk, Q quantized beforehand
+    ("llm_prefill", 520, 520, 4, 2, True, True, torch.float16),        # GQA, 4 query heads on 2 KV heads
+    ("video_dit", 32760, 32760, 1, 1, False, True, torch.bfloat16),    # the full video-DiT length, one head
+])
+def test_pingpong_schedule_equals_interleaved(dev, name, Lq, Lk, H, Hkv, causal, fused, out_dtype):
+    """The wave-pair ping-pong schedule (8-wave workgroups over two Q blocks,
+    MFMA and softmax phases of the two wave groups alternating) runs each
+    row's arithmetic in the interleaved kernel's order: outputs equal bit for
+    bit (the interleaved kernel is the one checked against the oracle)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, Lq=Lq, Lk=Lk, H=H, device=dev)
+    q, k, v = inp.q, inp.k, inp.v
+    if Hkv != H:
+        k, v = k[:, :, :Hkv], v[:, :, :Hkv]
+    say("ping-pong schedule", name, Lq, Lk, H, Hkv, causal, "fused Q" if fused else "Q codes", out_dtype)
+    qk = sage.sage_quantize_qk(None if fused else q, k, want_mean=False)
+    v_q, v_s = sage.sage_quantize_v(v)
+    kw = dict(causal=causal, sm_scale=w.sm_scale, out_dtype=out_dtype, num_kv_heads=Hkv,
+              q=q if fused else None)
+    ref = sage.sage_attn_fwd(qk, v_q, v_s, **kw)
+    got = sage.sage_attn_fwd(qk, v_q, v_s, schedule=sage.SCHED_PINGPONG, **kw)
+    again = sage.sage_attn_fwd(qk, v_q, v_s, schedule=sage.SCHED_PINGPONG, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(again, ref)
+
+
 @pytest.mark.parametrize("Lq,Lk,H,dtype,rotate", [
     (1000, 1000, 2, torch.bfloat16, True),      # strided video-DiT views, ragged last block
     (333, 333, 2, torch.bfloat16, False),       # no rotation
