@@ -459,6 +459,8 @@ def main():
              "attn_kernel_tops_literal": r["attn_kernel_tops_literal"],
              "quantize_qk_us": r["quantize_qk_us"], "quantize_v_us": r["quantize_v_us"],
              "ms_per_step_hip_graph": r["ms_per_step_hip_graph"]}
+    if "pingpong_schedule" in r:
+        extra["pingpong_schedule"] = r["pingpong_schedule"]
     if not args.no_extra:
         for wn in ("video_dit_mxfp4", "llm_prefill"):
             _, rr = prefill_bench(wn, args.steps, args.warmup, dev, time_unfused=True)
