@@ -513,18 +513,29 @@ __device__ __forceinline__ float tile_softmax(const SAccT<D, MX> (&S)[kNT], cons
         const int key = key0 + 32 * t + 16 * half + e;
         return key < Lk && (!causal || key <= qrow);
     };
-    // row max (on the integer scores for INT8: rounding is monotone)
+    // row max (on the integer scores for INT8: rounding is monotone, and
+    // c > 0, so the max of the scaled scores is the scaled max score)
     float tmax = -INFINITY;
+    if constexpr (FULL) {
+        auto mx = S[0][0];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-        if (st[t] == 2) {
-            auto mx = S[t][0];
+        for (int t = 0; t < kNT; ++t)
 #pragma unroll
-            for (int e = 1; e < 16; ++e) mx = vmax(mx, S[t][e]);
-            tmax = fmaxf(tmax, score_f(mx) * c);
-        } else if (st[t] == 1) {
+            for (int e = t == 0 ? 1 : 0; e < 16; ++e) mx = vmax(mx, S[t][e]);
+        tmax = score_f(mx) * c;
+    } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c : -INFINITY);
+        for (int t = 0; t < kNT; ++t) {
+            if (st[t] == 2) {
+                auto mx = S[t][0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) mx = vmax(mx, S[t][e]);
+                tmax = fmaxf(tmax, score_f(mx) * c);
+            } else if (st[t] == 1) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    tmax = fmaxf(tmax, visible(t, e) ? score_f(S[t][e]) * c : -INFINITY);
+            }
         }
     }
     const float m_new = fmaxf(m, half_pair_max(tmax));
@@ -561,7 +572,12 @@ __device__ __forceinline__ float tile_softmax(const SAccT<D, MX> (&S)[kNT], cons
             if (st[t] == 1 && !visible(t, e0 + jj)) xv = -INFINITY;
             p[jj] = __builtin_amdgcn_exp2f(xv);
         }
-        ls += (p[0] + p[1]) + (p[2] + p[3]);
+        // (in a full tile the first word's sum starts ls: 0 + x = x for the
+        // non-negative x here, so the sum is the same)
+        if (FULL && w == 0)
+            ls = (p[0] + p[1]) + (p[2] + p[3]);
+        else
+            ls += (p[0] + p[1]) + (p[2] + p[3]);
         uint32_t pk = cvt_pk_fp8<false>(p[0], p[1], (uint32_t)pf[w]);
         pk = cvt_pk_fp8<true>(p[2], p[3], pk);
         pf[w] = (int)pk;
