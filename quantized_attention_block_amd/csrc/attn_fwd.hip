@@ -22,7 +22,9 @@
 //    other waves of its SIMD issue VALU and MFMA work.  (A software-pipelined
 //    form of the loop, QK of tile j+1 and PV of tile j-1 around the softmax of
 //    tile j, needs ~226 VGPRs and so runs two waves per SIMD; it measured
-//    7-10 % slower.)
+//    7-10 % slower.  The wave-pair ping-pong schedule further down, two waves
+//    per SIMD alternating MFMA and softmax phases between barriers, is kept
+//    as an option; it measured about 1.4x slower.)
 //  - KV tiles of 64 keys are copied global -> LDS with 16-byte
 //    buffer_load ... lds instructions (no staging registers) into a ring of
 //    three LDS stages, two tiles ahead of use.  The per-tile barrier waits
