@@ -380,6 +380,8 @@ def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
     ("video_dit", 700, 1500, 2, 2, False, False, torch.float32),       # Lq != Lk, Q quantized beforehand
     ("llm_prefill", 520, 520, 4, 2, True, True, torch.float16),        # GQA, 4 query heads on 2 KV heads
     ("video_dit", 32760, 32760, 1, 1, False, True, torch.bfloat16),    # the full video-DiT length, one head
+    ("llm_prefill", 1, 1, 2, 2, True, True, torch.bfloat16),           # one row: one tile, second group empty
+    ("video_dit", 100, 3000, 2, 2, False, False, torch.float32),       # one Q block against 47 tiles
 ])
 def test_pingpong_schedule_equals_interleaved(dev, name, Lq, Lk, H, Hkv, causal, fused, out_dtype):
     """The wave-pair ping-pong schedule (8-wave workgroups over two Q blocks,
