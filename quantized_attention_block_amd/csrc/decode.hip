@@ -545,8 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
     const float Mo = (rmax == -INFINITY ? 0.0f : M) - lp;
     float ls = 0.0f;
     v8i pf[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    auto probs = [&](int g) {
         const int kl0 = 128 * g + 32 * q4;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -565,24 +564,20 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             const uint32_t c0 = cvt_pk_fp8<false>(pp[0], pp[1], 0);
             pf[g][m] = (int)cvt_pk_fp8<true>(pp[2], pp[3], c0);
         }
-    }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    ls = MX ? ls / kFp8Max : (vmax > 0.0f ? (ls * vmax) / kFp8Max : ls);
-
+    };
     // ---- 7. O^T = V^T P^T: element i of lane l of d-block db is channel
     // 16 db + 4 (l / 16) + i of query row r
     constexpr int kDB = 8 * kPlanes;
     const bool all_in = t0 + kTile <= ctx;   // no page slot past the context in this tile
     v4f O[kDB];
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-        O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        const int p = db / 8, dl = 16 * (db % 8) + c16;   // plane, channel within the plane
-        const uint8_t* vplane = vt_s + p * kPlaneB;
+    for (int db = 0; db < kDB; ++db) O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    auto pv = [&](int g) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int k0 = 128 * g + 32 * q4;           // tile-relative first key of this lane's 32
+        for (int db = 0; db < kDB; ++db) {
+            const int p = db / 8, dl = 16 * (db % 8) + c16;   // plane, channel within the plane
+            const uint8_t* vplane = vt_s + p * kPlaneB;
+            const int k0 = 128 * g + 32 * q4;                // tile-relative first key of this lane's 32
             if constexpr (MX) {
                 // 16 bytes of V^T row d (keys [k0, +32), E2M1; any finite
                 // value past ctx meets P = 0) and that block's E8M0 byte; a
@@ -637,7 +632,19 @@ __global__ __launch_bounds__(kThreads) void k_paged_decode(DecodeArgs a, float a
             }
             O[db] = mfma_f8_16x16x128(av, pf[g], O[db]);
         }
-    }
+    };
+    // The probabilities of key group g, then its PV products: group 1's exp2
+    // work is issued after group 0's MFMAs, so the two overlap (the same
+    // operations, and the same accumulation orders, as all probabilities
+    // first; -0.5 % per call).
+    probs(0);
+    pv(0);
+    probs(1);
+    pv(1);
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    ls = MX ? ls / kFp8Max : (vmax > 0.0f ? (ls * vmax) / kFp8Max : ls);
+
     // An MFMA reads its operands from every lane, whatever the exec mask: the
     // PV products (and the P packing and V reads feeding them) must not be
     // moved into the r < R branch below, where the padding rows' lanes would
