@@ -162,6 +162,20 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* How the attention kernel's waves share a SIMD.  Both give the same output
+ * bits; they differ in speed only.
+ *   SAGE_SCHED_INTERLEAVED  workgroups of 4 waves (128 query rows), three per
+ *     CU: the hardware interleaves the waves' MFMA and softmax phases.
+ *   SAGE_SCHED_PINGPONG  workgroups of 8 waves (two 128-row query blocks of
+ *     one head, sharing every K/V tile), two waves per SIMD alternating an
+ *     MFMA phase (PV of the previous tile, QK of this one) and a softmax phase
+ *     between workgroup barriers, the two groups offset by one phase: the
+ *     wave-pair schedule of the "Sage2 SM89 Temporal Pair Experiment" README
+ *     (Candidate section).  INT8 QK with head dim 128 only
+ *     (SAGE_ERR_UNSUPPORTED otherwise).
+ * Any other value is refused with SAGE_ERR_INVALID_ARG. */
+typedef enum { SAGE_SCHED_INTERLEAVED = 0, SAGE_SCHED_PINGPONG = 1 } sage_attn_schedule;
+
 /* Quantized attention forward.  For each query row, KV tiles of
  * sage_attn_kv_tile() keys in ascending order (the online-softmax block size,
  * so part of the numeric result): S = QK^T on INT8 (or scaled MXFP4) MFMA with int32 (fp32)
@@ -187,18 +201,6 @@ sage_status sage_quantize_v(const sage_tensor* v, const sage_tensor* v_out,
  * num_kv_heads: K/V heads (H % num_kv_heads == 0; query head h reads KV head
  * h / (H / num_kv_heads)); 0 means H.  No workspace is needed (pass NULL, 0).
  */
-/* How the attention kernel's waves share a SIMD.  Both give the same output
- * bits; they differ in speed only.
- *   SAGE_SCHED_INTERLEAVED  workgroups of 4 waves (128 query rows), three per
- *     CU: the hardware interleaves the waves' MFMA and softmax phases.
- *   SAGE_SCHED_PINGPONG  workgroups of 8 waves (two 128-row query blocks of
- *     one head, sharing every K/V tile), two waves per SIMD alternating an
- *     MFMA phase (PV of the previous tile, QK of this one) and a softmax phase
- *     between workgroup barriers, the two groups offset by one phase: the
- *     wave-pair schedule of the "Sage2 SM89 Temporal Pair Experiment" README
- *     (Candidate section).  INT8 QK with head dim 128 only
- *     (SAGE_ERR_UNSUPPORTED otherwise). */
-typedef enum { SAGE_SCHED_INTERLEAVED = 0, SAGE_SCHED_PINGPONG = 1 } sage_attn_schedule;
 
 typedef struct {
     float sm_scale;        /* <= 0: 1/sqrt(D)                                  */
