@@ -167,6 +167,24 @@ def test_int8_attention_matches_oracle(dev, orc, name, kw, causal):
     _check(canon(out), ref, exact, orc_exact=cosine(ref, exact) if name == "video_dit" else None)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_int8_attention_fp16_inputs_d128(dev, orc, causal):
+    """fp16 Q/K/V at head dim 128 (the D-128 workloads are bf16): the fp16
+    paths of the quantizers and of the fused-Q prologue against the oracle."""
+    w = wl.WORKLOADS["llm_prefill"]
+    inp = wl.make_prefill(w, device=dev, Lq=520, Lk=520, B=1, H=2)
+    q, k, v = (x.to(torch.float16) for x in (inp.q, inp.k, inp.v))
+    say("int8 attention, fp16 inputs, D 128", causal)
+    kq = sage.sage_quantize_qk(None, k)
+    v_q, v_s = sage.sage_quantize_v(v)
+    out = sage.sage_attn_fwd(kq, v_q, v_s, causal=causal, sm_scale=w.sm_scale, out_dtype=torch.float32, q=q)
+    torch.cuda.synchronize()
+    qc, kc, vc = canon(q), canon(k), canon(v)
+    ref, _ = orc.prefill_int8_pipeline(qc, kc, vc, causal=causal, sm_scale=w.sm_scale, BN=BN,
+                                       mu=kq.k_mean.cpu().numpy())
+    _check(canon(out), ref, orc.attn_exact(qc, kc, vc, causal, w.sm_scale))
+
+
 def test_gqa(dev, orc):
     """8 query heads on 2 KV heads: query head h reads KV head h // 4."""
     w = wl.WORKLOADS["llm_prefill"]
@@ -348,6 +366,7 @@ def test_boundary_lengths(dev, orc, L):
     ("llm_prefill", 4096, 128, True, torch.bfloat16),    # the benchmark's shape
     ("video_dit", 1000, 128, False, torch.bfloat16),     # outlier-heavy Q blocks
     ("llm_prefill", 200, 64, True, torch.float16),
+    ("llm_prefill", 520, 128, True, torch.float16),     # fp16 at D 128
     ("video_dit", -700, 128, False, torch.bfloat16),     # Lq 700 against Lk 1500
 ])
 def test_fused_q_quantization_equals_unfused(dev, name, Lq, D, causal, dtype):
