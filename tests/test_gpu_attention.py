@@ -167,6 +167,29 @@ def test_int8_attention_matches_oracle(dev, orc, name, kw, causal):
     _check(canon(out), ref, exact, orc_exact=cosine(ref, exact) if name == "video_dit" else None)
 
 
+@pytest.mark.parametrize("name,kw,causal", [
+    ("llm_prefill", dict(Lq=520, Lk=520, B=1, H=2), True),
+    ("video_dit", dict(Lq=700, Lk=1000, H=2), False),
+])
+def test_int8_attention_k_block_128(dev, orc, name, kw, causal):
+    """K quantized per 128 keys: each 64-key tile takes the scale of the
+    128-key block it lies in (both schedules for D 128)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_prefill(w, device=dev, **kw)
+    say("int8 attention, k_block 128", name, kw, causal)
+    out, qk = _gpu_out(inp, causal, w.sm_scale, k_block=128)
+    q, k, v = canon(inp.q), canon(inp.k), canon(inp.v)
+    ref, _ = orc.prefill_int8_pipeline(q, k, v, causal=causal, sm_scale=w.sm_scale, BN=BN, k_block=128,
+                                       mu=qk.k_mean.cpu().numpy())
+    _check(canon(out), ref, orc.attn_exact(q, k, v, causal, w.sm_scale),
+           orc_exact=cosine(ref, orc.attn_exact(q, k, v, causal, w.sm_scale)) if name == "video_dit" else None)
+    v_q, v_s = sage.sage_quantize_v(inp.v)
+    pp = sage.sage_attn_fwd(qk, v_q, v_s, causal=causal, sm_scale=w.sm_scale, out_dtype=torch.float32,
+                            schedule=sage.SCHED_PINGPONG)
+    torch.cuda.synchronize()
+    assert torch.equal(pp, out)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_int8_attention_fp16_inputs_d128(dev, orc, causal):
     """fp16 Q/K/V at head dim 128 (the D-128 workloads are bf16): the fp16
