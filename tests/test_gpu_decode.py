@@ -165,6 +165,28 @@ def test_paged_decode_more_than_32_splits(dev, orc, window, ctx, mtp):
     _check(g, _oracle(orc, inp, window, base.sm_scale), _oracle(orc, inp, window, base.sm_scale, False))
 
 
+# Contexts 0 (no query position), 1 and 3 (below MTP 4: the first query
+# tokens sit at negative positions and see no key), 4 and 5; 814 with window
+# 300 starts the window at key 511, so its first split holds one key that only
+# query token 0 sees and the other three rows are empty in that split.
+DEGENERATE_CTX = [0, 1, 3, 4, 5, 814]
+
+
+def test_paged_decode_degenerate_contexts(dev, orc):
+    """Rows with no visible key anywhere are 0; rows with none in one split
+    take nothing from it; the rest match the oracle."""
+    w = wl.WORKLOADS["paged_decode"]
+    inp = wl.make_decode(w, batch=len(DEGENERATE_CTX), ctx=814)
+    inp.ctx_lens[:] = torch.tensor(DEGENERATE_CTX, dtype=torch.int32)
+    say("paged decode, degenerate contexts", DEGENERATE_CTX)
+    g = _run(inp, dev, 300, 814, w.sm_scale)
+    o = _oracle(orc, inp, 300, w.sm_scale)
+    assert np.isfinite(g).all()
+    assert not g[0].any() and not g[1, :3].any() and not g[2, :1].any()   # positions < 0
+    assert not g[(o == 0).all(axis=-1)].any()                             # every empty row
+    _check(g, o, _oracle(orc, inp, 300, w.sm_scale, False))
+
+
 def test_paged_decode_context_above_max_ctx(dev, orc):
     """A context length above params.max_ctx (the page table still covering
     it) is treated as max_ctx: the output is finite and equals the oracle's at

@@ -84,6 +84,23 @@ def test_mx_decode_windows_and_contexts(dev, orc, window, ctx):
     _check(g, _oracle(orc, inp, window, w.sm_scale), _exact(orc, inp, window, w.sm_scale))
 
 
+def test_mx_decode_degenerate_contexts(dev, orc):
+    """Contexts 0, 1, 3 (query tokens at negative positions), 4, 5 and 814
+    with window 300 (a first split that only query token 0 sees): empty rows
+    are 0, the rest match the oracle."""
+    w = wl.WORKLOADS["paged_decode"]
+    ctxs = [0, 1, 3, 4, 5, 814]
+    inp = wl.make_decode_mx(w, batch=len(ctxs), ctx=814)
+    inp.ctx_lens[:] = torch.tensor(ctxs, dtype=torch.int32)
+    say("MXFP4 paged decode, degenerate contexts", ctxs)
+    g = _run(inp, dev, 300, 814, w.sm_scale)
+    o = _oracle(orc, inp, 300, w.sm_scale)
+    assert np.isfinite(g).all()
+    assert not g[0].any() and not g[1, :3].any() and not g[2, :1].any()
+    assert not g[(o == 0).all(axis=-1)].any()                             # every empty row
+    _check(g, o, _exact(orc, inp, 300, w.sm_scale))
+
+
 @pytest.mark.parametrize("mtp,hq,hkv,page", [(1, 8, 1, 64), (2, 16, 2, 256), (4, 16, 1, 512)])
 def test_mx_decode_shapes(dev, orc, mtp, hq, hkv, page):
     base = wl.WORKLOADS["paged_decode"]
