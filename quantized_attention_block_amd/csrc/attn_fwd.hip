@@ -377,7 +377,7 @@ __device__ __forceinline__ float quant_qfrag(QFrag<D, false>& qf, const uint4 (&
 #pragma unroll
         for (int i = 0; i < 4; ++i) am = fmaxf(fmaxf(am, fabsf(lo(w[i]))), fabsf(hi(w[i])));
     }
-    am = wave_max(am);
+    am = wave_max_xor(am);
     if ((threadIdx.x & 63) == 0) red[wave] = am;
     lds_barrier();
     float amax = red[red_base];

@@ -680,7 +680,9 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
     using Word = typename std::conditional<kCh == 2, uint32_t, uint2>::type;
     constexpr int kPB = part_bytes(DD);
     const int lane = threadIdx.x & 63;
-    const int rowg = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    // (the row is the wave's: read into a scalar register, the split count
+    // and every per-split condition below are scalar too)
+    const int rowg = __builtin_amdgcn_readfirstlane(blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6));
     const int R = a.MTP * (a.Hq / a.Hkv);
     const int bk = rowg / kRows, r = rowg % kRows;
     if (bk >= a.B * a.Hkv || r >= R) return;
@@ -738,8 +740,10 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void k_decode_merge(Decode
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             if (u < n) {
-                const float wj = __shfl(ow, u);
-                L = L + __shfl(lw, u);
+                // lane u's weights, read into scalar registers (u is a
+                // constant once unrolled: no LDS round trip per split)
+                const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ow), u));
+                L = L + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lw), u));
                 const uint32_t* hw = (const uint32_t*)&w[u];
 #pragma unroll
                 for (int c = 0; c < kCh / 2; ++c) {

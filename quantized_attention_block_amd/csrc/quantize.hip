@@ -62,7 +62,7 @@ struct ChunkRows {
 };
 
 __device__ __forceinline__ float block_max(float v, float* red) {
-    v = wave_max(v);
+    v = wave_max_xor(v);
     const int w = threadIdx.x / 64;
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8(HalfView q, HalfView k,
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
         if (row < L) am[p < G::kPasses / 2 ? 0 : 1] = fmaxf(am[p < G::kPasses / 2 ? 0 : 1], m);
     }
-    am[0] = wave_max(am[0]);
-    am[1] = wave_max(am[1]);
+    am[0] = wave_max_xor(am[0]);
+    am[1] = wave_max_xor(am[1]);
     if ((threadIdx.x & 63) == 0) {
         red[threadIdx.x / 64][0] = am[0];
         red[threadIdx.x / 64][1] = am[1];
@@ -558,7 +558,7 @@ __device__ __forceinline__ void quant_q_block(const HalfView& q, int b, int h, i
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
         if (row0 + p * G::kRowsPerPass + r0 < L) am = fmaxf(am, m);
     }
-    am = wave_max(am);
+    am = wave_max_xor(am);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = am;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) asm("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if (row0 + p * G::kRowsPerPass + r0 < L) am[p / kPer64] = fmaxf(am[p / kPer64], m);
     }
 #pragma unroll
-    for (int j = 0; j < kB64; ++j) am[j] = wave_max(am[j]);
+    for (int j = 0; j < kB64; ++j) am[j] = wave_max_xor(am[j]);
     if ((threadIdx.x & 63) == 0)
 #pragma unroll
         for (int j = 0; j < kB64; ++j) red[threadIdx.x / 64][j] = am[j];

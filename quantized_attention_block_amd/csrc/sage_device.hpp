@@ -204,10 +204,35 @@ __device__ __forceinline__ void mx_quant_rows(const float (&y)[4][16], int (&ex)
     }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Max over the wave, in every lane, by an xor butterfly of lane shuffles
+// (LDS permutes).  Used where registers are at their limit: the DPP form
+// below needs one more live register.
+__device__ __forceinline__ float wave_max_xor(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
+}
+
+// max of v and the value of the lane that DPP control CTRL names (all rows
+// and banks enabled; the controls used stay inside a 16-lane row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF,
+                                                                 0xF, false)));
+}
+
+// Max over the wave, in every lane, with no LDS round trip: within each quad
+// (lane ^ 1, lane ^ 2: quad_perm), across the two quads of a half-row
+// (row_half_mirror), the two halves of a row (row_mirror), then across rows
+// with v_permlane16_swap (lane ^ 16) and v_permlane32_swap (lane ^ 32).
+__device__ __forceinline__ float wave_max(float v) {
+    v = dpp_max<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_max<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_max<0x141>(v);   // row_half_mirror
+    v = dpp_max<0x140>(v);   // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return half_pair_max(v);
 }
 
 }  // namespace sage
