@@ -282,7 +282,9 @@ def decode_bench(steps, warmup, dev, pools=32, mx=False):
     graph.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    t = min(_events_time(graph.replay, max(10, steps), stream) for _ in range(5)) / pools
+    # five timed runs of max(10, steps) replays each, median (the pages' decode
+    # timing takes the median of five runs of many calls)
+    t = statistics.median(_events_time(graph.replay, max(10, steps), stream) for _ in range(5)) / pools
     t_eager = _events_time(call, 200, stream)
     keys = min(w.ctx, w.window + w.mtp - 1)
     # bytes per key and KV head: K and V codes plus their scales (e4m3: D + D

@@ -9,7 +9,9 @@ traffic <out.json> <copy_bytes> <copy_rd_dir>,<copy_wr_dir> <label>=<rd_dir>,<wr
     64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B, bytes written =
     64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) (the
     first pass per label collects the four read counters, the second the
-    two write counters; rocprofv3 --pmc -f csv).  No scale factor is
+    two write counters; rocprofv3 --pmc -f csv).  Entries of an existing
+    <out.json> whose label is not given again are kept, so one workload can
+    be re-collected alone after its kernel changed.  No scale factor is
     applied: the copy run (copy_bytes read and written by one plain device
     copy, see `copy`) is reported beside them as a check of the formulas.
     Entries are keyed "<kernel>@<label>" and carry the hash of the kernel's
@@ -126,6 +128,11 @@ def traffic(out, copy_bytes, copy_dirs, groups):
                           "read_ratio": round(copy["read_bytes"] / copy_bytes, 4),
                           "write_ratio": round(copy["write_bytes"] / copy_bytes, 4)},
            "kernels": {}}
+    labels = {g.split("=", 1)[0] for g in groups}
+    if os.path.exists(out):
+        with open(out) as f:
+            prev = json.load(f).get("kernels", {})
+        res["kernels"].update({k: v for k, v in prev.items() if k.split("@", 1)[1] not in labels})
     for g in groups:
         label, dirs = g.split("=", 1)
         rd, wr = (_pmc_rows(d) for d in dirs.split(","))
