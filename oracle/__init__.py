@@ -89,6 +89,9 @@ def _declare(L):
     L.orc_fp16_round.argtypes = [f32]; L.orc_fp16_round.restype = ctypes.c_uint16
     L.orc_e4m3_encode_array.argtypes = [_P, i64, _P]; L.orc_e4m3_encode_array.restype = None
     L.orc_e4m3_decode_array.argtypes = [_P, i64, _P]; L.orc_e4m3_decode_array.restype = None
+    L.orc_e2m1_code_scaled.argtypes = [f32, i32]; L.orc_e2m1_code_scaled.restype = u8
+    L.orc_e2m1_code_scaled_array.argtypes = [_P, i64, i32, _P]
+    L.orc_e2m1_code_scaled_array.restype = None
     L.orc_hadamard.argtypes = [i32, _P]; L.orc_hadamard.restype = None
     L.orc_k_mean.argtypes = [_P, i32, i32, i32, i32, _P]; L.orc_k_mean.restype = None
     L.orc_smooth_k.argtypes = [_P, _P, i32, i32, i32, i32, _P]; L.orc_smooth_k.restype = None
@@ -162,6 +165,18 @@ def e4m3_encode_array(x: np.ndarray) -> np.ndarray:
     x = _c(x, np.float32)
     out = np.empty(x.shape, dtype=np.uint8)
     lib().orc_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e2m1_code_scaled(x: float, e: int) -> int:
+    """E2M1 code of x * 2^-e (an element of an MX block with shared exponent e)."""
+    return int(lib().orc_e2m1_code_scaled(x, e))
+
+
+def e2m1_code_scaled_array(x: np.ndarray, e: int) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_e2m1_code_scaled_array(_ptr(x), x.size, e, _ptr(out))
     return out
 
 

@@ -357,6 +357,19 @@ void orc_rotate(const float* x, int B, int H, int L, int D, int R, float* out) {
 // e2m1_rne_sat(x * 2^-e) (exact power-of-two scaling).
 // Codes are returned one per byte; packing puts element 2i in the low nibble.
 // Pinned: amax * 2^-e in [4, 8); brute force on tiny inputs.
+// One element's code in a block whose shared exponent is e: E2M1 of x * 2^-e
+// [OCP MX] (the scaling is exact in binary64; taking the value to binary32
+// is exact too, except for magnitudes below 2^-126, which code to 0 either
+// way).
+uint8_t orc_e2m1_code_scaled(float x, int e) {
+    double scaled = std::ldexp((double)x, -e);
+    return orc_e2m1_encode((float)scaled);
+}
+
+void orc_e2m1_code_scaled_array(const float* x, int64_t n, int e, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_code_scaled(x[i], e);
+}
+
 void orc_quant_mxfp4(const float* x, int B, int H, int L, int D, uint8_t* codes, uint8_t* e8m0) {
     int64_t rows = (int64_t)B * H * L;
     int nblk = D / 32;
@@ -367,10 +380,7 @@ void orc_quant_mxfp4(const float* x, int B, int H, int L, int D, uint8_t* codes,
             for (int d = 0; d < 32; ++d) amax = std::max(amax, std::fabs(xb[d]));
             int e = orc_mx_shared_exponent(amax);
             e8m0[row * nblk + bl] = (uint8_t)(e + 127);
-            for (int d = 0; d < 32; ++d) {
-                double scaled = std::ldexp((double)xb[d], -e);
-                codes[row * D + bl * 32 + d] = orc_e2m1_encode((float)scaled);
-            }
+            for (int d = 0; d < 32; ++d) codes[row * D + bl * 32 + d] = orc_e2m1_code_scaled(xb[d], e);
         }
 }
 

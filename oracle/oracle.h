@@ -41,6 +41,9 @@ uint16_t orc_bf16_round(float x);
 uint16_t orc_fp16_round(float x);
 void orc_e4m3_encode_array(const float* x, int64_t n, uint8_t* out);
 void orc_e4m3_decode_array(const uint8_t* c, int64_t n, float* out);
+/* E2M1 code of x * 2^-e: an element of an MX block with shared exponent e */
+uint8_t orc_e2m1_code_scaled(float x, int e);
+void orc_e2m1_code_scaled_array(const float* x, int64_t n, int e, uint8_t* out);
 
 /* ---- Hadamard ---------------------------------------------------------- */
 void orc_hadamard(int R, float* H);

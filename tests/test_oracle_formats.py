@@ -163,3 +163,44 @@ def test_pack_fp4_low_nibble_is_even_element(orc):
     p = orc.pack_fp4(codes)
     assert p[0] == 0x10 and p[7] == 0xFE
     assert np.array_equal(orc.unpack_fp4(p), codes)
+
+
+def test_e2m1_code_scaled_brute_force(orc):
+    """An MX block element's code, E2M1(x 2^-e) [OCP MX v1.0], for every shared
+    exponent e: the E2M1 values and the points between them, scaled by 2^e
+    (each exactly representable in binary32, subnormals included), against a
+    nearest-even search in exact rationals; the array form agrees."""
+    vals = _gold("ocp_formats.json")["e2m1_positive_values_by_code"]
+    table = [(v, c) for c, v in enumerate(vals)]
+    pts = set()
+    for a, b in zip(vals[:-1], vals[1:]):
+        for t in np.linspace(a, b, 5):
+            pts.add(float(t))
+    pts.update([6.5, 7.0, 7.75])
+    pts = sorted(pts)
+    fmax = float(np.finfo(np.float32).max)
+    for e in range(-127, 128):
+        pe = [x for x in pts if math.ldexp(x, e) <= fmax]   # e = 126, 127: binary32's top binades
+        xs = np.array([math.ldexp(x, e) for x in pe], dtype=np.float32)
+        assert all(math.ldexp(float(v), -e) == x for v, x in zip(xs, pe)), e   # exact in binary32
+        got = orc.e2m1_code_scaled_array(xs, e)
+        neg = orc.e2m1_code_scaled_array(-xs, e)
+        for x, g, gn, v in zip(pe, got, neg, xs):
+            want = _nearest_even(Fraction(x), table)
+            assert g == want, (e, x)
+            assert gn == (want | 8 if x != 0 else 8), (e, x)
+            assert orc.e2m1_code_scaled(float(v), e) == g
+
+
+def test_mxfp4_quantizer_codes_are_scaled_element_codes(orc):
+    """orc_quant_mxfp4's element codes are E2M1(x 2^-e) with e its own E8M0
+    code - 127, for random blocks spanning many binades."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((3, 64)) * 2.0 ** rng.integers(-40, 40, (3, 64))).astype(np.float32)
+    codes, e8 = orc.quant_mxfp4(x.reshape(1, 1, 3, 64))
+    codes, e8 = codes.reshape(3, 64), e8.reshape(3, 2)
+    for r in range(3):
+        for b in range(2):
+            blk = x[r, 32 * b:32 * b + 32]
+            assert np.array_equal(codes[r, 32 * b:32 * b + 32],
+                                  orc.e2m1_code_scaled_array(blk, int(e8[r, b]) - 127))
