@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define SAGE_VERSION_MAJOR 0
-#define SAGE_VERSION_MINOR 3
+#define SAGE_VERSION_MINOR 4
 #define SAGE_PAD(L) ((((L) + 127) / 128) * 128)
 
 typedef enum {
@@ -362,6 +362,26 @@ sage_status sage_debug_qk_tile_mx(const sage_tensor* q_q, const sage_tensor* q_s
                                   const sage_tensor* k_q, const sage_tensor* k_scale, int32_t q0,
                                   int32_t nq, int32_t k0, int32_t nk, const sage_tensor* out,
                                   void* stream);
+
+/* Test hook: codes[i] = the OCP e4m3 code (OCP 8-bit floating point, E4M3:
+ * round to nearest even) that the kernels give x[i] -- the conversion that
+ * codes P8 = e4m3(448 p) in attention and decode, the V quantizers' codes and
+ * the decode's query codes ([aiter #7388], Changes: Q and P in FP8_MAX's
+ * format).  The kernels never convert a value of magnitude above 448 by more
+ * than rounding slack; beyond 464 the code is whatever the hardware gives.
+ *   x F32 [n] contiguous (device), codes U8 [n] contiguous (device); n = 0
+ *   does nothing.  Errors: DTYPE / SHAPE / LAYOUT / ALIGNMENT for the
+ *   descriptors, before any HIP call. */
+sage_status sage_debug_cvt_e4m3(const sage_tensor* x, const sage_tensor* codes, void* stream);
+
+/* Test hook: codes[i] = the E2M1 code (low nibble; OCP MX v1.0 FP4: round to
+ * nearest even, saturating at 6) of x[i] * 2^-exponent as the MXFP4 quantizer
+ * and the fused-Q attention prologue code an element of a block whose shared
+ * exponent is `exponent` ([xDiT #665]: the Sage v2 MXFP4 path).
+ *   x F32 [n], codes U8 [n] as above; exponent in [-127, 127], else
+ *   SAGE_ERR_INVALID_ARG. */
+sage_status sage_debug_cvt_e2m1(const sage_tensor* x, int32_t exponent, const sage_tensor* codes,
+                                void* stream);
 
 /* Thread-local message of the last failure on this thread ("" if none). */
 const char* sage_last_error(void);

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["quantize.hip", "attn_fwd.hip", "decode.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "attn_fwd.hip", "decode.hip", "debug_cvt.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -818,4 +818,35 @@ sage_status sage_debug_qk_tile_mx(const sage_tensor* q_q, const sage_tensor* q_s
                          "debug qk tile (MXFP4)");
 }
 
+sage_status sage_debug_cvt_e4m3(const sage_tensor* x, const sage_tensor* codes, void* stream) {
+    sage_status st = check_basic(x, "x", 1);
+    if (st) return st;
+    const int64_t n = x->shape[0];
+    const int64_t shape[1] = {n};
+    if ((st = check_exact(x, "x", SAGE_F32, 1, shape))) return st;
+    if ((st = check_exact(codes, "codes", SAGE_U8, 1, shape))) return st;
+    if (n == 0) return ok();
+    if ((st = check_device())) return st;
+    return launch_status(sage::launch_debug_cvt_e4m3((const float*)x->data, (uint8_t*)codes->data, n,
+                                                     (hipStream_t)stream),
+                         "debug e4m3 conversion");
+}
+
+sage_status sage_debug_cvt_e2m1(const sage_tensor* x, int32_t exponent, const sage_tensor* codes,
+                                void* stream) {
+    sage_status st = check_basic(x, "x", 1);
+    if (st) return st;
+    const int64_t n = x->shape[0];
+    const int64_t shape[1] = {n};
+    if ((st = check_exact(x, "x", SAGE_F32, 1, shape))) return st;
+    if ((st = check_exact(codes, "codes", SAGE_U8, 1, shape))) return st;
+    if (exponent < -127 || exponent > 127)
+        return fail(SAGE_ERR_INVALID_ARG, "exponent %d outside the E8M0 range [-127, 127]", (int)exponent);
+    if (n == 0) return ok();
+    if ((st = check_device())) return st;
+    return launch_status(sage::launch_debug_cvt_e2m1((const float*)x->data, (uint8_t*)codes->data, n,
+                                                     (int)exponent, (hipStream_t)stream),
+                         "debug E2M1 conversion");
+}
+
 }  // extern "C"

@@ -34,6 +34,8 @@ hipError_t launch_debug_qk_mx(const uint8_t*, const uint8_t*, const uint8_t*, co
                               int, int, int, int, int, float*, hipStream_t) {
     return hipErrorNoDevice;
 }
+hipError_t launch_debug_cvt_e4m3(const float*, uint8_t*, int64_t, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_debug_cvt_e2m1(const float*, uint8_t*, int64_t, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_paged_decode(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t decode_scratch(void**) { return hipErrorNoDevice; }
 hipError_t launch_hadamard_build(int, void*, void*, hipStream_t) { return hipErrorNoDevice; }

@@ -69,7 +69,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // Two fp32 -> two OCP e4m3 codes in the low (word 0) or high (word 1) half of
 // `old`.  Hardware conversion: round to nearest even, exact for |x| <= 448
 // (inputs of this library never exceed 448 by more than rounding slack, which
-// still rounds to 448).
+// still rounds to 448); the GPU tests compare it with the oracle's encoder
+// over every fp32 input of magnitude below 464.
 template <bool HI>
 __device__ __forceinline__ uint32_t cvt_pk_fp8(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
@@ -174,6 +175,24 @@ __device__ __forceinline__ void mx_rotate_rows(const uint16_t* hs, const uint4 (
     }
 }
 
+// Scale operand of gfx950's scaled conversions for the MX exponent ex in
+// [-127, 127]: the E8M0 byte ex + 127 in the fp32 exponent field (field 0
+// stands for 2^-127).
+__device__ __forceinline__ float mx_scale_operand(int ex) {
+    return __builtin_bit_cast(float, (uint32_t)(ex + 127) << 23);
+}
+
+// E2M1 codes of a * 2^-ex and b * 2^-ex (sc = mx_scale_operand(ex)) into
+// byte SEL of w, a in the low nibble.  gfx950's scaled conversion divides by
+// the E8M0 value of the scale and rounds to the nearest E2M1 value (0, 0.5,
+// 1, 1.5, 2, 3, 4, 6; ties to the even code), saturating at 6; the GPU tests
+// compare it with the oracle's encoder over every fp32 input below 8 * 2^ex
+// for ex = 0 and over the rounding boundaries of every ex.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pk_e2m1(uint32_t w, float a, float b, float sc) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, sc, SEL);
+}
+
 // MX blocks of the values above: per 32-channel block cb the shared exponent
 // ex[cb] = floor(log2 amax) - 2 (the lane and its partner l ^ 32 hold the
 // block's two halves) and the E2M1 codes of y * 2^-ex, packed four per
@@ -187,18 +206,12 @@ __device__ __forceinline__ void mx_quant_rows(const float (&y)[4][16], int (&ex)
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[cb][e]));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         ex[cb] = mx_exponent(amax);
-        // gfx950's scaled conversion divides by 2^(exponent field of the scale
-        // - 127) -- the E8M0 value of the scale's bits -- and rounds to the
-        // nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even
-        // code), saturating at 6: the E2M1 code of y * 2^-ex for every ex in
-        // [-127, 127] (checked against a software rounding over a grid of
-        // inputs and scales, exponent field 0 included).  Two values per
-        // instruction, the first in the low nibble, into byte `sel`.
-        const float sc = __builtin_bit_cast(float, (uint32_t)(ex[cb] + 127) << 23);
+        // the E2M1 code of y * 2^-ex, two values per instruction
+        const float sc = mx_scale_operand(ex[cb]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[cb][4 * i], y[cb][4 * i + 1], sc, 0);
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[cb][4 * i + 2], y[cb][4 * i + 3], sc, 1);
+            uint32_t w = cvt_pk_e2m1<0>(0u, y[cb][4 * i], y[cb][4 * i + 1], sc);
+            w = cvt_pk_e2m1<1>(w, y[cb][4 * i + 2], y[cb][4 * i + 3], sc);
             pk[cb][i] = (uint16_t)w;
         }
     }

@@ -122,6 +122,11 @@ hipError_t launch_debug_qk_mx(const uint8_t* q, const uint8_t* q_scale, const ui
                               const uint8_t* k_scale, int B, int H, int Lqp, int Lkp, int q0, int nq,
                               int k0, int nk, float* out, hipStream_t stream);
 
+// fp32 -> e4m3 codes (the kernels' conversion), and fp32 * 2^-ex -> E2M1
+// codes (the MXFP4 quantizer's), one code per byte, n >= 1
+hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_debug_cvt_e2m1(const float* x, uint8_t* out, int64_t n, int ex, hipStream_t stream);
+
 constexpr int kQueryBF16 = 0, kQueryF16 = 1, kQueryE4M3 = 2;
 struct DecodeArgs {
     const void* q;            // bf16 / fp16 / e4m3 (q_kind)

@@ -117,12 +117,15 @@ def lib():
         L.sage_debug_qk_tile_mx.argtypes = [_T, _T, _T, _T, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, _T, _P]
         L.sage_set_quant_wait_us.argtypes = [ctypes.c_int32]
+        L.sage_debug_cvt_e4m3.argtypes = [_T, _T, _P]
+        L.sage_debug_cvt_e2m1.argtypes = [_T, ctypes.c_int32, _T, _P]
         for name in ("sage_quantize_qk_workspace_size", "sage_quantize_qk",
                      "sage_quantize_v_workspace_size", "sage_quantize_v", "sage_attn_fwd",
                      "sage_paged_decode_workspace_size", "sage_paged_decode",
                      "sage_paged_decode_noalloc",
                      "sage_hadamard_create", "sage_hadamard_destroy", "sage_debug_qk_tile",
-                     "sage_debug_qk_tile_mx", "sage_set_quant_wait_us"):
+                     "sage_debug_qk_tile_mx", "sage_set_quant_wait_us", "sage_debug_cvt_e4m3",
+                     "sage_debug_cvt_e2m1"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -452,6 +455,25 @@ def sage_debug_qk_tile_mx(qk: QuantizedQK, q0: int, nq: int, k0: int, nk: int) -
                                        ctypes.byref(desc(qk.k_scale, E8M0)), q0, nq, k0, nk,
                                        ctypes.byref(desc(out)), _stream(qk.q.device)))
     return out
+
+
+def sage_debug_cvt_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """uint8 e4m3 codes of the fp32 device vector x by the kernels' conversion
+    (test hook)."""
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if x.numel():
+        _check(lib().sage_debug_cvt_e4m3(ctypes.byref(desc(x)), ctypes.byref(desc(codes)), _stream(x.device)))
+    return codes
+
+
+def sage_debug_cvt_e2m1(x: torch.Tensor, exponent: int) -> torch.Tensor:
+    """uint8 E2M1 codes (low nibble) of x * 2^-exponent by the MXFP4
+    quantizer's conversion (test hook)."""
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if x.numel():
+        _check(lib().sage_debug_cvt_e2m1(ctypes.byref(desc(x)), exponent, ctypes.byref(desc(codes)),
+                                         _stream(x.device)))
+    return codes
 
 
 def default_sm_scale(D: int) -> float:

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(S):
     assert len(names) >= 13
     for n in names:
         assert hasattr(S.lib(), n), n
-    assert S.lib().sage_version() == 3   # 0.3: adds sage_set_quant_wait_us
+    assert S.lib().sage_version() == 4   # 0.4: adds the conversion test hooks
 
 
 def test_quant_wait_bound_is_checked(S):
@@ -343,3 +343,23 @@ def test_paged_decode_noalloc_refuses_above_its_scratch(S):
     assert st == S.ERR_WORKSPACE
     assert b"scratch" in S.lib().sage_last_error()
     assert S.DECODE_SCRATCH_BYTES == 32 << 20
+
+
+def test_conversion_hooks_refusals(S):
+    """The e4m3 / E2M1 conversion hooks check their descriptors and the
+    exponent before any HIP call (CPU tensors: a call that got past
+    validation would need a device)."""
+    L = S.lib()
+    x = torch.zeros(64, dtype=torch.float32)
+    c = torch.zeros(64, dtype=torch.uint8)
+    d = lambda t, dt=None: ctypes.byref(S.desc(t, dt))
+    assert L.sage_debug_cvt_e4m3(d(x.to(torch.float16)), d(c), None) == S.ERR_DTYPE
+    assert L.sage_debug_cvt_e4m3(d(x), d(c.to(torch.int32)), None) == S.ERR_DTYPE
+    assert L.sage_debug_cvt_e4m3(d(x), d(c[:32]), None) == S.ERR_SHAPE
+    assert L.sage_debug_cvt_e4m3(d(x.view(8, 8)), d(c), None) == S.ERR_SHAPE
+    assert L.sage_debug_cvt_e4m3(d(torch.zeros(128)[::2]), d(c), None) == S.ERR_LAYOUT
+    assert L.sage_debug_cvt_e4m3(None, d(c), None) == S.ERR_INVALID_ARG
+    assert L.sage_debug_cvt_e2m1(d(x), 128, d(c), None) == S.ERR_INVALID_ARG
+    assert L.sage_debug_cvt_e2m1(d(x), -128, d(c), None) == S.ERR_INVALID_ARG
+    assert L.sage_debug_cvt_e2m1(d(x), 0, d(c[:8]), None) == S.ERR_SHAPE
+    assert L.sage_debug_cvt_e2m1(d(x.to(torch.float64)), 0, d(c), None) == S.ERR_DTYPE
