@@ -23,9 +23,14 @@
  * Conventions
  *  - Tensors are described by sage_tensor: a device pointer, a dtype, and a
  *    LOGICAL shape with element strides.  Q/K/V/out are logical [B, L, H, D];
- *    any B/L/H strides are accepted (so [B,L,H,D], [B,H,L,D] and views into a
- *    stacked QKV buffer all work) but stride[D] must be 1.  The library never
- *    copies an input to make it contiguous.
+ *    any non-negative B/L/H strides are accepted (so [B,L,H,D], [B,H,L,D] and
+ *    views into a stacked QKV buffer all work) but stride[D] must be 1; a
+ *    negative stride is refused with SAGE_ERR_LAYOUT.  The library never
+ *    copies an input to make it contiguous.  The kernels read one (b, h) slice
+ *    of an fp16/bf16 Q, K or V with 32-bit byte offsets, so a slice may span
+ *    at most 0x7FFFFF00 bytes, ((L - 1) stride[L] + D) * 2; a longer one is
+ *    refused with SAGE_ERR_UNSUPPORTED (for the stacked video-DiT layout,
+ *    stride[L] = 3 H D = 15360, that is L <= 69906).
  *  - Alignment: every pointer handed to the library must be 16-byte aligned;
  *    for strided Q/K/V/out, every row start (each B/L/H stride in bytes) must
  *    be a multiple of 16 bytes.
@@ -63,7 +68,7 @@ typedef enum {
     SAGE_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, inconsistent sizes  */
     SAGE_ERR_DTYPE = 2,        /* unsupported dtype or combination (incl. FNUZ FP8) */
     SAGE_ERR_SHAPE = 3,        /* shape mismatch, unsupported head dim, R != 128  */
-    SAGE_ERR_LAYOUT = 4,       /* stride[D] != 1, non-contiguous library tensor  */
+    SAGE_ERR_LAYOUT = 4,       /* stride[D] != 1, negative stride, non-contiguous library tensor */
     SAGE_ERR_ALIGNMENT = 5,    /* pointer or row stride not 16-byte aligned      */
     SAGE_ERR_WORKSPACE = 6,    /* workspace missing or too small                 */
     SAGE_ERR_ARCH = 7,         /* current device is not gfx950                   */

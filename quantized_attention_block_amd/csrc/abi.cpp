@@ -115,12 +115,31 @@ sage_status check_exact(const sage_tensor* t, const char* name, int32_t dtype, i
     return SAGE_OK;
 }
 
-// Strided half-precision [B, L, H, D] view: stride[D] == 1, 16-byte aligned rows.
+// A caller's view: no negative stride (it would address memory before the
+// view's base pointer, which the kernels' buffer resources start at).
+sage_status check_strides(const sage_tensor* t, const char* name) {
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->stride[i] < 0)
+            return fail(SAGE_ERR_LAYOUT, "%s: negative stride %lld in dim %d", name, (long long)t->stride[i], i);
+    return SAGE_OK;
+}
+
+// Strided half-precision [B, L, H, D] view: stride[D] == 1, 16-byte aligned
+// rows, non-negative strides.  The kernels read one (b, h) slice through a
+// buffer resource with 32-bit byte offsets, so a slice may span at most
+// 0x7FFFFF00 bytes: ((L - 1) stride[L] + D) * 2.
 sage_status check_half_view(const sage_tensor* t, const char* name) {
     sage_status st = check_basic(t, name, 4);
     if (st) return st;
     if (t->dtype != SAGE_F16 && t->dtype != SAGE_BF16)
         return fail(SAGE_ERR_DTYPE, "%s: expected f16 or bf16, got %s", name, dtype_name(t->dtype));
+    if ((st = check_strides(t, name))) return st;
+    for (int i = 0; i < 4; ++i)
+        if (t->shape[i] > 0x7FFFFFFF)
+            return fail(SAGE_ERR_SHAPE, "%s: dim %d (%lld) exceeds 2^31 - 1", name, i, (long long)t->shape[i]);
+    if (t->shape[1] > 0 && ((t->shape[1] - 1) * t->stride[1] + t->shape[3]) * 2 > 0x7FFFFF00LL)
+        return fail(SAGE_ERR_UNSUPPORTED, "%s: one (b, h) slice spans more than 2^31 bytes "
+                    "(L %lld, token stride %lld elements)", name, (long long)t->shape[1], (long long)t->stride[1]);
     if (t->shape[3] > 1 && t->stride[3] != 1)
         return fail(SAGE_ERR_LAYOUT, "%s: the head-dim stride must be 1 (got %lld)", name,
                     (long long)t->stride[3]);
@@ -449,6 +468,7 @@ sage_status sage_attn_fwd(const sage_tensor* q_q, const sage_tensor* q_scale, co
     if (out->shape[0] != B || out->shape[1] != Lq || out->shape[2] != H || out->shape[3] != D)
         return fail(SAGE_ERR_SHAPE, "out must be [B, Lq, H, D]");
     if (out->stride[3] != 1) return fail(SAGE_ERR_LAYOUT, "out: the head-dim stride must be 1");
+    if ((st = check_strides(out, "out"))) return st;
     for (int i = 0; i < 3; ++i)
         if (out->shape[i] > 1 && (out->stride[i] * (int64_t)elem_bytes(out->dtype)) % 16)
             return fail(SAGE_ERR_ALIGNMENT, "out: stride of dim %d is not a multiple of 16 bytes", i);
@@ -506,6 +526,7 @@ sage_status decode_query(const sage_tensor* q, const sage_tensor* page_table,
         return fail(SAGE_ERR_DTYPE, "q: expected bf16, f16 or fp8_e4m3fn, got %s", dtype_name(q->dtype));
     }
     if (q->shape[3] > 1 && q->stride[3] != 1) return fail(SAGE_ERR_LAYOUT, "q: head-dim stride must be 1");
+    if ((st = check_strides(q, "q"))) return st;
     const int64_t qeb = (int64_t)elem_bytes(q->dtype);
     for (int i = 0; i < 3; ++i)
         if (q->shape[i] > 1 && (q->stride[i] * qeb) % 16)
@@ -603,6 +624,7 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
     }
     if (page_table->shape[1] > 1 && page_table->stride[1] != 1)
         return fail(SAGE_ERR_LAYOUT, "page_table rows must be contiguous");
+    if ((st = check_strides(page_table, "page_table"))) return st;
     if ((int64_t)page_table->shape[1] * page < p->max_ctx)
         return fail(SAGE_ERR_SHAPE, "page_table covers %lld tokens < max_ctx %d",
                     (long long)page_table->shape[1] * page, p->max_ctx);
@@ -626,6 +648,7 @@ sage_status decode_setup(const sage_tensor* q, const sage_tensor* k_cache, const
     for (int i = 0; i < 4; ++i)
         if (out->shape[i] != q->shape[i]) return fail(SAGE_ERR_SHAPE, "out must be shaped like q");
     if (out->shape[3] > 1 && out->stride[3] != 1) return fail(SAGE_ERR_LAYOUT, "out: head-dim stride must be 1");
+    if ((st = check_strides(out, "out"))) return st;
     for (int i = 0; i < 3; ++i)
         if (out->shape[i] > 1 && (out->stride[i] * 2) % 16)
             return fail(SAGE_ERR_ALIGNMENT, "out: stride of dim %d is not a multiple of 16 bytes", i);

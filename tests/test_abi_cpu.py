@@ -363,3 +363,30 @@ def test_conversion_hooks_refusals(S):
     assert L.sage_debug_cvt_e2m1(d(x), -128, d(c), None) == S.ERR_INVALID_ARG
     assert L.sage_debug_cvt_e2m1(d(x), 0, d(c[:8]), None) == S.ERR_SHAPE
     assert L.sage_debug_cvt_e2m1(d(x.to(torch.float64)), 0, d(c), None) == S.ERR_DTYPE
+
+
+def test_negative_strides_and_oversized_slices_refused(S):
+    """A negative stride would address memory before a view's base, and a
+    (b, h) slice of an fp16/bf16 view longer than 2^31 bytes is beyond the
+    kernels' 32-bit buffer offsets: both are refused before any HIP call
+    (descriptors only; their memory is never touched)."""
+    L = S.lib()
+    prm = S.QkParams(mode=S.QK_INT8, q_block=128, k_block=64, smooth_k=1)
+    nbytes = ctypes.c_size_t()
+    k = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    d = S.desc(k)
+    assert L.sage_quantize_qk_workspace_size(None, ctypes.byref(d), ctypes.byref(prm),
+                                             ctypes.byref(nbytes)) == S.OK
+    d.stride[1] = -d.stride[1]
+    assert L.sage_quantize_qk_workspace_size(None, ctypes.byref(d), ctypes.byref(prm),
+                                             ctypes.byref(nbytes)) == S.ERR_LAYOUT
+    # the stacked video-DiT layout (token stride 3 H D = 15360): 69906 tokens
+    # fit in one slice's 2^31 bytes, 69907 do not
+    for Lk, want in ((69906, S.OK), (69907, S.ERR_UNSUPPORTED)):
+        d = S.desc(k)
+        d.shape[1] = Lk
+        d.shape[2] = 40
+        d.stride[0], d.stride[1], d.stride[2] = Lk * 15360, 15360, 128
+        assert L.sage_quantize_qk_workspace_size(None, ctypes.byref(d), ctypes.byref(prm),
+                                                 ctypes.byref(nbytes)) == want, Lk
+        assert L.sage_quantize_v_workspace_size(ctypes.byref(d), ctypes.byref(nbytes)) == want, Lk
