@@ -48,6 +48,8 @@ def _kernels(tmp_dir):
                 cur[m.group(1)] = m.group(2)
                 if m.group(1) == "name" and not m.group(2).endswith(".kd"):
                     kernels[m.group(2)] = cur
+    if not kernels and os.environ.get("SAGE_LIBRARY"):
+        pytest.skip("SAGE_LIBRARY selects a build without gfx950 code objects (the host-only sanitizer build)")
     names = subprocess.run([cxxfilt], input="\n".join(kernels), capture_output=True, text=True,
                            check=True).stdout.split("\n")
     return {d: kernels[m] for m, d in zip(kernels, names)}
