@@ -74,3 +74,44 @@ def test_noalloc_decode_refuses_more_than_the_scratch():
         sage.sage_paged_decode_noalloc(q, d["k"], d["v"], d["ks"], d["vs"], pt, ctx, torch.empty_like(q),
                                        max_ctx=8192, window=4096, sm_scale=w.sm_scale)
     assert e.value.status == sage.ERR_WORKSPACE
+
+
+def test_decode_replayed_from_a_hip_graph():
+    """Both decode entry points captured into a HIP graph (the no-allocation
+    one is meant for callers under capture): every replay, with eager work
+    and synchronizations between replays, equals the eager decode bit for
+    bit."""
+    dev = require_gpu()
+    w = wl.WORKLOADS["paged_decode"]
+    d = _dev_inputs(wl.make_decode(w), dev)
+    kw = dict(max_ctx=w.ctx, window=w.window, sm_scale=w.sm_scale)
+    say("decode graph: eager reference")
+    ref = sage.sage_paged_decode(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["pt"], d["ctx"], **kw)
+    torch.cuda.synchronize()
+    ws = torch.empty(sage.sage_paged_decode_workspace_size(d["q"], d["k"], d["pt"], max_ctx=w.ctx,
+                                                           window=w.window) + 256,
+                     dtype=torch.uint8, device=dev)
+    out_ws, out_na = torch.empty_like(ref), torch.empty_like(ref)
+    # one eager call of each form before capture (library set-up, such as the
+    # scratch address lookup, happens outside the graph)
+    sage.sage_paged_decode(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["pt"], d["ctx"], out=out_ws,
+                           workspace=ws, **kw)
+    sage.sage_paged_decode_noalloc(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["pt"], d["ctx"], out_na, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("decode graph: capture")
+    with torch.cuda.graph(graph):
+        sage.sage_paged_decode(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["pt"], d["ctx"], out=out_ws,
+                               workspace=ws, **kw)
+        sage.sage_paged_decode_noalloc(d["q"], d["k"], d["v"], d["ks"], d["vs"], d["pt"], d["ctx"], out_na,
+                                       **kw)
+    for i in range(3):
+        out_ws.fill_(float("nan"))
+        out_na.fill_(float("nan"))
+        ws.fill_(0x7F)
+        torch.cuda.synchronize()
+        say(f"decode graph: replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_ws, ref), i
+        assert torch.equal(out_na, ref), i
